@@ -1,0 +1,172 @@
+"""Benchmark of the QSGD compressor hot path on one MI355X.
+
+A step is one encode (quantize + Elias-omega stream, one pass over v) and one
+decode (parse + dequantize) of the ResNet-152-sized synthetic gradient
+(n = 60,192,808 fp32, buckets d = 4096, s = 64), inputs resident in HBM.
+Several copies of the input and output buffers are rotated so that no step
+finds its input in the 256 MB Infinity Cache.
+
+Prints one JSON line: value = whole-job round-trip throughput 4n bytes of fp32
+gradient / (encode + decode time) in GB/s, plus per-direction rates, the
+roofline object of the dominant kernel and the oracle's CPU rate on a bounded
+sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def cpu_baseline(w, max_coords: int, reps: int = 3):
+    """The oracle (single-threaded C, as it stands) on the first whole buckets
+    of the workload (all of it by default): quantize + encode + decode, median of
+    `reps` runs."""
+    import numpy as np
+
+    import oracle
+    if w.seg_len is not None:  # ragged batch: the whole batch
+        m = w.n
+        bst = oracle.ragged_buckets(w.seg_len, w.d)
+    else:
+        m = min(w.n, (max_coords // w.d) * w.d) if max_coords > 0 else w.n
+        bst = oracle.uniform_buckets(m, w.d)
+    v = np.ascontiguousarray(w.v[:m])
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        lev, nrm = oracle.quantize(v, bst, w.s, w.seed)
+        words, offs, nbits = oracle.encode(lev, nrm, bst, w.s)
+        rc, vh = oracle.decode(words, offs, bst, w.s)
+        times.append(time.perf_counter() - t0)
+        assert rc == oracle.OK
+    t = sorted(times)[len(times) // 2]
+    return {"value": round(4.0 * m / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{m} coordinates ({len(bst) - 1} buckets) of the same gradient; "
+                      f"quantize+encode+decode, median of {reps} runs, {t:.2f} s each"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--cpu-sample", type=int, default=0, help="coordinates for the oracle (0: all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the compressor needs no second GPU); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_sgd_amd as q
+    from quantized_sgd_amd import workloads as wl
+
+    w = wl.CONFIGS[args.config]()
+    n, s, d, seed = w.n, w.s, w.d, w.seed
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    R = max(1, args.rotate)
+    host = torch.from_numpy(w.v)
+    vs = [host.to(dev) for _ in range(R)]
+    ragged = w.seg_len is not None
+    lay = q.RaggedLayout(w.seg_len, d) if ragged else None
+    nb = lay.nb if ragged else q.num_buckets(n, d)
+    cap = lay.capacity_words(s) if ragged else q.encode_capacity_words(n, s, d)
+    outs = [torch.empty(cap, dtype=torch.int64, device=dev) for _ in range(R)]
+    bits = [torch.empty(1, dtype=torch.int64, device=dev) for _ in range(R)]
+    offs = [torch.empty(nb + 1, dtype=torch.int64, device=dev) for _ in range(R)]
+    vhs = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
+    stream = torch.cuda.current_stream()
+
+    def enc(r):
+        if ragged:
+            q.encode_ragged(vs[r], lay, s, seed, out=outs[r], out_bits=bits[r], offsets=offs[r])
+        else:
+            q.encode(vs[r], s, d, seed, out=outs[r], out_bits=bits[r], offsets=offs[r])
+
+    def dec(r):
+        if ragged:
+            q.decode_ragged(outs[r], offs[r], lay, s, v_hat=vhs[r])
+        else:
+            q.decode(outs[r], offs[r], n, s, d, v_hat=vhs[r])
+
+    for i in range(args.warmup):
+        enc(i % R)
+        dec(i % R)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        r = i % R
+        ev[i][0].record(stream)
+        enc(r)
+        ev[i][1].record(stream)
+        dec(r)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    enc_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    med = lambda a: a[len(a) // 2]
+    enc_avg = sum(enc_ms) / K
+    dec_avg = sum(dec_ms) / K
+    ms_per_step = (t1 - t0) * 1e3 / K
+    nbits = int(bits[0].item())
+    gbytes = 4.0 * n / 1e9
+    # algorithmic bytes per launch: encode reads v, writes the stream and offsets;
+    # decode reads the stream and offsets, writes v_hat
+    side = 8.0 * (nb + 1)
+    enc_bytes = 4.0 * n + nbits / 8.0 + side
+    dec_bytes = nbits / 8.0 + side + 4.0 * n
+    enc_gbps = enc_bytes / (enc_avg * 1e-3) / 1e9
+    dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
+    dominant = "encode" if enc_avg >= dec_avg else "decode"
+    ach = enc_gbps if dominant == "encode" else dec_gbps
+    res = {
+        "metric": "QSGD encode+decode round-trip GB/s of fp32 gradient on 1 MI355X",
+        "value": round(gbytes / ((enc_avg + dec_avg) * 1e-3), 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n": n, "d": d, "s": s, "buckets": nb,
+                   "input_copies_rotated": R},
+        "encode_ms_median": round(med(enc_ms), 4),
+        "decode_ms_median": round(med(dec_ms), 4),
+        "encode_GBps_fp32": round(gbytes / (enc_avg * 1e-3), 2),
+        "decode_GBps_fp32": round(gbytes / (dec_avg * 1e-3), 2),
+        "encode_hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
+        "decode_hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "bits_per_coord": round(nbits / n, 4),
+        "compression_vs_fp32": round(32.0 * n / nbits, 3),
+        "compression_vs_fp32_with_offsets": round(32.0 * n / (nbits + 64.0 * (nb + 1)), 3),
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

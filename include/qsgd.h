@@ -1,0 +1,157 @@
+/*
+ * qsgd.h -- C ABI of the MI355X (gfx950) QSGD compressor library (libqsgd.so).
+ *
+ * The method (page "QSGD (Quantized Stochastic Gradient Descent) with Elias
+ * Coding", definition paragraph): each bucket of d consecutive coordinates of an
+ * fp32 gradient v is stochastically quantized to
+ *     Q_s(v)_i = ||v||_2 * sgn(v_i) * k_i / s,   k_i in {0..s},
+ * where l_i = floor(s|v_i|/||v||_2), p_i = s|v_i|/||v||_2 - l_i and k_i = l_i + 1
+ * with probability p_i, else l_i. The tuple (norm, signs, gaps between non-zero
+ * coordinates, levels k_i) is written losslessly with Elias omega codes (same
+ * page, claim on Elias coding: F = 32 bit norm; bucketing per the claim on
+ * bucketed training, paper Section 3.3).
+ *
+ * Exact semantics (the pages give real-valued math only; these are the readings
+ * this library implements, bit for bit):
+ *   norm_b   = RN32(sqrt(sum_{i in b} (double)v_i^2)) with an fp64 sum in a fixed
+ *              (deterministic) order.
+ *   r_i      = RN32(|v_i| * RN64(s / norm_b));  l = floor(r);  p = r - l.
+ *   uniform  = (w >> 8) * 2^-24 where w is word (i & 3) of Philox4x32-10
+ *              (Salmon et al., SC'11) with key (lo32(seed), hi32(seed)) and
+ *              counter (lo32(i >> 2), hi32(i >> 2), 0, 0); i is the flat index
+ *              of the coordinate in v. k = l + [uniform < p].
+ *   stream   = for each bucket: the 32-bit pattern of norm_b, then for each
+ *              non-zero level in index order: omega(gap), 1 sign bit (1 =
+ *              negative), omega(k). gap = j - j_prev with j_prev = -1 at the
+ *              bucket start (bucket-local indices). Buckets are concatenated with
+ *              no padding. Stream bit t is bit 63 - (t mod 64) of 64-bit word
+ *              t / 64; unused bits of the last word are 0.
+ *   decode   = v_hat_i = +-RN32(k * RN64(norm_b / s)) for coded coordinates
+ *              (minus for sign bit 1), +0.0f elsewhere.
+ *   An all-zero bucket has norm 0 and no records.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers, allocated and owned by the caller,
+ *     except the arguments documented as HOST arrays. The library allocates no
+ *     device memory and keeps no device state between calls.
+ *   - Calls only enqueue work on `stream` (0 = the null stream) and return
+ *     without synchronizing; results are valid once the stream reaches them.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     reported as QSGD_ERR_INVALID_ARG; a failed kernel launch is
+ *     QSGD_ERR_LAUNCH. Data-dependent problems (non-finite v, a malformed stream
+ *     passed to decode) are not reported: the output is then unspecified, but no
+ *     kernel reads or writes outside the buffers described here.
+ *   - v must be 16-byte aligned. Outputs must not overlap inputs.
+ *   - Calls on different streams may run concurrently as long as their buffers
+ *     are disjoint.
+ *   - Preconditions: 1 <= s <= 2^24, d >= 1, every v_i finite, every bucket norm
+ *     finite in fp32.
+ */
+#ifndef QSGD_H
+#define QSGD_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QSGD_OK = 0,
+    QSGD_ERR_INVALID_ARG = 1,
+    QSGD_ERR_LAUNCH = 2,
+    QSGD_ERR_UNSUPPORTED = 3
+} qsgd_status;
+
+/* Human-readable name of a status code (static string). */
+const char *qsgd_status_string(qsgd_status status);
+
+/* ceil(n / d): the number of buckets of a single vector (0 if d == 0). */
+uint64_t qsgd_num_buckets(uint64_t n, uint32_t d);
+
+/* Largest bucket length that qsgd_quantize / qsgd_encode accept (4096 in this
+ * build); larger d returns QSGD_ERR_UNSUPPORTED. Decode accepts any d. */
+uint32_t qsgd_max_bucket(void);
+
+/* Number of uint64 words the `out` buffer of qsgd_encode must hold for (n, s, d):
+ * a worst-case stream bound, 32 nb + n (2.5 + |omega(s)|) bits (|omega(g)| <=
+ * 1.5 g bounds the gap codes of a bucket by 1.5 times its length), followed by
+ * the encoder's workspace (two words per tile and a work counter). */
+uint64_t qsgd_encode_capacity_words(uint64_t n, uint32_t s, uint32_t d);
+
+/*
+ * qsgd_quantize: Q_s per bucket (page "QSGD ... with Elias Coding", definition
+ * paragraph), without encoding.
+ *   v       [n] fp32 input.
+ *   levels  [n] int32 output: sgn(v_i) * k_i (0 where k_i = 0).
+ *   norms   [ceil(n/d)] fp32 output: norm_b.
+ * n == 0 enqueues nothing.
+ */
+qsgd_status qsgd_quantize(const float *v, uint64_t n, uint32_t s, uint32_t d, uint64_t seed,
+                          int32_t *levels, float *norms, hipStream_t stream);
+
+/*
+ * qsgd_encode: quantize and Elias-omega encode v into one bitstream (same page,
+ * definition paragraph and claim on Elias coding), in a single pass over v.
+ *   out                 [qsgd_encode_capacity_words(n, s, d)] uint64 output: the
+ *                       stream in words [0, ceil(out_bits/64)); the words after it
+ *                       are workspace and hold unspecified values afterwards.
+ *   out_bits            [1] uint64 output: stream length in bits.
+ *   bucket_bit_offsets  [ceil(n/d) + 1] uint64 output: start bit of each bucket;
+ *                       the last entry equals out_bits.
+ * n == 0 writes out_bits = 0 and bucket_bit_offsets[0] = 0.
+ */
+qsgd_status qsgd_encode(const float *v, uint64_t n, uint32_t s, uint32_t d, uint64_t seed,
+                        uint64_t *out, uint64_t *out_bits, uint64_t *bucket_bit_offsets,
+                        hipStream_t stream);
+
+/*
+ * qsgd_decode: parse the stream and dequantize (the coding is lossless: same
+ * page, definition paragraph).
+ *   in                  stream words written by qsgd_encode (read-only).
+ *   bucket_bit_offsets  [ceil(n/d) + 1] the offsets written by qsgd_encode.
+ *   v_hat               [n] fp32 output; every element is written.
+ * n, s, d must be those of the encode call.
+ */
+qsgd_status qsgd_decode(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
+                        uint32_t s, uint32_t d, float *v_hat, hipStream_t stream);
+
+/* ---- ragged batches: several tensors in one flat buffer --------------------
+ * Buckets restart at every tensor boundary (per-tensor quantization); the
+ * Philox index of a coordinate is its flat index in the concatenation. The
+ * bucket layout is a table bucket_start[nb + 1] (bucket b covers flat
+ * coordinates [bucket_start[b], bucket_start[b+1]), every bucket at most d long),
+ * built on the host by qsgd_ragged_bucket_table and copied to the device by the
+ * caller. */
+
+/* Number of buckets for host seg_len[nseg] (tensor lengths; zero-length tensors
+ * have no buckets). */
+uint64_t qsgd_num_buckets_ragged(const uint64_t *seg_len, uint32_t nseg, uint32_t d);
+
+/* Fills the HOST array bucket_start[nb + 1] from HOST seg_len[nseg]; nb must be
+ * qsgd_num_buckets_ragged(seg_len, nseg, d). */
+qsgd_status qsgd_ragged_bucket_table(const uint64_t *seg_len, uint32_t nseg, uint32_t d,
+                                     uint64_t *bucket_start, uint64_t nb);
+
+/* Capacity of `out` for qsgd_encode_ragged with n coordinates and nb buckets. */
+uint64_t qsgd_encode_capacity_words_ragged(uint64_t n, uint64_t nb, uint32_t s, uint32_t d);
+
+/* Ragged variants of the three calls: bucket_start is the DEVICE copy of the
+ * table; n = bucket_start[nb] (passed by value). Other arguments as above. */
+qsgd_status qsgd_quantize_ragged(const float *v, uint64_t n, const uint64_t *bucket_start,
+                                 uint64_t nb, uint32_t s, uint32_t d, uint64_t seed,
+                                 int32_t *levels, float *norms, hipStream_t stream);
+qsgd_status qsgd_encode_ragged(const float *v, uint64_t n, const uint64_t *bucket_start,
+                               uint64_t nb, uint32_t s, uint32_t d, uint64_t seed,
+                               uint64_t *out, uint64_t *out_bits,
+                               uint64_t *bucket_bit_offsets, hipStream_t stream);
+qsgd_status qsgd_decode_ragged(const uint64_t *in, const uint64_t *bucket_bit_offsets,
+                               uint64_t n, const uint64_t *bucket_start, uint64_t nb,
+                               uint32_t s, uint32_t d, float *v_hat, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QSGD_H */

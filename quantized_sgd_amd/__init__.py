@@ -1,0 +1,221 @@
+"""MI355X-native QSGD compressor: thin Python binding over libqsgd.so.
+
+Every step of the compressor runs in the HIP kernels behind the C ABI of
+include/qsgd.h; this module only marshals torch tensors (device memory and the
+current HIP stream) into those calls. There is no CPU fallback: if the library
+is not built, every entry point raises.
+
+Method: page "QSGD (Quantized Stochastic Gradient Descent) with Elias Coding"
+(definition paragraph; claims on Elias coding and on bucketed training).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "QsgdError", "lib", "num_buckets", "encode_capacity_words", "quantize", "encode",
+    "decode", "RaggedLayout", "quantize_ragged", "encode_ragged", "decode_ragged",
+    "max_bucket",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsgd.so")
+_lib = None
+
+_u64 = ctypes.c_uint64
+_u32 = ctypes.c_uint32
+_vp = ctypes.c_void_p
+
+QSGD_OK, QSGD_ERR_INVALID_ARG, QSGD_ERR_LAUNCH, QSGD_ERR_UNSUPPORTED = 0, 1, 2, 3
+
+
+class QsgdError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        name = lib().qsgd_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{what}: {name}")
+        self.status = status
+
+
+def lib():
+    """Loads libqsgd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m quantized_sgd_amd.build` "
+                "(the QSGD compressor has no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.qsgd_status_string.argtypes = [ctypes.c_int]
+        L.qsgd_status_string.restype = ctypes.c_char_p
+        L.qsgd_num_buckets.argtypes = [_u64, _u32]
+        L.qsgd_num_buckets.restype = _u64
+        L.qsgd_max_bucket.argtypes = []
+        L.qsgd_max_bucket.restype = _u32
+        L.qsgd_encode_capacity_words.argtypes = [_u64, _u32, _u32]
+        L.qsgd_encode_capacity_words.restype = _u64
+        L.qsgd_encode_capacity_words_ragged.argtypes = [_u64, _u64, _u32, _u32]
+        L.qsgd_encode_capacity_words_ragged.restype = _u64
+        L.qsgd_quantize.argtypes = [_vp, _u64, _u32, _u32, _u64, _vp, _vp, _vp]
+        L.qsgd_encode.argtypes = [_vp, _u64, _u32, _u32, _u64, _vp, _vp, _vp, _vp]
+        L.qsgd_decode.argtypes = [_vp, _vp, _u64, _u32, _u32, _vp, _vp]
+        L.qsgd_num_buckets_ragged.argtypes = [_vp, _u32, _u32]
+        L.qsgd_num_buckets_ragged.restype = _u64
+        L.qsgd_ragged_bucket_table.argtypes = [_vp, _u32, _u32, _vp, _u64]
+        L.qsgd_quantize_ragged.argtypes = [_vp, _u64, _vp, _u64, _u32, _u32, _u64, _vp, _vp, _vp]
+        L.qsgd_encode_ragged.argtypes = [_vp, _u64, _vp, _u64, _u32, _u32, _u64, _vp, _vp, _vp, _vp]
+        L.qsgd_decode_ragged.argtypes = [_vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp, _vp]
+        for name in ("qsgd_quantize", "qsgd_encode", "qsgd_decode", "qsgd_ragged_bucket_table",
+                     "qsgd_quantize_ragged", "qsgd_encode_ragged", "qsgd_decode_ragged"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != QSGD_OK:
+        raise QsgdError(status, what)
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def num_buckets(n: int, d: int) -> int:
+    return int(lib().qsgd_num_buckets(n, d))
+
+
+def max_bucket() -> int:
+    return int(lib().qsgd_max_bucket())
+
+
+def encode_capacity_words(n: int, s: int, d: int) -> int:
+    return int(lib().qsgd_encode_capacity_words(n, s, d))
+
+
+def quantize(v: torch.Tensor, s: int, d: int, seed: int, levels=None, norms=None, stream=None):
+    """Q_s per bucket: returns (levels int32 = sgn * k, norms float32)."""
+    n = v.numel()
+    nb = num_buckets(n, d)
+    if levels is None:
+        levels = torch.empty(n, dtype=torch.int32, device=v.device)
+    if norms is None:
+        norms = torch.empty(max(nb, 1), dtype=torch.float32, device=v.device)
+    _check(lib().qsgd_quantize(_dev(v, torch.float32, "v"), n, s, d, seed,
+                               _dev(levels, torch.int32, "levels"),
+                               _dev(norms, torch.float32, "norms"), _stream(stream)),
+           "qsgd_quantize")
+    return levels, norms[:nb]
+
+
+def encode(v: torch.Tensor, s: int, d: int, seed: int, out=None, out_bits=None, offsets=None,
+           stream=None):
+    """Returns (out words, out_bits [1], bucket bit offsets [nb + 1]) as device
+    tensors (uint64 data in int64 tensors). The stream is out[: ceil(bits/64)]."""
+    n = v.numel()
+    nb = num_buckets(n, d)
+    cap = encode_capacity_words(n, s, d)
+    if cap == 0:
+        raise QsgdError(QSGD_ERR_UNSUPPORTED, "qsgd_encode_capacity_words")
+    if out is None:
+        out = torch.empty(cap, dtype=torch.int64, device=v.device)
+    elif out.numel() < cap:
+        raise ValueError(f"out holds {out.numel()} words, needs {cap}")
+    if out_bits is None:
+        out_bits = torch.empty(1, dtype=torch.int64, device=v.device)
+    if offsets is None:
+        offsets = torch.empty(nb + 1, dtype=torch.int64, device=v.device)
+    _check(lib().qsgd_encode(_dev(v, torch.float32, "v"), n, s, d, seed,
+                             _dev(out, torch.int64, "out"), _dev(out_bits, torch.int64, "out_bits"),
+                             _dev(offsets, torch.int64, "offsets"), _stream(stream)),
+           "qsgd_encode")
+    return out, out_bits, offsets
+
+
+def decode(words: torch.Tensor, offsets: torch.Tensor, n: int, s: int, d: int, v_hat=None,
+           stream=None):
+    """Decodes a stream written by encode back to Q_s(v) (float32 [n])."""
+    if v_hat is None:
+        v_hat = torch.empty(n, dtype=torch.float32, device=words.device)
+    _check(lib().qsgd_decode(_dev(words, torch.int64, "words"), _dev(offsets, torch.int64, "offsets"),
+                             n, s, d, _dev(v_hat, torch.float32, "v_hat"), _stream(stream)),
+           "qsgd_decode")
+    return v_hat
+
+
+class RaggedLayout:
+    """Bucket layout of a batch of tensors laid out back to back in one buffer:
+    buckets of at most d coordinates that restart at every tensor."""
+
+    def __init__(self, seg_len, d: int, device="cuda"):
+        import numpy as np
+        sl = np.ascontiguousarray(np.asarray(seg_len, dtype=np.uint64))
+        self.d = int(d)
+        self.n = int(sl.sum())
+        self.nseg = len(sl)
+        nb = int(lib().qsgd_num_buckets_ragged(sl.ctypes.data, len(sl), d))
+        table = np.zeros(nb + 1, dtype=np.uint64)
+        _check(lib().qsgd_ragged_bucket_table(sl.ctypes.data, len(sl), d, table.ctypes.data, nb),
+               "qsgd_ragged_bucket_table")
+        self.nb = nb
+        self.bucket_start_host = table
+        self.bucket_start = torch.from_numpy(table.view(np.int64)).to(device)
+
+    def capacity_words(self, s: int) -> int:
+        return int(lib().qsgd_encode_capacity_words_ragged(self.n, self.nb, s, self.d))
+
+
+def quantize_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, stream=None):
+    levels = torch.empty(layout.n, dtype=torch.int32, device=v.device)
+    norms = torch.empty(max(layout.nb, 1), dtype=torch.float32, device=v.device)
+    _check(lib().qsgd_quantize_ragged(_dev(v, torch.float32, "v"), layout.n,
+                                      _dev(layout.bucket_start, torch.int64, "bucket_start"),
+                                      layout.nb, s, layout.d, seed, _dev(levels, torch.int32, "levels"),
+                                      _dev(norms, torch.float32, "norms"), _stream(stream)),
+           "qsgd_quantize_ragged")
+    return levels, norms[: layout.nb]
+
+
+def encode_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, out=None, out_bits=None,
+                  offsets=None, stream=None):
+    cap = layout.capacity_words(s)
+    if cap == 0:
+        raise QsgdError(QSGD_ERR_UNSUPPORTED, "qsgd_encode_capacity_words_ragged")
+    if out is None:
+        out = torch.empty(cap, dtype=torch.int64, device=v.device)
+    if out_bits is None:
+        out_bits = torch.empty(1, dtype=torch.int64, device=v.device)
+    if offsets is None:
+        offsets = torch.empty(layout.nb + 1, dtype=torch.int64, device=v.device)
+    _check(lib().qsgd_encode_ragged(_dev(v, torch.float32, "v"), layout.n,
+                                    _dev(layout.bucket_start, torch.int64, "bucket_start"), layout.nb,
+                                    s, layout.d, seed, _dev(out, torch.int64, "out"),
+                                    _dev(out_bits, torch.int64, "out_bits"),
+                                    _dev(offsets, torch.int64, "offsets"), _stream(stream)),
+           "qsgd_encode_ragged")
+    return out, out_bits, offsets
+
+
+def decode_ragged(words: torch.Tensor, offsets: torch.Tensor, layout: RaggedLayout, s: int,
+                  v_hat=None, stream=None):
+    if v_hat is None:
+        v_hat = torch.empty(layout.n, dtype=torch.float32, device=words.device)
+    _check(lib().qsgd_decode_ragged(_dev(words, torch.int64, "words"),
+                                    _dev(offsets, torch.int64, "offsets"), layout.n,
+                                    _dev(layout.bucket_start, torch.int64, "bucket_start"), layout.nb,
+                                    s, layout.d, _dev(v_hat, torch.float32, "v_hat"), _stream(stream)),
+           "qsgd_decode_ragged")
+    return v_hat

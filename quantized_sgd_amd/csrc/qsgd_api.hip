@@ -1,0 +1,278 @@
+// Host side of libqsgd.so: the C ABI declared in include/qsgd.h. Validates
+// arguments, derives the tiling, and enqueues the gfx950 kernels on the caller's
+// stream. No device memory is allocated here; the encoder's workspace lives in
+// the tail of the caller's `out` buffer.
+#include "qsgd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "qsgd_decode.h"
+#include "qsgd_encode.h"
+
+using namespace qsgd;
+
+namespace {
+
+uint32_t host_omega_len(uint64_t N) {  // Elias omega codeword length
+    uint32_t L = 1;
+    while (N > 1) {
+        uint32_t b = 0;
+        for (uint64_t x = N; x; x >>= 1) ++b;
+        L += b;
+        N = b - 1;
+    }
+    return L;
+}
+
+// Buckets per tile: whole buckets whose coordinates fit 4096 slots after the
+// tile start is rounded down to a multiple of 16 (no rounding when every bucket
+// start is a multiple of 16).
+uint32_t buckets_per_tile(uint32_t d, bool aligned_starts) {
+    if (d == 0) return 0;
+    const uint32_t room = aligned_starts ? (uint32_t)kTC : (uint32_t)(kTC - 15);
+    return std::min<uint32_t>((uint32_t)kKMax, room / d);
+}
+
+struct EncodePlan {
+    uint32_t K = 0;
+    uint64_t ntiles = 0;
+    uint64_t stream_words = 0;  // capacity reserved for the stream
+    uint64_t ws_words = 0;      // workspace words after the stream
+    uint32_t stage_words = 0;
+    uint32_t obuf_words = 0;
+    size_t lds_bytes = 0;
+};
+
+EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool aligned_starts) {
+    EncodePlan p;
+    p.K = buckets_per_tile(d, aligned_starts);
+    if (p.K == 0) return p;
+    p.ntiles = (nb + p.K - 1) / p.K;
+    const uint64_t Ls = host_omega_len(s);
+    // stream bound: 32 nb + n (2.5 + Ls) bits, rounded up to words, plus one
+    const uint64_t twice_bits = 64 * nb + n * (5 + 2 * Ls);
+    p.stream_words = (twice_bits + 127) / 128 + 1;
+    p.stream_words = (p.stream_words + 31) & ~(uint64_t)31;
+    p.ws_words = 2 * p.ntiles + 1;
+    // LDS: staging bound per tile (records of at most 12 + Ls bits beside the
+    // pending first gap, 32 bits per bucket norm, word rounding per thread), the
+    // output window (adds the pending gap codes and a spare word at each end).
+    const uint64_t Ld = host_omega_len(std::max<uint32_t>(d, 1));
+    const uint64_t stage_bits = (uint64_t)kTC * (12 + Ls) + 32ull * p.K;
+    p.stage_words = (uint32_t)((stage_bits + 63) / 64 + kWG);
+    p.obuf_words = (uint32_t)((stage_bits + (uint64_t)kWG * Ld + 63) / 64 + 3);
+    size_t off = (size_t)p.stage_words * 8 + (size_t)p.obuf_words * 8;
+    off += (size_t)p.K * 8 + kWaves * 8;
+    off = (off + (size_t)(p.K + 1) * 4 + 7) & ~(size_t)7;
+    off = (off + (size_t)p.K * 4 + 7) & ~(size_t)7;
+    off = (off + kWaves * 4 + 7) & ~(size_t)7;
+    off = (off + (size_t)p.K * 4 + 7) & ~(size_t)7;
+    off += (size_t)kWG * 4;
+    p.lds_bytes = off;
+    return p;
+}
+
+size_t quantize_lds_bytes(const EncodePlan &p) {
+    // quantize_kernel carves the same layout with empty staging / output areas
+    size_t off = (size_t)p.K * 8 + kWaves * 8;
+    off = (off + (size_t)(p.K + 1) * 4 + 7) & ~(size_t)7;
+    off = (off + (size_t)p.K * 4 + 7) & ~(size_t)7;
+    off = (off + kWaves * 4 + 7) & ~(size_t)7;
+    off = (off + (size_t)p.K * 4 + 7) & ~(size_t)7;
+    off += (size_t)kWG * 4;
+    return off;
+}
+
+constexpr size_t kMaxLds = 64 * 1024;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+qsgd_status launch_status() {
+    return hipGetLastError() == hipSuccess ? QSGD_OK : QSGD_ERR_LAUNCH;
+}
+
+qsgd_status check_common(const float *v, uint32_t s, uint32_t d) {
+    if (s == 0 || s > (1u << 24) || d == 0) return QSGD_ERR_INVALID_ARG;
+    if (v && !aligned16(v)) return QSGD_ERR_INVALID_ARG;
+    return QSGD_OK;
+}
+
+qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb,
+                          uint32_t s, uint32_t d, uint64_t seed, int32_t *levels, float *norms,
+                          hipStream_t stream) {
+    qsgd_status st = check_common(v, s, d);
+    if (st != QSGD_OK) return st;
+    if (n == 0) return QSGD_OK;
+    if (!v || !levels || !norms || !aligned16(levels)) return QSGD_ERR_INVALID_ARG;
+    const bool ragged = bstart != nullptr;
+    EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0));
+    if (p.K == 0) return QSGD_ERR_UNSUPPORTED;
+    QsgdParams P{};
+    P.v = v; P.n = n; P.nb = nb; P.bstart = bstart; P.seed = seed; P.s = s; P.d = d;
+    P.K = p.K; P.ntiles = (uint32_t)p.ntiles; P.levels = levels; P.norms = norms;
+    P.stage_words = 0; P.obuf_words = 0;
+    const size_t lds = quantize_lds_bytes(p);
+    if (ragged)
+        hipLaunchKernelGGL(quantize_kernel<true>, dim3((uint32_t)p.ntiles), dim3(kWG), lds, stream, P);
+    else
+        hipLaunchKernelGGL(quantize_kernel<false>, dim3((uint32_t)p.ntiles), dim3(kWG), lds, stream, P);
+    return launch_status();
+}
+
+qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb, uint32_t s,
+                        uint32_t d, uint64_t seed, uint64_t *out, uint64_t *out_bits,
+                        uint64_t *offsets, hipStream_t stream) {
+    qsgd_status st = check_common(v, s, d);
+    if (st != QSGD_OK) return st;
+    if (!out_bits || !offsets) return QSGD_ERR_INVALID_ARG;
+    if (n == 0 || nb == 0) {
+        hipLaunchKernelGGL(encode_empty_kernel, dim3(1), dim3(64), 0, stream, out_bits, offsets);
+        return launch_status();
+    }
+    if (!v || !out) return QSGD_ERR_INVALID_ARG;
+    const bool ragged = bstart != nullptr;
+    EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0));
+    if (p.K == 0) return QSGD_ERR_UNSUPPORTED;
+    if (p.lds_bytes > kMaxLds || p.ntiles >= (1ull << 32)) return QSGD_ERR_UNSUPPORTED;
+    QsgdParams P{};
+    P.v = v; P.n = n; P.nb = nb; P.bstart = bstart; P.seed = seed; P.s = s; P.d = d;
+    P.K = p.K; P.ntiles = (uint32_t)p.ntiles;
+    P.out = out; P.out_bits = out_bits; P.offsets = offsets;
+    P.status = out + p.stream_words;
+    P.carry = P.status + p.ntiles;
+    P.ticket = reinterpret_cast<uint32_t *>(P.carry + p.ntiles);
+    P.stage_words = p.stage_words; P.obuf_words = p.obuf_words;
+    const uint32_t init_blocks = (uint32_t)std::min<uint64_t>((p.ntiles + 255) / 256, 1024);
+    hipLaunchKernelGGL(encode_init_kernel, dim3(std::max<uint32_t>(init_blocks, 1)), dim3(256), 0,
+                       stream, P.status, P.carry, P.ticket, (uint32_t)p.ntiles);
+    if (ragged)
+        hipLaunchKernelGGL(encode_kernel<true>, dim3((uint32_t)p.ntiles), dim3(kWG), p.lds_bytes, stream, P);
+    else
+        hipLaunchKernelGGL(encode_kernel<false>, dim3((uint32_t)p.ntiles), dim3(kWG), p.lds_bytes, stream, P);
+    return launch_status();
+}
+
+qsgd_status decode_impl(const uint64_t *in, const uint64_t *offsets, uint64_t n, const uint64_t *bstart,
+                        uint64_t nb, uint32_t s, uint32_t d, float *v_hat, hipStream_t stream) {
+    qsgd_status st = check_common(nullptr, s, d);
+    if (st != QSGD_OK) return st;
+    if (n == 0 || nb == 0) return QSGD_OK;
+    if (!in || !offsets || !v_hat) return QSGD_ERR_INVALID_ARG;
+    DecodeParams D{};
+    D.in = in; D.offsets = offsets; D.bstart = bstart; D.v_hat = v_hat;
+    D.n = n; D.nb = nb; D.s = s; D.d = d;
+    const uint64_t want = (nb + kWaves - 1) / kWaves;
+    const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, 256ull * 16);
+    if (bstart)
+        hipLaunchKernelGGL(decode_kernel<true>, dim3(blocks), dim3(kWG), 0, stream, D);
+    else
+        hipLaunchKernelGGL(decode_kernel<false>, dim3(blocks), dim3(kWG), 0, stream, D);
+    return launch_status();
+}
+
+uint64_t ragged_count(const uint64_t *seg_len, uint32_t nseg, uint32_t d, uint64_t *table) {
+    uint64_t nb = 0, base = 0;
+    for (uint32_t t = 0; t < nseg; ++t) {
+        const uint64_t end = base + seg_len[t];
+        for (uint64_t pos = base; pos < end; pos = (end - pos > d) ? pos + d : end) {
+            if (table) table[nb] = pos;
+            ++nb;
+        }
+        base = end;
+    }
+    if (table) table[nb] = base;
+    return nb;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qsgd_status_string(qsgd_status status) {
+    switch (status) {
+        case QSGD_OK: return "QSGD_OK";
+        case QSGD_ERR_INVALID_ARG: return "QSGD_ERR_INVALID_ARG";
+        case QSGD_ERR_LAUNCH: return "QSGD_ERR_LAUNCH";
+        case QSGD_ERR_UNSUPPORTED: return "QSGD_ERR_UNSUPPORTED";
+    }
+    return "QSGD_UNKNOWN_STATUS";
+}
+
+uint64_t qsgd_num_buckets(uint64_t n, uint32_t d) { return d ? (n + d - 1) / d : 0; }
+
+uint32_t qsgd_max_bucket(void) { return (uint32_t)kTC; }
+
+uint64_t qsgd_encode_capacity_words(uint64_t n, uint32_t s, uint32_t d) {
+    if (d == 0 || s == 0) return 0;
+    const uint64_t nb = qsgd_num_buckets(n, d);
+    if (nb == 0) return 1;
+    EncodePlan p = make_plan(n, nb, s, d, d % 16 == 0);
+    if (p.K == 0) return 0;
+    return p.stream_words + p.ws_words;
+}
+
+uint64_t qsgd_encode_capacity_words_ragged(uint64_t n, uint64_t nb, uint32_t s, uint32_t d) {
+    if (d == 0 || s == 0) return 0;
+    if (nb == 0) return 1;
+    EncodePlan p = make_plan(n, nb, s, d, false);
+    if (p.K == 0) return 0;
+    return p.stream_words + p.ws_words;
+}
+
+qsgd_status qsgd_quantize(const float *v, uint64_t n, uint32_t s, uint32_t d, uint64_t seed,
+                          int32_t *levels, float *norms, hipStream_t stream) {
+    return quantize_impl(v, n, nullptr, qsgd_num_buckets(n, d), s, d, seed, levels, norms, stream);
+}
+
+qsgd_status qsgd_encode(const float *v, uint64_t n, uint32_t s, uint32_t d, uint64_t seed,
+                        uint64_t *out, uint64_t *out_bits, uint64_t *bucket_bit_offsets,
+                        hipStream_t stream) {
+    return encode_impl(v, n, nullptr, qsgd_num_buckets(n, d), s, d, seed, out, out_bits,
+                       bucket_bit_offsets, stream);
+}
+
+qsgd_status qsgd_decode(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
+                        uint32_t s, uint32_t d, float *v_hat, hipStream_t stream) {
+    return decode_impl(in, bucket_bit_offsets, n, nullptr, qsgd_num_buckets(n, d), s, d, v_hat, stream);
+}
+
+uint64_t qsgd_num_buckets_ragged(const uint64_t *seg_len, uint32_t nseg, uint32_t d) {
+    if (d == 0 || (!seg_len && nseg)) return 0;
+    return ragged_count(seg_len, nseg, d, nullptr);
+}
+
+qsgd_status qsgd_ragged_bucket_table(const uint64_t *seg_len, uint32_t nseg, uint32_t d,
+                                     uint64_t *bucket_start, uint64_t nb) {
+    if (d == 0 || (!seg_len && nseg) || !bucket_start) return QSGD_ERR_INVALID_ARG;
+    if (ragged_count(seg_len, nseg, d, nullptr) != nb) return QSGD_ERR_INVALID_ARG;
+    ragged_count(seg_len, nseg, d, bucket_start);
+    return QSGD_OK;
+}
+
+qsgd_status qsgd_quantize_ragged(const float *v, uint64_t n, const uint64_t *bucket_start,
+                                 uint64_t nb, uint32_t s, uint32_t d, uint64_t seed,
+                                 int32_t *levels, float *norms, hipStream_t stream) {
+    if (!bucket_start && nb) return QSGD_ERR_INVALID_ARG;
+    if (nb == 0) return n == 0 ? QSGD_OK : QSGD_ERR_INVALID_ARG;
+    return quantize_impl(v, n, bucket_start, nb, s, d, seed, levels, norms, stream);
+}
+
+qsgd_status qsgd_encode_ragged(const float *v, uint64_t n, const uint64_t *bucket_start,
+                               uint64_t nb, uint32_t s, uint32_t d, uint64_t seed,
+                               uint64_t *out, uint64_t *out_bits, uint64_t *bucket_bit_offsets,
+                               hipStream_t stream) {
+    if (!bucket_start && nb) return QSGD_ERR_INVALID_ARG;
+    return encode_impl(v, n, bucket_start, nb, s, d, seed, out, out_bits, bucket_bit_offsets, stream);
+}
+
+qsgd_status qsgd_decode_ragged(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
+                               const uint64_t *bucket_start, uint64_t nb, uint32_t s, uint32_t d,
+                               float *v_hat, hipStream_t stream) {
+    if (!bucket_start && nb) return QSGD_ERR_INVALID_ARG;
+    return decode_impl(in, bucket_bit_offsets, n, bucket_start, nb, s, d, v_hat, stream);
+}
+
+}  // extern "C"

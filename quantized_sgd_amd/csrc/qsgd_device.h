@@ -1,0 +1,155 @@
+// Device-side building blocks of the QSGD compressor for gfx950 (CDNA4, wave64).
+//
+// Method: page "QSGD (Quantized Stochastic Gradient Descent) with Elias Coding",
+// definition paragraph (Q_s, Elias recursive coding of the quantized tuple) and
+// its claims on Elias coding (F = 32 bit norm) and bucketed training (paper
+// Section 3.3). The exact floating-point and stream-layout readings are stated in
+// include/qsgd.h and repeated at each helper below.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsgd {
+
+constexpr int kWG = 256;           // threads per workgroup: 4 wave64
+constexpr int kWaves = kWG / 64;
+constexpr int kCPT = 16;           // contiguous coordinates per thread
+constexpr int kTC = kWG * kCPT;    // coordinates per tile (4096)
+constexpr int kKMax = 512;         // buckets per tile at most
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32->64
+// multiplies with the round key bumped by the Weyl constants after each round.
+// Counter words 2 and 3 are zero in this library (the counter is the 64-bit
+// block index i >> 2), so the first round's second product is 0.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0,
+                                              uint32_t k1, uint32_t (&o)[4]) {
+    uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+        const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+        const uint32_t y2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+        x1 = (uint32_t)p1;
+        x3 = (uint32_t)p0;
+        x0 = y0;
+        x2 = y2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    o[0] = x0; o[1] = x1; o[2] = x2; o[3] = x3;
+}
+
+// Level k of one coordinate: r = RN32(|v| * c) with c = RN64(s / norm) of its
+// bucket, l = floor(r), p = r - l (exact), uniform u = (w >> 8) 2^-24, k = l + [u < p].
+// Each operation is one IEEE op (the library is built with -ffp-contract=off).
+__device__ __forceinline__ uint32_t qlevel(float v, double c, uint32_t w) {
+    const float a = fabsf(v);
+    const float r = (float)((double)a * c);
+    const float l = floorf(r);
+    const float p = r - l;
+    const float u = (float)(w >> 8) * 0x1p-24f;
+    return (uint32_t)l + (u < p ? 1u : 0u);
+}
+
+// Elias omega codeword of N >= 1 (Elias 1975), right-aligned: a final 0 bit, and
+// in front of it the binary forms of N, floor(log2 N), ... while the value is > 1.
+// At most 43 bits for N < 2^32.
+__device__ __forceinline__ uint64_t omega_code(uint32_t N, uint32_t &len) {
+    uint64_t code = 0;
+    uint32_t L = 1;
+    uint32_t m = N;
+    while (m > 1u) {
+        const uint32_t b = 32u - (uint32_t)__clz(m);
+        code |= (uint64_t)m << L;
+        L += b;
+        m = b - 1u;
+    }
+    len = L;
+    return code;
+}
+
+__device__ __forceinline__ uint32_t omega_len(uint32_t N) {
+    uint32_t L = 1;
+    uint32_t m = N;
+    while (m > 1u) {
+        const uint32_t b = 32u - (uint32_t)__clz(m);
+        L += b;
+        m = b - 1u;
+    }
+    return L;
+}
+
+// ---- wave/block scans (wave64, fixed combination order: deterministic) ----
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_incl_scan(T x, Op op) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const T y = __shfl_up(x, off, 64);
+        if (lane >= off) x = op(y, x);
+    }
+    return x;
+}
+
+// Exclusive block scan; `scratch` holds kWaves entries and must not be reused by
+// another scan before the next __syncthreads(). Returns the block total too.
+template <typename T, typename Op>
+__device__ __forceinline__ T block_excl_scan(T x, Op op, T identity, T *scratch, T &total) {
+    const T incl = wave_incl_scan(x, op);
+    const int lane = lane_id(), wave = wave_id();
+    if (lane == 63) scratch[wave] = incl;
+    __syncthreads();
+    T prefix = identity;
+    T tot = identity;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wave) prefix = op(prefix, scratch[w]);
+        tot = op(tot, scratch[w]);
+    }
+    T ex = __shfl_up(incl, 1, 64);
+    if (lane == 0) ex = identity;
+    total = tot;
+    return op(prefix, ex);
+}
+
+// Segmented inclusive scan of (flag, value) over the block in thread order:
+// S_j = v_j if f_j else S_{j-1} + v_j. Returns S_{j-1} (the exclusive value; 0
+// for thread 0). Used for bucket sums of squares that span several threads.
+__device__ __forceinline__ double block_seg_excl_sum(double v, int f, double *sv, int *sf) {
+    const int lane = lane_id(), wave = wave_id();
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double yv = __shfl_up(v, off, 64);
+        const int yf = __shfl_up(f, off, 64);
+        if (lane >= off) {
+            if (!f) v = yv + v;
+            f |= yf;
+        }
+    }
+    if (lane == 63) { sv[wave] = v; sf[wave] = f; }
+    __syncthreads();
+    double pv = 0.0;
+    for (int w = 0; w < wave; ++w) {  // combine the earlier waves in order
+        if (sf[w]) pv = sv[w]; else pv = pv + sv[w];
+    }
+    const double incl = f ? v : pv + v;
+    double ex = __shfl_up(incl, 1, 64);
+    if (lane == 0) ex = pv;
+    return ex;
+}
+
+// ---- agent-scope flags for the cross-workgroup protocol ----
+__device__ __forceinline__ uint64_t ld_acquire_agent(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace qsgd

@@ -1,0 +1,85 @@
+"""The C-ABI library loads and exports every entry point include/qsgd.h declares
+(no compute calls: this runs without a GPU). Host-only helpers (bucket counts,
+capacities, the ragged bucket table, argument checks) are exercised too."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import quantized_sgd_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "qsgd.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsgd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(q.LIB_PATH)
+    names = declared_functions()
+    assert len(names) == 13
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_library_is_built_for_gfx950():
+    data = open(q.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_host_helpers_match_oracle_bucketing():
+    for n, d in [(0, 4), (1, 1), (10, 3), (4096, 4096), (25_557_032, 512), (60_192_808, 4096)]:
+        assert q.num_buckets(n, d) == len(oracle.uniform_buckets(n, d)) - 1
+    rng = np.random.default_rng(3)
+    seg = rng.integers(0, 5000, size=60)
+    seg[[2, 9]] = 0
+    lay_host = np.zeros(1)
+    lib = q.lib()
+    sl = np.ascontiguousarray(seg.astype(np.uint64))
+    nb = lib.qsgd_num_buckets_ragged(sl.ctypes.data, len(sl), 512)
+    tab = np.zeros(nb + 1, np.uint64)
+    assert lib.qsgd_ragged_bucket_table(sl.ctypes.data, len(sl), 512, tab.ctypes.data, nb) == 0
+    assert np.array_equal(tab, oracle.ragged_buckets(seg, 512))
+    # a wrong nb is rejected
+    assert lib.qsgd_ragged_bucket_table(sl.ctypes.data, len(sl), 512, tab.ctypes.data, nb + 1) == 1
+
+
+def test_capacity_bounds_oracle_streams():
+    # the capacity helper bounds the worst case; check it against oracle streams
+    for n, d, s in [(4096, 4096, 64), (5000, 1, 1 << 24), (10000, 7, 3), (20000, 512, 16)]:
+        cap = q.encode_capacity_words(n, s, d)
+        v = np.full(n, 1.0, np.float32)
+        bst = oracle.uniform_buckets(n, d)
+        _, _, _, _, nbits = oracle.compress(v, bst, s, 1)
+        assert cap * 64 > nbits
+    assert q.encode_capacity_words(100, 4, 5000) == 0  # d beyond the tile: unsupported
+    assert q.max_bucket() == 4096
+
+
+def test_status_strings():
+    lib = q.lib()
+    assert lib.qsgd_status_string(0) == b"QSGD_OK"
+    assert lib.qsgd_status_string(1) == b"QSGD_ERR_INVALID_ARG"
+
+
+def test_no_cpu_fallback_in_product(monkeypatch, tmp_path):
+    # the binding refuses to run without the HIP library
+    monkeypatch.setattr(q, "_lib", None)
+    monkeypatch.setattr(q, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        q.lib()
+
+
+def test_product_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "quantized_sgd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "qsgd_oracle" not in text, f
