@@ -20,7 +20,7 @@ ARCH = os.environ.get("QSGD_OFFLOAD_ARCH", "gfx950")
 def hipcc_command(out: str = LIB, extra=()):
     return [
         "/opt/rocm/bin/hipcc", "-O3", "-std=c++17", f"--offload-arch={ARCH}",
-        "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+        "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-fno-strict-aliasing",
         "-fno-gpu-flush-denormals-to-zero",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",

@@ -164,8 +164,13 @@ qsgd_status decode_impl(const uint64_t *in, const uint64_t *offsets, uint64_t n,
     DecodeParams D{};
     D.in = in; D.offsets = offsets; D.bstart = bstart; D.v_hat = v_hat;
     D.n = n; D.nb = nb; D.s = s; D.d = d;
-    const uint64_t want = (nb + kWaves - 1) / kWaves;
-    const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, 256ull * 16);
+    // lanes per bucket: about one per 64 coordinates, a power of two in [1, 64]
+    uint32_t team = 1;
+    while (team < 64 && (uint64_t)team * 2 * 64 <= d) team *= 2;
+    D.team = team;
+    const uint64_t groups = (nb + (64 / team) - 1) / (64 / team);
+    const uint64_t want = (groups + kWaves - 1) / kWaves;
+    const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, 256ull * 8);
     if (bstart)
         hipLaunchKernelGGL(decode_kernel<true>, dim3(blocks), dim3(kWG), 0, stream, D);
     else
