@@ -72,7 +72,7 @@ const char *qsgd_status_string(qsgd_status status);
 uint64_t qsgd_num_buckets(uint64_t n, uint32_t d);
 
 /* Largest bucket length that qsgd_quantize / qsgd_encode accept (4096 in this
- * build); larger d returns QSGD_ERR_UNSUPPORTED. Decode accepts any d. */
+ * build); larger d returns QSGD_ERR_UNSUPPORTED. Decode accepts d <= 2^24. */
 uint32_t qsgd_max_bucket(void);
 
 /* Number of uint64 words the `out` buffer of qsgd_encode must hold for (n, s, d):
@@ -112,8 +112,10 @@ qsgd_status qsgd_encode(const float *v, uint64_t n, uint32_t s, uint32_t d, uint
  * page, definition paragraph).
  *   in                  stream words written by qsgd_encode (read-only).
  *   bucket_bit_offsets  [ceil(n/d) + 1] the offsets written by qsgd_encode.
- *   v_hat               [n] fp32 output; every element is written.
- * n, s, d must be those of the encode call.
+ *   v_hat               [n] fp32 output, 16-byte aligned; every element is written
+ *                       exactly once.
+ * n, s, d must be those of the encode call; d <= 2^24 (larger d returns
+ * QSGD_ERR_UNSUPPORTED).
  */
 qsgd_status qsgd_decode(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
                         uint32_t s, uint32_t d, float *v_hat, hipStream_t stream);

@@ -160,7 +160,8 @@ qsgd_status decode_impl(const uint64_t *in, const uint64_t *offsets, uint64_t n,
     qsgd_status st = check_common(nullptr, s, d);
     if (st != QSGD_OK) return st;
     if (n == 0 || nb == 0) return QSGD_OK;
-    if (!in || !offsets || !v_hat) return QSGD_ERR_INVALID_ARG;
+    if (!in || !offsets || !v_hat || !aligned16(v_hat)) return QSGD_ERR_INVALID_ARG;
+    if (d > (1u << 24)) return QSGD_ERR_UNSUPPORTED;
     DecodeParams D{};
     D.in = in; D.offsets = offsets; D.bstart = bstart; D.v_hat = v_hat;
     D.n = n; D.nb = nb; D.s = s; D.d = d;
@@ -171,10 +172,11 @@ qsgd_status decode_impl(const uint64_t *in, const uint64_t *offsets, uint64_t n,
     const uint64_t groups = (nb + (64 / team) - 1) / (64 / team);
     const uint64_t want = (groups + kWaves - 1) / kWaves;
     const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, 256ull * 8);
+    const size_t lds = decode_lds_bytes();
     if (bstart)
-        hipLaunchKernelGGL(decode_kernel<true>, dim3(blocks), dim3(kWG), 0, stream, D);
+        hipLaunchKernelGGL(decode_kernel<true>, dim3(blocks), dim3(kWG), lds, stream, D);
     else
-        hipLaunchKernelGGL(decode_kernel<false>, dim3(blocks), dim3(kWG), 0, stream, D);
+        hipLaunchKernelGGL(decode_kernel<false>, dim3(blocks), dim3(kWG), lds, stream, D);
     return launch_status();
 }
 
