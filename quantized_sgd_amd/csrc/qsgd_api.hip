@@ -41,8 +41,8 @@ struct EncodePlan {
     uint64_t ntiles = 0;
     uint64_t stream_words = 0;  // capacity reserved for the stream
     uint64_t ws_words = 0;      // workspace words after the stream
-    uint32_t stage_words = 0;
     uint32_t obuf_words = 0;
+    bool table = false;         // record codes from the LDS table (s <= kTabS)
     size_t lds_bytes = 0;
 };
 
@@ -57,33 +57,36 @@ EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool align
     p.stream_words = (twice_bits + 127) / 128 + 1;
     p.stream_words = (p.stream_words + 31) & ~(uint64_t)31;
     p.ws_words = 2 * p.ntiles + 1;
-    // LDS: staging bound per tile (records of at most 12 + Ls bits beside the
-    // pending first gap, 32 bits per bucket norm, word rounding per thread), the
-    // output window (adds the pending gap codes and a spare word at each end).
+    // the tile's word window: records of at most 12 + Ls bits besides the
+    // pending first gaps (at most |omega(d)| bits each, one per thread), 32 bits
+    // per bucket norm, a spare word at each end
     const uint64_t Ld = host_omega_len(std::max<uint32_t>(d, 1));
-    const uint64_t stage_bits = (uint64_t)kTC * (12 + Ls) + 32ull * p.K;
-    p.stage_words = (uint32_t)((stage_bits + 63) / 64 + kWG);
-    p.obuf_words = (uint32_t)((stage_bits + (uint64_t)kWG * Ld + 63) / 64 + 3);
-    size_t off = (size_t)p.stage_words * 8 + (size_t)p.obuf_words * 8;
-    off += (size_t)p.K * 8 + kWaves * 8;
-    off = (off + (size_t)(p.K + 1) * 4 + 7) & ~(size_t)7;
-    off = (off + (size_t)p.K * 4 + 7) & ~(size_t)7;
-    off = (off + kWaves * 4 + 7) & ~(size_t)7;
-    off = (off + (size_t)p.K * 4 + 7) & ~(size_t)7;
-    off += (size_t)kWG * 4;
-    p.lds_bytes = off;
+    const uint64_t tile_bits = (uint64_t)kTC * (12 + Ls) + 32ull * p.K + (uint64_t)kWG * Ld;
+    p.obuf_words = (uint32_t)((tile_bits + 63) / 64 + 3);
+    p.table = s <= kTabS;
+    p.lds_bytes = EncodeLayout(p.obuf_words, p.table ? code_table_entries(s) : 0u, p.K).total;
     return p;
 }
 
-size_t quantize_lds_bytes(const EncodePlan &p) {
-    // quantize_kernel carves the same layout with empty staging / output areas
-    size_t off = (size_t)p.K * 8 + kWaves * 8;
-    off = (off + (size_t)(p.K + 1) * 4 + 7) & ~(size_t)7;
-    off = (off + (size_t)p.K * 4 + 7) & ~(size_t)7;
-    off = (off + kWaves * 4 + 7) & ~(size_t)7;
-    off = (off + (size_t)p.K * 4 + 7) & ~(size_t)7;
-    off += (size_t)kWG * 4;
-    return off;
+size_t quantize_lds_bytes(const EncodePlan &p) { return EncodeLayout(0, 0, p.K).total; }
+
+// Resident workgroups of an encode kernel on the current device (cached).
+template <typename K>
+uint32_t resident_blocks(K kernel, size_t lds) {
+    struct Entry { const void *k; size_t lds; int dev; uint32_t blocks; };
+    static Entry cache[16];
+    static int used = 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].k == (const void *)kernel && cache[i].lds == lds && cache[i].dev == dev)
+            return cache[i].blocks;
+    int cus = 0, per_cu = 0;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWG, lds);
+    uint32_t blocks = (uint32_t)std::max(1, cus) * (uint32_t)std::max(1, per_cu);
+    if (used < 16) cache[used++] = Entry{(const void *)kernel, lds, dev, blocks};
+    return blocks;
 }
 
 constexpr size_t kMaxLds = 64 * 1024;
@@ -113,7 +116,7 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
     QsgdParams P{};
     P.v = v; P.n = n; P.nb = nb; P.bstart = bstart; P.seed = seed; P.s = s; P.d = d;
     P.K = p.K; P.ntiles = (uint32_t)p.ntiles; P.levels = levels; P.norms = norms;
-    P.stage_words = 0; P.obuf_words = 0;
+    P.obuf_words = 0;
     const size_t lds = quantize_lds_bytes(p);
     if (ragged)
         hipLaunchKernelGGL(quantize_kernel<true>, dim3((uint32_t)p.ntiles), dim3(kWG), lds, stream, P);
@@ -144,14 +147,19 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     P.status = out + p.stream_words;
     P.carry = P.status + p.ntiles;
     P.ticket = reinterpret_cast<uint32_t *>(P.carry + p.ntiles);
-    P.stage_words = p.stage_words; P.obuf_words = p.obuf_words;
+    P.obuf_words = p.obuf_words;
     const uint32_t init_blocks = (uint32_t)std::min<uint64_t>((p.ntiles + 255) / 256, 1024);
     hipLaunchKernelGGL(encode_init_kernel, dim3(std::max<uint32_t>(init_blocks, 1)), dim3(256), 0,
                        stream, P.status, P.carry, P.ticket, (uint32_t)p.ntiles);
-    if (ragged)
-        hipLaunchKernelGGL(encode_kernel<true>, dim3((uint32_t)p.ntiles), dim3(kWG), p.lds_bytes, stream, P);
-    else
-        hipLaunchKernelGGL(encode_kernel<false>, dim3((uint32_t)p.ntiles), dim3(kWG), p.lds_bytes, stream, P);
+    auto launch = [&](auto kernel) {
+        const uint32_t blocks = (uint32_t)std::min<uint64_t>(p.ntiles, resident_blocks(kernel, p.lds_bytes));
+        hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), p.lds_bytes, stream, P);
+    };
+    if (ragged) {
+        if (p.table) launch(encode_kernel<true, true>); else launch(encode_kernel<true, false>);
+    } else {
+        if (p.table) launch(encode_kernel<false, true>); else launch(encode_kernel<false, false>);
+    }
     return launch_status();
 }
 

@@ -21,7 +21,13 @@ constexpr int kKMax = 512;         // buckets per tile at most
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32->64
 // multiplies with the round key bumped by the Weyl constants after each round.
 // Counter words 2 and 3 are zero in this library (the counter is the 64-bit
-// block index i >> 2), so the first round's second product is 0.
+// block index i >> 2), so the first round's second product is 0. The two
+// three-way XORs of a round are single v_bitop3_b32 instructions on gfx950
+// (truth table 0x96 = a ^ b ^ c).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0,
                                               uint32_t k1, uint32_t (&o)[4]) {
     uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
@@ -29,8 +35,8 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
     for (int r = 0; r < 10; ++r) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
-        const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
-        const uint32_t y2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+        const uint32_t y0 = xor3((uint32_t)(p1 >> 32), x1, k0);
+        const uint32_t y2 = xor3((uint32_t)(p0 >> 32), x3, k1);
         x1 = (uint32_t)p1;
         x3 = (uint32_t)p0;
         x0 = y0;
@@ -145,7 +151,7 @@ __device__ __forceinline__ double block_seg_excl_sum(double v, int f, double *sv
 }
 
 // ---- agent-scope flags for the cross-workgroup protocol ----
-__device__ __forceinline__ uint64_t ld_acquire_agent(const uint64_t *p) {
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_agent(uint64_t *p, uint64_t v) {

@@ -4,96 +4,115 @@
 // definition paragraph (Q_s and the Elias-coded tuple of norm, signs, non-zero
 // gaps and levels) and the claim on Elias coding (F = 32 bit norm).
 //
-// Encode, per tile (a run of whole buckets, <= 4096 coordinates, one workgroup):
+// Encode, per tile (a run of whole buckets, <= 4096 coordinates, one workgroup;
+// workgroups are persistent and take tiles in order from a work counter):
 //   1. load v once from HBM, per-bucket norms, Philox rounding (qsgd_front.h);
-//   2. each thread stages the records of its 16 coordinates in LDS: the 32-bit
-//      norm at a bucket start, and omega(gap) | sign | omega(k) per non-zero;
-//      the gap of a thread's first non-zero, when its origin lies in an earlier
-//      thread, is resolved after an exclusive max-scan of "last marker" positions;
+//   2. each thread looks up the code of every coordinate's record -- the 32-bit
+//      norm at a bucket start, and omega(gap) | sign | omega(k) per non-zero --
+//      in a table of all records with gap <= 16 and k <= s (gaps inside one
+//      thread's 16 coordinates never exceed 16) and sums their lengths. The gap
+//      of a thread's first non-zero, when its origin lies in an earlier thread,
+//      is resolved after an exclusive max-scan of "last marker" positions;
 //   3. an exclusive sum-scan of per-thread bit counts gives each thread's offset
 //      in the tile and the tile's size T;
 //   4. decoupled lookback over earlier tiles' status words (agent-scope atomics,
 //      flag and value packed in one 64-bit word) gives the tile's stream offset;
-//   5. the tile's bits are assembled into 64-bit words in LDS and stored with
-//      coalesced 8-byte stores. The word shared with the previous tile is
-//      completed with that tile's published "carry" (its partial last word); the
-//      tile's own partial last word is published the same way for the next tile.
-// Every output word is written by exactly one tile; no pass re-reads v.
+//   5. every record is OR-ed into the tile's 64-bit words in LDS at its final
+//      bit position, and the words are stored with coalesced 8-byte stores. The
+//      word shared with the previous tile is completed with that tile's
+//      published "carry" (its partial last word); the tile's own partial last
+//      word is published the same way for the next tile.
+// Every output word is written by exactly one tile; v is read once.
 #pragma once
 
 #include "qsgd_front.h"
 
 namespace qsgd {
 
-// Appends bit strings MSB-first into 64-bit LDS words.
-struct Stager {
-    uint64_t *w;
-    uint64_t acc;
-    uint32_t nacc;
-    uint32_t widx;
-    __device__ __forceinline__ uint32_t bitpos() const { return widx * 64u + nacc; }
-    // bits right-aligned, 1 <= len <= 64
-    __device__ __forceinline__ void put(uint64_t bits, uint32_t len) {
-        const uint32_t total = nacc + len;
-        if (total < 64u) {
-            acc |= bits << (64u - total);
-            nacc = total;
-        } else {
-            const uint32_t over = total - 64u;
-            acc |= bits >> over;
-            w[widx++] = acc;
-            acc = over ? bits << (64u - over) : 0ull;
-            nacc = over;
-        }
-    }
-    __device__ __forceinline__ void flush() {
-        if (nacc) w[widx] = acc;
-    }
-};
+// Record code table for s <= kTabS: entry (code << 5) | length of
+// omega(g) | sign | omega(k) for g in [0, 16] (g = 0: no gap code) and k in
+// [0, s] (k = 0: no record, entry 0). Index ((g (s + 1) + k) << 1) | sign.
+constexpr uint32_t kTabS = 64;
+constexpr uint32_t kTabG = 17;
 
-// OR a left-aligned 64-bit word into the LDS bit window at bit position pos.
-__device__ __forceinline__ void or_bits(uint64_t *buf, uint32_t pos, uint64_t word) {
+__host__ __device__ constexpr uint32_t code_table_entries(uint32_t s) { return kTabG * (s + 1) * 2; }
+
+__device__ inline void build_code_table(uint32_t *rt, uint32_t s) {
+    const uint32_t n = code_table_entries(s);
+    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const uint32_t neg = i & 1u;
+        const uint32_t k = (i >> 1) % (s + 1);
+        const uint32_t g = (i >> 1) / (s + 1);
+        uint32_t e = 0;
+        if (k) {
+            uint32_t Lk;
+            const uint64_t kc = omega_code(k, Lk);
+            uint64_t code = ((uint64_t)neg << Lk) | kc;
+            uint32_t len = Lk + 1;
+            if (g) {
+                uint32_t Lg;
+                const uint64_t gc = omega_code(g, Lg);
+                code |= gc << len;
+                len += Lg;
+            }
+            e = ((uint32_t)code << 5) | len;
+        }
+        rt[i] = e;
+    }
+}
+
+// OR a left-aligned bit string (len <= 64 bits at the top of `word`) into the
+// LDS word window at bit position pos.
+__device__ __forceinline__ void or_bits(uint64_t *buf, uint32_t pos, uint64_t word, uint32_t len) {
     const uint32_t idx = pos >> 6, sh = pos & 63u;
     atomicOr(reinterpret_cast<unsigned long long *>(buf + idx), (unsigned long long)(word >> sh));
-    if (sh) {
-        const uint64_t lo = word << (64u - sh);
-        if (lo) atomicOr(reinterpret_cast<unsigned long long *>(buf + idx + 1), (unsigned long long)lo);
-    }
+    if (sh + len > 64u)
+        atomicOr(reinterpret_cast<unsigned long long *>(buf + idx + 1),
+                 (unsigned long long)(word << (64u - sh)));
 }
 
 struct EncodeLds {
     FrontLds f;
-    uint64_t *stage;
     uint64_t *obuf;
-    uint32_t *bpos;  // [K] staged bit position of each bucket's norm
-    uint32_t *tb;    // [kWG] per-thread offset of the staged bits within the tile
+    uint32_t *rt;   // record code table (table path)
 };
 
-__device__ __forceinline__ size_t align8(size_t x) { return (x + 7) & ~(size_t)7; }
+__host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// Carves the dynamic LDS block. K = P.K (the largest tile).
-__device__ __forceinline__ EncodeLds carve_encode_lds(unsigned char *smem, const QsgdParams &P) {
+// Dynamic LDS layout shared by host and device: [obuf][rt][cb][segv][bs][nrm][segf].
+struct EncodeLayout {
+    size_t obuf, rt, cb, segv, bs, nrm, segf, total;
+    __host__ __device__ EncodeLayout(uint32_t obuf_words, uint32_t rt_entries, uint32_t K) {
+        size_t off = 0;
+        obuf = off; off = align16(off + (size_t)obuf_words * 8);
+        rt = off;   off = align16(off + (size_t)rt_entries * 4);
+        cb = off;   off = align16(off + (size_t)K * 8);
+        segv = off; off = align16(off + kWaves * 8);
+        bs = off;   off = align16(off + (size_t)(K + 1) * 4);
+        nrm = off;  off = align16(off + (size_t)K * 4);
+        segf = off; off = align16(off + kWaves * 4);
+        total = off;
+    }
+};
+
+__device__ __forceinline__ EncodeLds carve_encode_lds(unsigned char *smem, const QsgdParams &P,
+                                                      uint32_t rt_entries) {
+    const EncodeLayout lay(P.obuf_words, rt_entries, P.K);
     EncodeLds L;
-    size_t off = 0;
-    L.stage = reinterpret_cast<uint64_t *>(smem + off); off += (size_t)P.stage_words * 8;
-    L.obuf = reinterpret_cast<uint64_t *>(smem + off); off += (size_t)P.obuf_words * 8;
-    L.f.cb = reinterpret_cast<double *>(smem + off); off += (size_t)P.K * 8;
-    L.f.segv = reinterpret_cast<double *>(smem + off); off += kWaves * 8;
-    L.f.bs = reinterpret_cast<int32_t *>(smem + off); off = align8(off + (size_t)(P.K + 1) * 4);
-    L.f.nrm = reinterpret_cast<float *>(smem + off); off = align8(off + (size_t)P.K * 4);
-    L.f.segf = reinterpret_cast<int *>(smem + off); off = align8(off + kWaves * 4);
-    L.bpos = reinterpret_cast<uint32_t *>(smem + off); off = align8(off + (size_t)P.K * 4);
-    L.tb = reinterpret_cast<uint32_t *>(smem + off);
+    L.obuf = reinterpret_cast<uint64_t *>(smem + lay.obuf);
+    L.rt = reinterpret_cast<uint32_t *>(smem + lay.rt);
+    L.f.cb = reinterpret_cast<double *>(smem + lay.cb);
+    L.f.segv = reinterpret_cast<double *>(smem + lay.segv);
+    L.f.bs = reinterpret_cast<int32_t *>(smem + lay.bs);
+    L.f.nrm = reinterpret_cast<float *>(smem + lay.nrm);
+    L.f.segf = reinterpret_cast<int *>(smem + lay.segf);
     return L;
 }
-
-// Bytes of dynamic LDS the encode / quantize kernels need (host side mirror in
-// the API file).
 
 template <bool RAGGED>
 __global__ __launch_bounds__(kWG) void quantize_kernel(QsgdParams P) {
     extern __shared__ __align__(16) unsigned char smem[];
-    EncodeLds L = carve_encode_lds(smem, P);
+    EncodeLds L = carve_encode_lds(smem, P, 0);
     const uint32_t tile = blockIdx.x;
     const Tile t = tile_geometry<RAGGED>(P, tile);
     fill_bucket_starts<RAGGED>(P, t, L.f);
@@ -148,192 +167,236 @@ constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kValMask = (1ull << 62) - 1;
 
-template <bool RAGGED>
+// Code and length of one record, table path (g <= 16, k <= s <= kTabS) or
+// arithmetic path. g = 0 means "no gap code" (resolved later).
+template <bool TABLE>
+__device__ __forceinline__ uint32_t record_entry(const uint32_t *rt, uint32_t s1, uint32_t g, uint32_t k,
+                                                 uint32_t neg, uint64_t &code) {
+    if (TABLE) {
+        const uint32_t e = rt[((g * s1 + k) << 1) | neg];
+        code = e >> 5;
+        return e & 31u;
+    }
+    if (k == 0) { code = 0; return 0; }
+    uint32_t Lk;
+    const uint64_t kc = omega_code(k, Lk);
+    code = ((uint64_t)neg << Lk) | kc;
+    uint32_t len = Lk + 1;
+    if (g) {
+        uint32_t Lg;
+        const uint64_t gc = omega_code(g, Lg);
+        code |= gc << len;
+        len += Lg;
+    }
+    return len;  // <= 11 + 1 + 36 = 48 bits
+}
+
+template <bool RAGGED, bool TABLE>
 __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ uint32_t sh_tile;
     __shared__ uint64_t sh_base;
     __shared__ int sh_mx[kWaves];
-    __shared__ uint32_t sh_ub[kWaves];
     __shared__ uint32_t sh_bits[kWaves];
 
-    EncodeLds L = carve_encode_lds(smem, P);
+    const uint32_t rt_entries = TABLE ? code_table_entries(P.s) : 0u;
+    EncodeLds L = carve_encode_lds(smem, P, rt_entries);
+    if (TABLE) build_code_table(L.rt, P.s);
     const int j = (int)threadIdx.x;
-    const int lane = lane_id(), wave = wave_id();
-    if (j == 0) sh_tile = atomicAdd(P.ticket, 1u);
-    __syncthreads();
-    const uint32_t tile = sh_tile;
-    const Tile t = tile_geometry<RAGGED>(P, tile);
-    fill_bucket_starts<RAGGED>(P, t, L.f);
-    ThreadCoords c;
-    load_coords(P, t, c);
-    __syncthreads();
-    bucket_norms<RAGGED>(P, t, L.f, c);
-    ThreadLevels lv;
-    quantize_coords(P, t, L.f, c, lv);
+    const int lane = lane_id();
+    // the wave index as a scalar, so that branches on it are uniform to the compiler
+    const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+    const uint32_t s1 = P.s + 1;
 
-    // ---- events, markers and staging bounds ----
-    const uint32_t ev = lv.nz | lv.bst;
-    int marker = INT_MIN;
-    if (ev) {
-        const int h = 31 - __clz(ev);
-        marker = j * kCPT + h - (((lv.nz >> h) & 1u) ? 0 : 1);
-    }
-    const uint32_t Ls = omega_len(P.s);
-    const uint32_t ub_bits = (uint32_t)__popc(lv.nz) * (12u + Ls) + 32u * (uint32_t)__popc(lv.bst);
-    const uint32_t ub_words = (ub_bits + 63u) >> 6;
-    // fused exclusive scans: max of markers, sum of staging words
-    int mi = wave_incl_scan(marker, [](int a, int b) { return a > b ? a : b; });
-    uint32_t ui = wave_incl_scan(ub_words, [](uint32_t a, uint32_t b) { return a + b; });
-    if (lane == 63) { sh_mx[wave] = mi; sh_ub[wave] = ui; }
-    __syncthreads();
-    int mpre = INT_MIN;
-    uint32_t upre = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        if (w < wave) {
-            mpre = mpre > sh_mx[w] ? mpre : sh_mx[w];
-            upre += sh_ub[w];
+    for (;;) {
+        // Every wait and every single-lane section below sits in wave-uniform
+        // control flow (decisions on readfirstlane values): a lane-divergent
+        // spin loop inside this persistent loop lets the compiler run the next
+        // iteration's barrier for some lanes of wave 0 before the waiting lane
+        // has left, which desynchronises the workgroup's barriers.
+        if (wave == 0) {
+            uint32_t tk = 0;
+            if (lane == 0) tk = atomicAdd(P.ticket, 1u);
+            tk = __builtin_amdgcn_readfirstlane(tk);
+            if (lane == 0) sh_tile = tk;
         }
-    }
-    int mex = __shfl_up(mi, 1, 64);
-    uint32_t uex = __shfl_up(ui, 1, 64);
-    if (lane == 0) { mex = INT_MIN; uex = 0; }
-    mex = mex > mpre ? mex : mpre;
-    uex += upre;
+        __syncthreads();  // also separates this tile's LDS use from the previous one
+        const uint32_t tile = __builtin_amdgcn_readfirstlane(sh_tile);
+        if (tile >= P.ntiles) break;
+        const Tile t = tile_geometry<RAGGED>(P, tile);
+        fill_bucket_starts<RAGGED>(P, t, L.f);
+        ThreadCoords c;
+        load_coords(P, t, c);
+        __syncthreads();
+        bucket_norms<RAGGED>(P, t, L.f, c);
+        ThreadLevels lv;
+        quantize_coords(P, t, L.f, c, lv);
 
-    // ---- stage records ----
-    Stager st{L.stage + uex, 0ull, 0u, 0u};
-    int prev = 0;
-    int have = 0;
-    int pendx = -1;
-    int kb = c.kf;
-    if (c.vx0 < c.vx1 && ((lv.bst >> (c.vx0 - j * kCPT)) & 1u)) kb -= 1;
+        // ---- phase 1: record codes, bit count, last marker ----
+        uint32_t ec[kCPT];
+        uint64_t ecx[TABLE ? 1 : kCPT];
+        uint32_t r = 0;
+        int prev = 0;
+        int have = 0;
+        int pendx = -1;
 #pragma unroll
-    for (int q = 0; q < kCPT; ++q) {
-        const int x = j * kCPT + q;
-        if ((lv.bst >> q) & 1u) {
-            ++kb;
-            L.bpos[kb] = st.bitpos();
-            st.put((uint64_t)__float_as_uint(L.f.nrm[kb]), 32u);
-            prev = x - 1;
-            have = 1;
-        }
-        if ((lv.nz >> q) & 1u) {
-            uint32_t Lk;
-            uint64_t kc = omega_code(lv.k[q], Lk);
-            kc |= (uint64_t)((lv.neg >> q) & 1u) << Lk;
-            Lk += 1u;
-            if (have) {
-                uint32_t Lg;
-                const uint64_t gc = omega_code((uint32_t)(x - prev), Lg);
-                if (Lg + Lk <= 64u) {
-                    st.put((gc << Lk) | kc, Lg + Lk);
-                } else {
-                    st.put(gc, Lg);
-                    st.put(kc, Lk);
-                }
-            } else {
-                pendx = x;
+        for (int q = 0; q < kCPT; ++q) {
+            const int x = j * kCPT + q;
+            if ((lv.bst >> q) & 1u) {
+                r += 32u;
+                prev = x - 1;
                 have = 1;
-                st.put(kc, Lk);
             }
-            prev = x;
+            const uint32_t k = lv.k[q];
+            const uint32_t g = have ? (uint32_t)(x - prev) : 0u;
+            uint64_t code;
+            const uint32_t len = record_entry<TABLE>(L.rt, s1, g, k, (lv.neg >> q) & 1u, code);
+            if (TABLE) ec[q] = ((uint32_t)code << 5) | len;
+            else { ec[q] = len; ecx[TABLE ? 0 : q] = code; }
+            r += len;
+            if (k) {
+                if (!have) pendx = x;
+                prev = x;
+                have = 1;
+            }
         }
-    }
-    st.flush();
-    const uint32_t staged = st.bitpos();
-    uint32_t Lp = 0;
-    uint64_t pc = 0;
-    if (pendx >= 0) pc = omega_code((uint32_t)(pendx - mex), Lp);
-    const uint32_t bits = staged + Lp;
+        const int marker = have ? prev : INT_MIN;
 
-    // ---- tile scan of bit counts ----
-    uint32_t bi = wave_incl_scan(bits, [](uint32_t a, uint32_t b) { return a + b; });
-    if (lane == 63) sh_bits[wave] = bi;
-    __syncthreads();
-    uint32_t bpre = 0, T = 0;
+        // ---- exclusive max-scan of markers: origin of the pending first gap ----
+        int mi = wave_incl_scan(marker, [](int a, int b) { return a > b ? a : b; });
+        if (lane == 63) sh_mx[wave] = mi;
+        __syncthreads();
+        int mpre = INT_MIN;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        if (w < wave) bpre += sh_bits[w];
-        T += sh_bits[w];
-    }
-    uint32_t off = __shfl_up(bi, 1, 64);
-    if (lane == 0) off = 0;
-    off += bpre;
+        for (int w = 0; w < kWaves; ++w)
+            if (w < wave) mpre = mpre > sh_mx[w] ? mpre : sh_mx[w];
+        int mex = __shfl_up(mi, 1, 64);
+        if (lane == 0) mex = INT_MIN;
+        mex = mex > mpre ? mex : mpre;
+        uint32_t Lp = 0;
+        uint64_t pc = 0;
+        if (pendx >= 0) pc = omega_code((uint32_t)(pendx - mex), Lp);
+        const uint32_t bits = r + Lp;
 
-    // ---- decoupled lookback: stream offset of this tile ----
-    if (j == 0) {
-        uint64_t excl = 0;
-        if (tile == 0) {
-            st_agent(&P.status[0], kFlagIncl | (uint64_t)T);
-        } else {
-            st_agent(&P.status[tile], kFlagAgg | (uint64_t)T);
+        // ---- tile scan of bit counts ----
+        const uint32_t bi = wave_incl_scan(bits, [](uint32_t a, uint32_t b) { return a + b; });
+        if (lane == 63) sh_bits[wave] = bi;
+        __syncthreads();
+        uint32_t bpre = 0, T = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            if (w < wave) bpre += sh_bits[w];
+            T += sh_bits[w];
+        }
+        uint32_t off = __shfl_up(bi, 1, 64);
+        if (lane == 0) off = 0;
+        off += bpre;
+
+        // ---- decoupled lookback: stream offset of this tile ----
+        // wave 0 inspects 64 predecessors at once (lane l: tile - 1 - l)
+        if (wave == 0) {
+            if (lane == 0)
+                st_agent(&P.status[tile], (tile == 0 ? kFlagIncl : kFlagAgg) | (uint64_t)T);
+            uint64_t excl = 0;
             int64_t i = (int64_t)tile - 1;
-            while (true) {
-                const uint64_t w = ld_acquire_agent(&P.status[i]);
+            while (i >= 0) {
+                const int64_t idx = i - lane;
+                const uint64_t w = idx >= 0 ? ld_agent(&P.status[idx]) : kFlagIncl;
                 const uint64_t f = w & ~kValMask;
-                if (f == 0) { __builtin_amdgcn_s_sleep(1); continue; }
-                excl += w & kValMask;
-                if (f == kFlagIncl) break;
-                --i;
+                const uint64_t incl = __ballot(f == kFlagIncl);
+                const uint64_t zero = __ballot(f == 0);
+                // lanes up to (and including) the nearest inclusive one, if all ready
+                const int pfx = incl ? __builtin_ctzll(incl) : 63;
+                const uint64_t need = (pfx == 63) ? ~0ull : ((2ull << pfx) - 1ull);
+                if ((zero & need) != 0) {
+                    __builtin_amdgcn_s_sleep(1);
+                    continue;
+                }
+                uint64_t v = (lane <= pfx) ? (w & kValMask) : 0ull;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+                excl += v;
+                if (incl) break;
+                i -= 64;
             }
-            st_agent(&P.status[tile], kFlagIncl | (excl + (uint64_t)T));
-        }
-        sh_base = excl;
-    }
-    L.tb[j] = off + Lp;
-    __syncthreads();
-    const uint64_t base = sh_base;
-
-    // ---- bucket offsets ----
-    for (uint32_t b = threadIdx.x; b < t.K; b += kWG)
-        P.offsets[t.b0 + b] = base + L.tb[L.f.bs[b] >> 4] + L.bpos[b];
-    const bool last = (tile == P.ntiles - 1);
-    if (last && j == 0) {
-        P.offsets[P.nb] = base + T;
-        *P.out_bits = base + T;
-    }
-
-    // ---- assemble the tile's words in LDS ----
-    const uint32_t head = (uint32_t)(base & 63u);
-    const uint32_t W = (head + T + 63u) >> 6;
-    for (uint32_t w = threadIdx.x; w < W; w += kWG) L.obuf[w] = 0;
-    __syncthreads();
-    uint32_t pos = head + off;
-    if (Lp) or_bits(L.obuf, pos, pc << (64u - Lp));
-    pos += Lp;
-    const uint32_t nw = (staged + 63u) >> 6;
-    for (uint32_t i = 0; i < nw; ++i) or_bits(L.obuf, pos + 64u * i, L.stage[uex + i]);
-    __syncthreads();
-
-    // ---- store: interior words by all threads, edge words by thread 0 ----
-    uint64_t *dst = P.out + (base >> 6);
-    for (uint32_t w = 1 + threadIdx.x; w + 1 < W; w += kWG) dst[w] = L.obuf[w];
-    if (j == 0) {
-        const bool head_shared = head != 0;
-        const bool tail_partial = ((base + T) & 63u) != 0;
-        if (W > 1) {
-            if (tail_partial && !last) {
-                st_agent(&P.carry[tile], L.obuf[W - 1] | 1ull);
-            } else {
-                dst[W - 1] = L.obuf[W - 1];
-                st_agent(&P.carry[tile], 1ull);
+            excl = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(excl >> 32)) << 32) |
+                   (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)excl);
+            if (lane == 0) {
+                if (tile != 0) st_agent(&P.status[tile], kFlagIncl | (excl + (uint64_t)T));
+                sh_base = excl;
             }
         }
-        uint64_t hw = L.obuf[0];
-        if (head_shared) {
-            uint64_t cw;
-            while (((cw = ld_acquire_agent(&P.carry[tile - 1])) & 1ull) == 0) __builtin_amdgcn_s_sleep(1);
-            hw |= cw & ~1ull;
+        __syncthreads();
+        const uint64_t base = sh_base;
+        const uint32_t head = (uint32_t)(base & 63u);
+        const uint32_t W = (head + T + 63u) >> 6;
+        for (uint32_t w = threadIdx.x; w < W; w += kWG) L.obuf[w] = 0;
+        const bool last = (tile == P.ntiles - 1);
+        if (last && j == 0) {
+            P.offsets[P.nb] = base + T;
+            *P.out_bits = base + T;
         }
-        if (W > 1) {
-            dst[0] = hw;
-        } else if (tail_partial && !last) {
-            st_agent(&P.carry[tile], hw | 1ull);
-        } else {
-            dst[0] = hw;
-            st_agent(&P.carry[tile], 1ull);
+        __syncthreads();
+
+        // ---- phase 2: OR every record into the tile's words at its position ----
+        uint32_t p = head + off;
+        if (Lp) or_bits(L.obuf, p, pc << (64u - Lp), Lp);
+        p += Lp;
+        int kb = c.kf;
+        if (c.vx0 < c.vx1 && ((lv.bst >> (c.vx0 - j * kCPT)) & 1u)) kb -= 1;
+#pragma unroll
+        for (int q = 0; q < kCPT; ++q) {
+            if ((lv.bst >> q) & 1u) {
+                ++kb;
+                P.offsets[t.b0 + kb] = base - head + p;
+                or_bits(L.obuf, p, (uint64_t)__float_as_uint(L.f.nrm[kb]) << 32, 32u);
+                p += 32u;
+            }
+            const uint32_t len = TABLE ? (ec[q] & 31u) : ec[q];
+            if (len) {
+                const uint64_t code = TABLE ? (uint64_t)(ec[q] >> 5) : ecx[TABLE ? 0 : q];
+                or_bits(L.obuf, p, code << (64u - len), len);
+            }
+            p += len;
+        }
+        __syncthreads();
+
+        // ---- store: interior words by all threads, edge words by thread 0 ----
+        uint64_t *dst = P.out + (base >> 6);
+        for (uint32_t w = 1 + threadIdx.x; w + 1 < W; w += kWG) dst[w] = L.obuf[w];
+        if (wave == 0) {
+            const bool head_shared = head != 0;
+            const bool tail_partial = ((base + T) & 63u) != 0;
+            if (W > 1) {
+                if (tail_partial && !last) {
+                    if (lane == 0) st_agent(&P.carry[tile], L.obuf[W - 1] | 1ull);
+                } else {
+                    if (lane == 0) {
+                        dst[W - 1] = L.obuf[W - 1];
+                        st_agent(&P.carry[tile], 1ull);
+                    }
+                }
+            }
+            uint64_t hw = L.obuf[0];
+            if (head_shared) {
+                uint64_t cw;
+                while (true) {
+                    cw = ld_agent(&P.carry[tile - 1]);
+                    if (__builtin_amdgcn_readfirstlane((uint32_t)cw) & 1u) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                hw |= cw & ~1ull;
+            }
+            if (lane == 0) {
+                if (W > 1) {
+                    dst[0] = hw;
+                } else if (tail_partial && !last) {
+                    st_agent(&P.carry[tile], hw | 1ull);
+                } else {
+                    dst[0] = hw;
+                    st_agent(&P.carry[tile], 1ull);
+                }
+            }
         }
     }
 }

@@ -35,7 +35,6 @@ struct QsgdParams {
     uint64_t *status;   // [ntiles] lookback words (flag:2 | value:62)
     uint64_t *carry;    // [ntiles] partial last word of each tile, bit 0 = ready
     uint32_t *ticket;   // work counter
-    uint32_t stage_words;  // LDS words for staged records
     uint32_t obuf_words;   // LDS words for the tile's output window
 };
 
