@@ -20,6 +20,47 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c3.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: counter-derived traffic is only reported for the
+    kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_sgd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None if it is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mbytes: int, reps: int):
+    """A plain device-to-device copy of known size (the counter calibration run
+    for FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    n = mbytes * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 4 * n, "reps": reps}), flush=True)
 
 
 def cpu_baseline(w, max_coords: int, reps: int = 3):
@@ -59,7 +100,12 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--cpu-sample", type=int, default=0, help="coordinates for the oracle (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calib_mb:
+        copy_calibration(args.copy_calib_mb, max(1, args.steps))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the compressor needs no second GPU); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -161,7 +207,8 @@ def main():
         "compression_vs_fp32_with_offsets": round(32.0 * n / (nbits + 64.0 * (nb + 1)), 3),
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(dominant),
+                     "algorithmic_bytes": round(enc_bytes if dominant == "encode" else dec_bytes)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
