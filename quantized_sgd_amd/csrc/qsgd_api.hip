@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <cstdint>
 
 #include "qsgd_decode.h"
@@ -70,22 +71,28 @@ EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool align
 
 size_t quantize_lds_bytes(const EncodePlan &p) { return EncodeLayout(0, 0, p.K).total; }
 
-// Resident workgroups of an encode kernel on the current device (cached).
+// Workgroups of a kernel that fit on the current device at once (cached per
+// kernel, LDS size and device; safe to call from several host threads).
 template <typename K>
 uint32_t resident_blocks(K kernel, size_t lds) {
     struct Entry { const void *k; size_t lds; int dev; uint32_t blocks; };
-    static Entry cache[16];
+    static std::mutex mu;
+    static Entry cache[32];
     static int used = 0;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    for (int i = 0; i < used; ++i)
-        if (cache[i].k == (const void *)kernel && cache[i].lds == lds && cache[i].dev == dev)
-            return cache[i].blocks;
+    {
+        std::lock_guard<std::mutex> g(mu);
+        for (int i = 0; i < used; ++i)
+            if (cache[i].k == (const void *)kernel && cache[i].lds == lds && cache[i].dev == dev)
+                return cache[i].blocks;
+    }
     int cus = 0, per_cu = 0;
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWG, lds);
-    uint32_t blocks = (uint32_t)std::max(1, cus) * (uint32_t)std::max(1, per_cu);
-    if (used < 16) cache[used++] = Entry{(const void *)kernel, lds, dev, blocks};
+    const uint32_t blocks = (uint32_t)std::max(1, cus) * (uint32_t)std::max(1, per_cu);
+    std::lock_guard<std::mutex> g(mu);
+    if (used < 32) cache[used++] = Entry{(const void *)kernel, lds, dev, blocks};
     return blocks;
 }
 
@@ -173,18 +180,30 @@ qsgd_status decode_impl(const uint64_t *in, const uint64_t *offsets, uint64_t n,
     DecodeParams D{};
     D.in = in; D.offsets = offsets; D.bstart = bstart; D.v_hat = v_hat;
     D.n = n; D.nb = nb; D.s = s; D.d = d;
-    // lanes per bucket: about one per 64 coordinates, a power of two in [1, 64]
-    uint32_t team = 1;
-    while (team < 64 && (uint64_t)team * 2 * 64 <= d) team *= 2;
+    // LDS-staged output: whole groups of buckets of at most kGroupCoords
+    // coordinates, levels fit int8. Team size: a power of two, about one lane per
+    // 64 coordinates of a bucket, teams * buckets per group <= 64.
+    const bool lds_out = s <= 127 && d <= (uint32_t)kGroupCoords;
+    uint32_t tpw, team = 1;
+    if (lds_out) {
+        tpw = std::max<uint32_t>(1, std::min<uint32_t>(64, (uint32_t)kGroupCoords / d));
+        while (team * 2 * tpw <= 64) team *= 2;
+    } else {
+        while (team < 64 && (uint64_t)team * 2 * 64 <= d) team *= 2;
+        tpw = 64 / team;
+    }
     D.team = team;
-    const uint64_t groups = (nb + (64 / team) - 1) / (64 / team);
+    D.tpw = tpw;
+    D.lds_out = lds_out ? 1u : 0u;
+    const uint64_t groups = (nb + tpw - 1) / tpw;
     const uint64_t want = (groups + kWaves - 1) / kWaves;
-    const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, 256ull * 8);
     const size_t lds = decode_lds_bytes();
-    if (bstart)
-        hipLaunchKernelGGL(decode_kernel<true>, dim3(blocks), dim3(kWG), lds, stream, D);
-    else
-        hipLaunchKernelGGL(decode_kernel<false>, dim3(blocks), dim3(kWG), lds, stream, D);
+    auto launch = [&](auto kernel) {
+        const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, resident_blocks(kernel, lds));
+        hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), lds, stream, D);
+    };
+    if (bstart) launch(decode_kernel<true>);
+    else launch(decode_kernel<false>);
     return launch_status();
 }
 

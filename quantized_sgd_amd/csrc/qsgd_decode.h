@@ -6,9 +6,7 @@
 //
 // Work split. A wave64 owns a group of consecutive buckets and a team of T lanes
 // (T = 1..64, chosen from the bucket size) decodes each bucket. The wave first
-// copies the group's stream words into LDS with coalesced loads and clears the
-// group's output coordinates with coalesced 16-byte stores; values are then
-// scattered on top.
+// copies the group's stream words into LDS with coalesced loads.
 //
 // Parallel parse of one bucket. Its records form a chain that can only be
 // followed serially, so the team splits the payload into equal bit segments
@@ -27,11 +25,14 @@
 //   count:   each lane's index span is the sum of the gaps of its exact records
 //            (phase A + B sums minus those before its sync point, re-parsed);
 //            a team prefix sum gives absolute indices.
-//   write:   each lane parses its exact range again and stores the values.
-// Record parsing: a 64-bit MSB-aligned bit window refilled 32 bits at a time
-// from LDS, and a 4096-entry table indexed by the next 12 bits that decodes a
-// whole record (gap <= 16, k <= 16) at once; longer codewords take the general
-// omega loop.
+//   write:   each lane parses its exact range again. For levels that fit a byte
+//            and groups of at most 4096 coordinates, it stores (sign, k) bytes
+//            in an LDS copy of the group, which the wave then dequantizes and
+//            writes with coalesced 16-byte stores; otherwise each lane writes
+//            its own index range directly.
+// Record parsing reads the 64 stream bits at any bit position from LDS (two
+// dwords) and looks the next 12 bits up in a table that decodes a whole record
+// (gap <= 16, k <= 16) at once; other records take the general omega loop.
 #pragma once
 
 #include "qsgd_device.h"
@@ -40,7 +41,9 @@ namespace qsgd {
 
 constexpr int kLutBits = 12;
 constexpr int kSyncWin = 128;       // bits
-constexpr int kStageWords = 512;    // 64-bit stream words staged per wave
+constexpr int kStageWords = 384;    // 64-bit stream words staged per wave
+constexpr int kStagePad = 4;        // zero words after the staged stream
+constexpr int kGroupCoords = 4096;  // coordinates of a group whose levels are staged in LDS
 
 struct DecodeParams {
     const uint64_t *in;
@@ -52,196 +55,211 @@ struct DecodeParams {
     uint32_t s;
     uint32_t d;
     uint32_t team;           // lanes per bucket (power of two, 1..64)
+    uint32_t tpw;            // buckets per wave group (tpw * team <= 64)
+    uint32_t lds_out;        // 1: levels staged in LDS (s <= 127, tpw * d <= kGroupCoords)
 };
 
-// Record table: entry for the next 12 stream bits. bits 0-3: record length
-// (0: the record is longer than 12 bits or has gap/level > 16), 4-7: gap - 1,
-// 8-11: k - 1, 12: sign.
-__device__ inline void build_record_lut(uint16_t *lut) {
-    for (uint32_t i = threadIdx.x; i < (1u << kLutBits); i += blockDim.x) {
-        int pos = 0;
-        auto take = [&](int nbits) -> int {
-            if (pos + nbits > kLutBits) return -1;
-            const int v = (int)((i >> (kLutBits - pos - nbits)) & ((1u << nbits) - 1u));
-            pos += nbits;
-            return v;
-        };
-        auto omega = [&]() -> int {  // Elias omega, values up to 16
-            int N = 1;
-            while (true) {
-                const int b = take(1);
-                if (b < 0) return -1;
-                if (b == 0) return N;
-                const int v = take(N);
-                if (v < 0) return -1;
-                N = (1 << N) | v;
-                if (N > 16) return -1;
-            }
-        };
-        uint16_t e = 0;
-        const int gap = omega();
-        if (gap > 0) {
-            const int sg = take(1);
-            if (sg >= 0) {
-                const int k = omega();
-                if (k > 0) e = (uint16_t)(pos | ((gap - 1) << 4) | ((k - 1) << 8) | (sg << 12));
-            }
-        }
-        lut[i] = e;
+// ---- record table -------------------------------------------------------
+// Entry for the next 12 stream bits: bits 0-3 record length (0: the record is
+// longer than 12 bits or has a gap or level above 16), bits 4-7 gap - 1, bits
+// 8-15 the level byte sign << 7 | k. Computed at compile time.
+struct alignas(16) RecordLut {
+    uint16_t e[1 << kLutBits];
+};
+
+struct LutCursor {
+    uint32_t bits;
+    int pos;
+};
+
+constexpr int lut_take(LutCursor &c, int nbits) {
+    if (c.pos + nbits > kLutBits) return -1;
+    const int v = (int)((c.bits >> (kLutBits - c.pos - nbits)) & ((1u << nbits) - 1u));
+    c.pos += nbits;
+    return v;
+}
+
+// Elias omega (Elias 1975) for values up to 16: N = 1; while the next bit is 1,
+// that bit and the N bits after it are the new N; a 0 bit ends the codeword.
+constexpr int lut_omega(LutCursor &c) {
+    int N = 1;
+    while (true) {
+        const int b = lut_take(c, 1);
+        if (b < 0) return -1;
+        if (b == 0) return N;
+        const int v = lut_take(c, N);
+        if (v < 0) return -1;
+        N = (1 << N) | v;
+        if (N > 16) return -1;
     }
 }
 
+constexpr RecordLut make_record_lut() {
+    RecordLut t{};
+    for (uint32_t i = 0; i < (1u << kLutBits); ++i) {
+        LutCursor c{i, 0};
+        uint16_t e = 0;
+        const int gap = lut_omega(c);
+        if (gap > 0) {
+            const int sg = lut_take(c, 1);
+            if (sg >= 0) {
+                const int k = lut_omega(c);
+                if (k > 0) e = (uint16_t)(c.pos | ((gap - 1) << 4) | (((sg << 7) | k) << 8));
+            }
+        }
+        t.e[i] = e;
+    }
+    return t;
+}
 
+__constant__ RecordLut kRecordLut = make_record_lut();
+
+// ---- bit access -----------------------------------------------------------
 // Bit positions are relative to the first stream word of the wave's bucket
 // group; a group spans fewer than 2^31 bits (buckets of at most 2^24
-// coordinates).
-//
-// MSB-first bit window over the stream. Half-word h (32 bits) is the high (h
-// even) or low (h odd) half of 64-bit word h / 2, i.e. dword h ^ 1 in memory.
-// LDS mode reads the group's staged words (padded with zero words, so no bound
-// check is needed); global mode reads the stream and treats half-words past
-// `hlast` as zero.
+// coordinates). LDS mode: dword h of the staged copy holds stream bits
+// [32h, 32h + 32) most significant first (the halves of each 64-bit word
+// swapped), followed by kStagePad zero words, so no bound check is needed.
+// Global mode: the stream's own words (bits [32h, 32h + 32) are dword h ^ 1),
+// dwords past `hlast` read as zero.
 template <bool LDS>
-struct Reader {
+struct Bits {
     const uint32_t *src;
     uint32_t hlast;
-    uint64_t win;   // next bits, MSB-aligned
-    uint32_t nb;    // valid bits in win (>= 32 after every step)
-    uint32_t next;  // next half-word to load
 
-    __device__ __forceinline__ uint32_t half(uint32_t h) const {
-        if (LDS) return src[h ^ 1u];
+    __device__ __forceinline__ uint32_t dw(uint32_t h) const {
+        if (LDS) return src[h];
         return h <= hlast ? src[h ^ 1u] : 0u;
     }
-    __device__ __forceinline__ void seek(uint32_t p) {
-        const uint32_t h = p >> 5, off = p & 31u;
-        const uint64_t w = ((uint64_t)half(h) << 32) | (uint64_t)half(h + 1);
-        win = w << off;
-        nb = 64u - off;
-        next = h + 2u;
-    }
-    __device__ __forceinline__ uint32_t pos() const { return next * 32u - nb; }
-    __device__ __forceinline__ void consume(uint32_t n) {  // 1 <= n <= 32
-        win <<= n;
-        nb -= n;
-        if (nb < 32u) {
-            win |= (uint64_t)half(next) << (32u - nb);
-            nb += 32u;
-            ++next;
-        }
+    // The 64 stream bits from bit p on, most significant first; at least the
+    // first 33 of them lie within the two dwords read.
+    __device__ __forceinline__ uint64_t at(uint32_t p) const {
+        const uint32_t h = p >> 5;
+        const uint64_t w = ((uint64_t)dw(h) << 32) | (uint64_t)dw(h + 1u);
+        return w << (p & 31u);
     }
 };
-
-// General omega decoding (Elias 1975): N = 1; while the next bit is 1, that bit
-// and the N bits after it form the new N; a 0 ends the codeword. 0 = invalid (a
-// group longer than maxbits).
-template <bool LDS>
-__device__ __forceinline__ uint32_t read_omega(Reader<LDS> &r, uint32_t maxbits) {
-    uint32_t N = 1;
-    while (true) {
-        if ((r.win >> 63) == 0) {
-            r.consume(1);
-            return N;
-        }
-        const uint32_t g = N + 1u;
-        if (g > maxbits) return 0;
-        N = (uint32_t)(r.win >> (64u - g));
-        r.consume(g);
-    }
-}
 
 struct RecordCtx {
     const uint16_t *lut;
     uint32_t gbits, kbits, s;
 };
 
-// One record omega(gap) | sign | omega(k). False if it does not parse. The table
-// covers records of at most 12 bits with gap, k <= 16 (it does not check k <= s
-// or gap <= bucket length: on the true chain those hold anyway, and a
-// speculative chain only has to be a deterministic function of its start).
+// General omega decoding from bit p: returns N and advances p, or 0 if a group
+// is longer than maxbits (<= 25, so each group lies in one 64-bit read).
 template <bool LDS>
-__device__ __forceinline__ bool read_record(Reader<LDS> &r, const RecordCtx &x, uint32_t &gap,
-                                            uint32_t &neg, uint32_t &k) {
-    const uint32_t e = x.lut[(uint32_t)(r.win >> (64 - kLutBits))];
+__device__ __forceinline__ uint32_t omega_at(const Bits<LDS> &r, uint32_t &p, uint32_t maxbits) {
+    uint32_t N = 1;
+    while (true) {
+        const uint64_t w = r.at(p);
+        if ((w >> 63) == 0) {
+            p += 1u;
+            return N;
+        }
+        const uint32_t g = N + 1u;
+        if (g > maxbits) return 0;
+        N = (uint32_t)(w >> (64u - g));
+        p += g;
+    }
+}
+
+// One record omega(gap) | sign | omega(k) at bit p. Returns the position after
+// it, or 0 if it does not parse (a record never ends at 0). The table covers
+// records of at most 12 bits with gap, k <= 16 (it does not check k <= s or gap
+// <= bucket length: on the true chain those hold anyway, and a speculative chain
+// only has to be a deterministic function of its start).
+template <bool LDS>
+__device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const RecordCtx &x, uint32_t p,
+                                              uint32_t &gap, uint32_t &neg, uint32_t &k) {
+    const uint64_t w = r.at(p);
+    const uint32_t e = x.lut[(uint32_t)(w >> (64 - kLutBits))];
     if (e & 15u) {
         gap = ((e >> 4) & 15u) + 1u;
-        k = ((e >> 8) & 15u) + 1u;
-        neg = (e >> 12) & 1u;
-        r.consume(e & 15u);
-        return true;
+        k = (e >> 8) & 127u;
+        neg = (e >> 15) & 1u;
+        return p + (e & 15u);
     }
-    gap = read_omega(r, x.gbits);
-    if (gap == 0) return false;
-    neg = (uint32_t)(r.win >> 63);
-    r.consume(1);
-    k = read_omega(r, x.kbits);
-    return k != 0 && k <= x.s;
+    uint32_t q = p;
+    gap = omega_at(r, q, x.gbits);
+    if (gap == 0) return 0;
+    neg = (uint32_t)(r.at(q) >> 63);
+    q += 1u;
+    k = omega_at(r, q, x.kbits);
+    if (k == 0 || k > x.s) return 0;
+    return q;
+}
+
+// One step of a chain: past the record at p, or one bit on if none parses.
+template <bool LDS>
+__device__ __forceinline__ void chain_step(const Bits<LDS> &r, const RecordCtx &x, uint32_t &p,
+                                           uint32_t &sum) {
+    uint32_t gap, neg, k;
+    const uint32_t q = record_at(r, x, p, gap, neg, k);
+    if (q) {
+        p = q;
+        sum += gap;
+    } else {
+        p += 1u;
+    }
 }
 
 __device__ __forceinline__ uint32_t bitlen32(uint32_t x) { return 32u - (uint32_t)__clz(x); }
 
-__device__ __forceinline__ bool mask_has(uint64_t m0, uint64_t m1, uint32_t rel) {
-    return rel < 64u ? ((m0 >> rel) & 1u) : (rel < 128u ? ((m1 >> (rel - 64u)) & 1u) : false);
-}
-
-// Parse state of one lane over its bucket.
-struct Chain {
-    uint32_t x;      // first chain position >= segment end (the exit)
-    uint32_t ynext;  // where the chain met the next lane's chain (or E)
-    uint32_t ga;     // gap sum of records starting before the exit
-    uint32_t gb;     // gap sum of records from the exit to ynext
-    bool found;
-};
-
-// Phase A: follows a chain from `start` to its first position >= sn (the exit).
-// With `mark`, positions in [start, start + 128) where it starts a record are
-// set in own0/own1.
-template <bool LDS>
-__device__ __forceinline__ void follow_chain(Reader<LDS> &r, const RecordCtx &x, uint32_t start,
-                                             uint32_t sn, uint32_t E, bool mark, uint64_t &own0,
-                                             uint64_t &own1, Chain &c) {
-    uint32_t pos = start;
-    r.seek(pos);
-    c.ga = 0;
-    c.gb = 0;
-    while (pos < sn) {
-        if (mark) {
-            const uint32_t rel = pos - start;
-            if (rel < 64u) own0 |= 1ull << rel;
-            else if (rel < 128u) own1 |= 1ull << (rel - 64u);
+// Phase A: follows a chain from `start` to its first position >= sn and returns
+// that position (the exit), with the gap sum of the records passed. MARK: sets
+// bit (p - start) of own0:own1 for each chain position p in [start, start + 128).
+template <bool LDS, bool MARK>
+__device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const RecordCtx &x, uint32_t start,
+                                                 uint32_t sn, uint32_t &ga, uint64_t &own0,
+                                                 uint64_t &own1) {
+    uint32_t p = start, sum = 0;
+    if (MARK) {
+        const uint32_t l1 = sn < start + 64u ? sn : start + 64u;
+        while (p < l1) {
+            own0 |= 1ull << (p - start);
+            chain_step(r, x, p, sum);
         }
-        uint32_t gap, neg, k;
-        if (read_record(r, x, gap, neg, k) && r.pos() <= E) {
-            pos = r.pos();
-            c.ga += gap;
-        } else {
-            pos = pos + 1u;
-            r.seek(pos);
+        const uint32_t l2 = sn < start + 128u ? sn : start + 128u;
+        while (p < l2) {
+            own1 |= 1ull << (p - start - 64u);
+            chain_step(r, x, p, sum);
         }
     }
-    c.x = pos;
-    c.found = false;
-    c.ynext = E;
+    while (p < sn) chain_step(r, x, p, sum);
+    ga = sum;
+    return p;
 }
 
-// Phase B: continues the chain from its exit until it lands on a position noted
-// by the next lane (window nxt0/nxt1 starting at sn) or on E; gives up after
-// 128 bits or at an invalid record.
+// Phase B: continues the chain from its exit x0 (>= sn) until it lands on a
+// position noted by the next lane (nxt0:nxt1, relative to sn) or on E. Gives up
+// 128 bits past sn, past E, or at a record that does not parse.
 template <bool LDS>
-__device__ __forceinline__ void extend_chain(Reader<LDS> &r, const RecordCtx &x, uint32_t sn,
-                                             uint32_t E, uint64_t nxt0, uint64_t nxt1, Chain &c) {
-    uint32_t pos = c.x;
-    r.seek(pos);
+__device__ __forceinline__ bool extend_chain(const Bits<LDS> &r, const RecordCtx &x, uint32_t x0,
+                                             uint32_t sn, uint32_t E, uint64_t nxt0, uint64_t nxt1,
+                                             uint32_t &y, uint32_t &gb) {
+    uint32_t p = x0, sum = 0;
+    bool found = false;
     while (true) {
-        if (pos == E) { c.found = true; c.ynext = E; return; }
-        const uint32_t rel = pos - sn;
-        if (rel >= (uint32_t)kSyncWin) return;
-        if (mask_has(nxt0, nxt1, rel)) { c.found = true; c.ynext = pos; return; }
+        if (p == E) {
+            found = true;
+            break;
+        }
+        const uint32_t rel = p - sn;
+        if (rel >= (uint32_t)kSyncWin || p > E) break;
+        const uint64_t m = rel < 64u ? nxt0 : nxt1;
+        if ((m >> (rel & 63u)) & 1u) {
+            found = true;
+            break;
+        }
         uint32_t gap, neg, k;
-        if (!(read_record(r, x, gap, neg, k) && r.pos() <= E)) return;
-        pos = r.pos();
-        c.gb += gap;
+        const uint32_t q = record_at(r, x, p, gap, neg, k);
+        if (!q) break;
+        p = q;
+        sum += gap;
     }
+    y = found ? p : E;
+    gb = sum;
+    return found;
 }
 
 // Writes one lane's output range [lo, hi) in index order, exactly once: values
@@ -298,23 +316,22 @@ __device__ __forceinline__ uint64_t bucket_first(const DecodeParams &D, uint64_t
     return g < D.n ? g : D.n;
 }
 
-// Decodes the buckets [b0, b1) of one wave group; `src` holds the group's
-// stream from bit `gbit` on (LDS: staged; global: the stream itself).
-template <bool RAGGED, bool LDS>
+// Decodes the buckets [b0, b1) of one wave group; `r` reads the group's stream,
+// bit 0 being stream bit `gbit`. LDS_OUT: each record's level byte (sign << 7 |
+// k) goes to the group's LDS buffer `lvl` (index = coordinate - lbase, cleared
+// by the caller) and each bucket's RN64(norm / s) to ebs[team]; otherwise every
+// lane writes its own output range with a QuadWriter.
+template <bool RAGGED, bool LDS_IN, bool LDS_OUT>
 __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16_t *lut,
-                                             const uint32_t *src, uint32_t hlast, uint64_t gbit,
-                                             uint64_t b0, uint64_t b1) {
+                                             const Bits<LDS_IN> &r, uint64_t gbit, uint64_t b0,
+                                             uint64_t b1, uint8_t *lvl, double *ebs, uint64_t lbase) {
     const int lane = lane_id();
     const uint32_t T = D.team;
     const uint32_t q = (uint32_t)lane % T;
     const uint32_t team = (uint32_t)lane / T;
 
-    Reader<LDS> r;
-    r.src = src;
-    r.hlast = hlast;
-
     const uint64_t b = b0 + team;
-    const bool tactive = b < b1;
+    const bool tactive = team < D.tpw && b < b1;
     uint32_t A = 0, E = 0;
     uint64_t c0 = 0, len = 0;
     double e_b = 0.0;
@@ -325,8 +342,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
         c0 = bucket_first<RAGGED>(D, b);
         len = bucket_first<RAGGED>(D, b + 1) - c0;
         if (E >= A + 32u && len > 0) {
-            r.seek(A);
-            const float norm = __uint_as_float((uint32_t)(r.win >> 32));
+            const float norm = __uint_as_float((uint32_t)(r.at(A) >> 32));
             e_b = (double)norm / (double)D.s;
             const uint32_t Lp = E - (A + 32u);
             if (Lp > 0) {
@@ -336,7 +352,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
             }
         }
     }
-    RecordCtx x{lut, tactive ? bitlen32((uint32_t)len) : 1u, bitlen32(D.s), D.s};
+    if (LDS_OUT && tactive && q == 0) ebs[team] = e_b;
+    const RecordCtx x{lut, tactive ? bitlen32((uint32_t)len) : 1u, bitlen32(D.s), D.s};
     const uint32_t P0 = A + 32u;
     const uint32_t seg = nl ? ((E - P0) + nl - 1u) / nl : 0u;
     const bool act = q < nl;
@@ -346,13 +363,14 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
 
     // phase A on every lane's own segment, noting its first 128 bits
     uint64_t own0 = 0, own1 = 0;
-    Chain c{E, E, 0u, 0u, false};
-    if (act) follow_chain(r, x, sq, sn, E, true, own0, own1, c);
-    if (act && last) { c.found = true; c.ynext = E; }
+    uint32_t cx = E, ga = 0, gb = 0, ynext = E;
+    bool found = false;
+    if (act) cx = follow_chain<LDS_IN, true>(r, x, sq, sn, ga, own0, own1);
+    if (act && last) found = true;
     // phase B against the next lane's window
     const uint64_t nxt0 = __shfl_down(own0, 1, (int)T);
     const uint64_t nxt1 = __shfl_down(own1, 1, (int)T);
-    if (act && !last) extend_chain(r, x, sn, E, nxt0, nxt1, c);
+    if (act && !last) found = extend_chain(r, x, cx, sn, E, nxt0, nxt1, ynext, gb);
 
     // repair: restart, in order, every lane whose predecessor did not meet it.
     // All lanes below the lowest broken lane of a team are exact and each round
@@ -360,8 +378,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
     bool repaired = false;
     uint32_t rstart = 0;
     while (true) {
-        const bool pf = __shfl_up(c.found ? 1 : 0, 1, (int)T) != 0;
-        const uint32_t px = __shfl_up(c.x, 1, (int)T);
+        const bool pf = __shfl_up(found ? 1 : 0, 1, (int)T) != 0;
+        const uint32_t px = __shfl_up(cx, 1, (int)T);
         const bool broken = act && q >= 1 && !pf && !repaired;
         const uint64_t bm = __ballot(broken);
         if (bm == 0) break;
@@ -371,22 +389,27 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
         // the predecessor of a restarted lane ends at its own exit
         const bool succ_fix = __shfl_down(fix ? 1 : 0, 1, (int)T) != 0 && !last;
         if (act && succ_fix) {
-            c.ynext = c.x;
-            c.gb = 0;
-            c.found = true;
+            ynext = cx;
+            gb = 0;
+            found = true;
         }
         if (fix) {
             uint64_t d0 = 0, d1 = 0;
-            follow_chain(r, x, px, sn, E, false, d0, d1, c);
-            if (last) { c.found = true; c.ynext = E; }
-            else extend_chain(r, x, sn, E, nxt0, nxt1, c);
+            cx = follow_chain<LDS_IN, false>(r, x, px, sn, ga, d0, d1);
+            if (last) {
+                found = true;
+                ynext = E;
+                gb = 0;
+            } else {
+                found = extend_chain(r, x, cx, sn, E, nxt0, nxt1, ynext, gb);
+            }
             repaired = true;
             rstart = px;
         }
     }
 
     // exact start of each lane's records
-    const uint32_t py = __shfl_up(c.ynext, 1, (int)T);
+    const uint32_t py = __shfl_up(ynext, 1, (int)T);
     uint32_t ystart = E;
     if (act) {
         if (q == 0) ystart = P0;
@@ -395,21 +418,11 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
     }
     // gaps of the records before the sync point (same speculative chain)
     uint32_t gpre = 0;
-    if (act && q >= 1 && !repaired && ystart > sq) {
-        uint32_t pos = sq;
-        r.seek(pos);
-        while (pos < ystart) {
-            uint32_t gap, neg, k;
-            if (read_record(r, x, gap, neg, k) && r.pos() <= E) {
-                pos = r.pos();
-                gpre += gap;
-            } else {
-                pos = pos + 1u;
-                r.seek(pos);
-            }
-        }
+    if (act && q >= 1 && !repaired) {
+        uint32_t p = sq;
+        while (p < ystart) chain_step(r, x, p, gpre);
     }
-    const uint32_t G = act ? c.ga + c.gb - gpre : 0u;
+    const uint32_t G = act ? ga + gb - gpre : 0u;
     // team-exclusive prefix sum of the index spans
     uint32_t incl = G;
     for (uint32_t off = 1; off < T; off <<= 1) {
@@ -418,6 +431,23 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
     }
     const uint32_t basej = incl - G;
 
+    if (LDS_OUT) {
+        if (act) {
+            uint8_t *lb = lvl + (c0 - lbase);
+            uint32_t p = ystart;
+            uint32_t jj = basej - 1u;
+            while (p < ynext) {
+                uint32_t gap, neg, k;
+                const uint32_t nq = record_at(r, x, p, gap, neg, k);
+                if (!nq) break;
+                jj += gap;
+                if (jj >= (uint32_t)len) break;
+                lb[jj] = (uint8_t)((neg << 7) | k);
+                p = nq;
+            }
+        }
+        return;
+    }
     // output: lane q owns [basej, basej + G), the last lane up to the bucket end;
     // a bucket without records is written by its team's first lane
     if (tactive && (act || (nl == 0 && q == 0))) {
@@ -427,35 +457,87 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
         if (hi < lo) hi = lo;
         QuadWriter w;
         w.init(D.v_hat, c0 + lo, c0 + hi);
-        if (act && ystart < c.ynext) {
-            r.seek(ystart);
-            int64_t jj = (int64_t)basej - 1;
-            while (r.pos() < c.ynext) {
+        if (act) {
+            uint32_t p = ystart;
+            uint64_t jj = (uint64_t)basej - 1u;
+            while (p < ynext) {
                 uint32_t gap, neg, k;
-                if (!read_record(r, x, gap, neg, k)) break;
+                const uint32_t nq = record_at(r, x, p, gap, neg, k);
+                if (!nq) break;
                 jj += gap;
-                if (jj >= (int64_t)hi) break;
+                if (jj >= hi) break;
                 const float m = (float)((double)k * e_b);
-                w.put(c0 + (uint64_t)jj, neg ? -m : m);
+                w.put(c0 + jj, neg ? -m : m);
+                p = nq;
             }
         }
         w.finish();
     }
 }
 
-// Dynamic LDS: the record table, then per wave kStageWords + 2 staged words.
+// Writes the group's buckets from the LDS level bytes: RN32(k * RN64(norm / s))
+// with the byte's sign (+0.0f for k = 0), 16-byte stores for whole aligned
+// quads of a bucket, single floats for quads that a bucket boundary cuts.
+template <bool RAGGED>
+__device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t *lvl, const double *ebs,
+                                            uint64_t lbase, uint64_t b0, uint64_t b1) {
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t *lw = reinterpret_cast<const uint32_t *>(lvl);
+    for (uint64_t b = b0; b < b1; ++b) {
+        const uint64_t A = bucket_first<RAGGED>(D, b), B = bucket_first<RAGGED>(D, b + 1);
+        const double e = ebs[b - b0];
+        const uint64_t qa = A >> 2, qb = (B + 3) >> 2;
+        for (uint64_t qd = qa + lane; qd < qb; qd += 64) {
+            const uint64_t a = qd << 2;
+            const uint32_t word = lw[(a - lbase) >> 2];
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t byte = (word >> (8 * t)) & 0xffu;
+                const float m = (float)((double)(byte & 127u) * e);
+                v[t] = __uint_as_float(__float_as_uint(m) | ((byte & 128u) << 24));
+            }
+            if (a >= A && a + 4 <= B) {
+                *reinterpret_cast<float4 *>(D.v_hat + a) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                if (a >= A && a < B) D.v_hat[a] = v[0];
+                if (a + 1 >= A && a + 1 < B) D.v_hat[a + 1] = v[1];
+                if (a + 2 >= A && a + 2 < B) D.v_hat[a + 2] = v[2];
+                if (a + 3 >= A && a + 3 < B) D.v_hat[a + 3] = v[3];
+            }
+        }
+    }
+}
+
+// Dynamic LDS: the record table, then per wave the staged stream words, the
+// group's level bytes and the per-bucket dequantization factors.
+constexpr size_t kStageBytes = (size_t)(kStageWords + kStagePad) * 8;
+constexpr size_t kLevelBytes = (size_t)kGroupCoords + 16;
+constexpr size_t kWaveLdsBytes = kStageBytes + kLevelBytes + 64 * 8;
+
+constexpr size_t decode_lds_bytes() {
+    return sizeof(RecordLut) + (size_t)kWaves * kWaveLdsBytes;
+}
+
 template <bool RAGGED>
 __global__ __launch_bounds__(kWG) void decode_kernel(DecodeParams D) {
     extern __shared__ __align__(16) uint64_t dsmem[];
     uint16_t *lut = reinterpret_cast<uint16_t *>(dsmem);
-    build_record_lut(lut);
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(kRecordLut.e);
+        uint4 *dst = reinterpret_cast<uint4 *>(lut);
+        for (uint32_t i = threadIdx.x; i < sizeof(RecordLut) / 16; i += kWG) dst[i] = src[i];
+    }
     __syncthreads();
 
     const int lane = lane_id();
     const int wv = wave_id();
-    uint64_t *stage = dsmem + (1u << kLutBits) / 4 + (size_t)wv * (kStageWords + 2);
-    const uint32_t T = D.team;
-    const uint32_t tpw = 64u / T;
+    unsigned char *wbase = reinterpret_cast<unsigned char *>(dsmem) + sizeof(RecordLut) +
+                           (size_t)wv * kWaveLdsBytes;
+    uint64_t *stage = reinterpret_cast<uint64_t *>(wbase);
+    uint8_t *lvl = wbase + kStageBytes;
+    double *ebs = reinterpret_cast<double *>(wbase + kStageBytes + kLevelBytes);
+    const uint32_t tpw = D.tpw;
     const uint64_t ngroups = (D.nb + tpw - 1) / tpw;
     const uint64_t total_bits = D.offsets[D.nb];
     const uint64_t total_words = (total_bits + 63) >> 6;
@@ -469,26 +551,44 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeParams D) {
         uint64_t w1 = E1 > A0 ? ((E1 + 63) >> 6) : w0;
         if (w1 > total_words) w1 = total_words;
         const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
-        if (nw <= (uint64_t)kStageWords) {
-            for (uint64_t i = (uint64_t)lane; i < nw + 2; i += 64) stage[i] = i < nw ? D.in[w0 + i] : 0ull;
-            // the staged words are read by other lanes of this wave
+        const bool in_lds = nw <= (uint64_t)kStageWords;
+        if (in_lds) {
+            // halves swapped: dword 2i = bits [64i, 64i + 32) of the group
+            for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64) {
+                const uint64_t w = i < nw ? D.in[w0 + i] : 0ull;
+                stage[i] = (w << 32) | (w >> 32);
+            }
+        }
+        const uint64_t lbase = bucket_first<RAGGED>(D, b0) & ~(uint64_t)3;
+        if (D.lds_out) {
+            const uint64_t lend = bucket_first<RAGGED>(D, b1);
+            const uint32_t nq16 = (uint32_t)((lend - lbase + 15) >> 4);
+            uint4 *l4 = reinterpret_cast<uint4 *>(lvl);
+            for (uint32_t i = (uint32_t)lane; i < nq16; i += 64) l4[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        // staged words and cleared levels are used by other lanes of this wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        Bits<true> rl{reinterpret_cast<const uint32_t *>(stage), 0u};
+        Bits<false> rg{reinterpret_cast<const uint32_t *>(D.in + w0),
+                       (uint32_t)(2 * (total_words - w0)) - 1u};
+        if (D.lds_out) {
+            if (in_lds) decode_group<RAGGED, true, true>(D, lut, rl, w0 * 64, b0, b1, lvl, ebs, lbase);
+            else decode_group<RAGGED, false, true>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            decode_group<RAGGED, true>(D, lut, reinterpret_cast<const uint32_t *>(stage), 0u, w0 * 64,
-                                       b0, b1);
+            store_group<RAGGED>(D, lvl, ebs, lbase, b0, b1);
         } else {
-            const uint32_t hlast = (uint32_t)(2 * (total_words - w0)) - 1u;
-            decode_group<RAGGED, false>(D, lut, reinterpret_cast<const uint32_t *>(D.in + w0), hlast,
-                                        w0 * 64, b0, b1);
+            if (in_lds) decode_group<RAGGED, true, false>(D, lut, rl, w0 * 64, b0, b1, lvl, ebs, lbase);
+            else decode_group<RAGGED, false, false>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase);
         }
-        // the stage buffer is reused by the next group of this wave
+        // the LDS buffers are reused by the next group of this wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-}
-
-constexpr size_t decode_lds_bytes() {
-    return (size_t)(1u << kLutBits) * 2 + (size_t)kWaves * (kStageWords + 2) * 8;
 }
 
 }  // namespace qsgd
