@@ -110,6 +110,15 @@ qsgd_status check_common(const float *v, uint32_t s, uint32_t d) {
     return QSGD_OK;
 }
 
+// The fast path serves single vectors whose buckets are 2^m coordinates with
+// 16 <= d <= 4096 and s within the record table; quantize and encode take the
+// same path for the same arguments, so their norms agree bit for bit.
+bool use_aligned(const uint64_t *bstart, uint32_t s, uint32_t d) {
+    return bstart == nullptr && d >= 16 && d <= (uint32_t)kTC && (d & (d - 1)) == 0 && s <= kTabS;
+}
+
+uint32_t log2u(uint32_t d) { return 31u - (uint32_t)__builtin_clz(d); }
+
 qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb,
                           uint32_t s, uint32_t d, uint64_t seed, int32_t *levels, float *norms,
                           hipStream_t stream) {
@@ -124,6 +133,11 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
     P.v = v; P.n = n; P.nb = nb; P.bstart = bstart; P.seed = seed; P.s = s; P.d = d;
     P.K = p.K; P.ntiles = (uint32_t)p.ntiles; P.levels = levels; P.norms = norms;
     P.obuf_words = 0;
+    if (use_aligned(bstart, s, d)) {
+        hipLaunchKernelGGL(quantize_aligned_kernel, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P,
+                           log2u(d));
+        return launch_status();
+    }
     const size_t lds = quantize_lds_bytes(p);
     if (ragged)
         hipLaunchKernelGGL(quantize_kernel<true>, dim3((uint32_t)p.ntiles), dim3(kWG), lds, stream, P);
@@ -158,6 +172,13 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     const uint32_t init_blocks = (uint32_t)std::min<uint64_t>((p.ntiles + 255) / 256, 1024);
     hipLaunchKernelGGL(encode_init_kernel, dim3(std::max<uint32_t>(init_blocks, 1)), dim3(256), 0,
                        stream, P.status, P.carry, P.ticket, (uint32_t)p.ntiles);
+    if (use_aligned(bstart, s, d)) {
+        const size_t lds = aligned_encode_lds_bytes(p.obuf_words, s);
+        const uint32_t blocks =
+            (uint32_t)std::min<uint64_t>(p.ntiles, resident_blocks(encode_aligned_kernel, lds));
+        hipLaunchKernelGGL(encode_aligned_kernel, dim3(blocks), dim3(kWG), lds, stream, P, log2u(d));
+        return launch_status();
+    }
     auto launch = [&](auto kernel) {
         const uint32_t blocks = (uint32_t)std::min<uint64_t>(p.ntiles, resident_blocks(kernel, p.lds_bytes));
         hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), p.lds_bytes, stream, P);
