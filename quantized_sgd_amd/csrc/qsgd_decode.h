@@ -163,22 +163,12 @@ __device__ __forceinline__ uint32_t omega_at(const Bits<LDS> &r, uint32_t &p, ui
     }
 }
 
-// One record omega(gap) | sign | omega(k) at bit p. Returns the position after
-// it, or 0 if it does not parse (a record never ends at 0). The table covers
-// records of at most 12 bits with gap, k <= 16 (it does not check k <= s or gap
-// <= bucket length: on the true chain those hold anyway, and a speculative chain
-// only has to be a deterministic function of its start).
+// One record omega(gap) | sign | omega(k) at bit p by general omega decoding.
+// Returns the position after it, or 0 if it does not parse (a record never
+// ends at 0): a group longer than the bound, or k > s.
 template <bool LDS>
-__device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const RecordCtx &x, uint32_t p,
-                                              uint32_t &gap, uint32_t &neg, uint32_t &k) {
-    const uint64_t w = r.at(p);
-    const uint32_t e = x.lut[(uint32_t)(w >> (64 - kLutBits))];
-    if (e & 15u) {
-        gap = ((e >> 4) & 15u) + 1u;
-        k = (e >> 8) & 127u;
-        neg = (e >> 15) & 1u;
-        return p + (e & 15u);
-    }
+__device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const RecordCtx &x, uint32_t p,
+                                                uint32_t &gap, uint32_t &neg, uint32_t &k) {
     uint32_t q = p;
     gap = omega_at(r, q, x.gbits);
     if (gap == 0) return 0;
@@ -189,45 +179,100 @@ __device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const RecordCt
     return q;
 }
 
-// One step of a chain: past the record at p, or one bit on if none parses.
+// Table entry of the 12 stream bits at p (0: take record_slow). The table
+// covers records of at most 12 bits with gap, k <= 16; it does not check k <= s
+// or gap <= bucket length: on the true chain those hold anyway, and a
+// speculative chain only has to be a deterministic function of its start.
+template <bool LDS>
+__device__ __forceinline__ uint32_t lut_at(const Bits<LDS> &r, const RecordCtx &x, uint32_t p) {
+    return x.lut[(uint32_t)(r.at(p) >> (64 - kLutBits))];
+}
+
+// One step of a chain: past the record at p adding its gap to sum, or one bit
+// on if no record parses there.
 template <bool LDS>
 __device__ __forceinline__ void chain_step(const Bits<LDS> &r, const RecordCtx &x, uint32_t &p,
                                            uint32_t &sum) {
-    uint32_t gap, neg, k;
-    const uint32_t q = record_at(r, x, p, gap, neg, k);
-    if (q) {
-        p = q;
-        sum += gap;
+    const uint32_t e = lut_at(r, x, p);
+    if (e & 15u) {
+        p += e & 15u;
+        sum += ((e >> 4) & 15u) + 1u;
     } else {
-        p += 1u;
+        uint32_t gap, neg, k;
+        const uint32_t q = record_slow(r, x, p, gap, neg, k);
+        sum += q ? gap : 0u;
+        p = q ? q : p + 1u;
     }
+}
+
+// One record of the true chain at p: its end (0 if it does not parse), gap and
+// level byte sign << 7 | k (k <= 127 when the caller uses the byte).
+template <bool LDS>
+__device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const RecordCtx &x, uint32_t p,
+                                              uint32_t &gap, uint32_t &neg, uint32_t &k) {
+    const uint32_t e = lut_at(r, x, p);
+    if (e & 15u) {
+        gap = ((e >> 4) & 15u) + 1u;
+        k = (e >> 8) & 127u;
+        neg = (e >> 15) & 1u;
+        return p + (e & 15u);
+    }
+    return record_slow(r, x, p, gap, neg, k);
 }
 
 __device__ __forceinline__ uint32_t bitlen32(uint32_t x) { return 32u - (uint32_t)__clz(x); }
 
+// Slots of a lane's gap-prefix table (bytes, in the wave's level buffer while
+// the chains are being synchronised).
+constexpr uint32_t kCumSlots = 48;
+
 // Phase A: follows a chain from `start` to its first position >= sn and returns
 // that position (the exit), with the gap sum of the records passed. MARK: sets
-// bit (p - start) of own0:own1 for each chain position p in [start, start + 128).
+// bit (p - start) of own0:own1 for each chain position p in [start, start + 128)
+// and stores in cum[i] the gap sum before the i-th of them (saturated at 255;
+// the last slot collects the positions past kCumSlots - 2).
 template <bool LDS, bool MARK>
 __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const RecordCtx &x, uint32_t start,
                                                  uint32_t sn, uint32_t &ga, uint64_t &own0,
-                                                 uint64_t &own1) {
+                                                 uint64_t &own1, uint8_t *cum) {
     uint32_t p = start, sum = 0;
     if (MARK) {
+        uint32_t i = 0;
         const uint32_t l1 = sn < start + 64u ? sn : start + 64u;
         while (p < l1) {
             own0 |= 1ull << (p - start);
+            cum[i] = (uint8_t)(sum < 255u ? sum : 255u);
+            i = i + 1u < kCumSlots ? i + 1u : kCumSlots - 1u;
             chain_step(r, x, p, sum);
         }
         const uint32_t l2 = sn < start + 128u ? sn : start + 128u;
         while (p < l2) {
             own1 |= 1ull << (p - start - 64u);
+            cum[i] = (uint8_t)(sum < 255u ? sum : 255u);
+            i = i + 1u < kCumSlots ? i + 1u : kCumSlots - 1u;
             chain_step(r, x, p, sum);
         }
     }
     while (p < sn) chain_step(r, x, p, sum);
     ga = sum;
     return p;
+}
+
+// Gap sum of a lane's speculative chain before its position y, from the table
+// follow_chain<MARK> filled; false if the table cannot tell (y not a noted
+// position, past the table, or a saturated entry).
+__device__ __forceinline__ bool cum_lookup(const uint8_t *cum, uint64_t own0, uint64_t own1,
+                                           uint32_t rel, uint32_t &g) {
+    if (rel >= 128u) return false;
+    const uint64_t m = rel < 64u ? own0 : own1;
+    if (((m >> (rel & 63u)) & 1u) == 0) return false;
+    const uint32_t i = rel < 64u
+                           ? (uint32_t)__popcll(own0 & ((1ull << rel) - 1ull))
+                           : (uint32_t)__popcll(own0) +
+                                 (uint32_t)__popcll(own1 & ((1ull << (rel - 64u)) - 1ull));
+    if (i >= kCumSlots - 1u) return false;
+    g = cum[i];
+    return g < 255u;
 }
 
 // Phase B: continues the chain from its exit x0 (>= sn) until it lands on a
@@ -316,15 +361,31 @@ __device__ __forceinline__ uint64_t bucket_first(const DecodeParams &D, uint64_t
     return g < D.n ? g : D.n;
 }
 
+// Orders the wave's LDS accesses before this point before those after it, for
+// data that other lanes of the same wave read or overwrite.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// LDS slot of level byte i of a group: one spare dword after every 16, so the
+// lanes of a team, which write at about 64-byte strides, hit different banks,
+// while the conversion pass still reads consecutive dwords (dword q of the
+// levels sits at q + q / 16).
+__device__ __forceinline__ uint32_t level_slot(uint32_t i) { return i + ((i >> 6) << 2); }
+
 // Decodes the buckets [b0, b1) of one wave group; `r` reads the group's stream,
 // bit 0 being stream bit `gbit`. LDS_OUT: each record's level byte (sign << 7 |
 // k) goes to the group's LDS buffer `lvl` (index = coordinate - lbase, cleared
-// by the caller) and each bucket's RN64(norm / s) to ebs[team]; otherwise every
+// by the caller, slot level_slot(index)) and each bucket's RN64(norm / s) to
+// ebs[team]; otherwise every
 // lane writes its own output range with a QuadWriter.
 template <bool RAGGED, bool LDS_IN, bool LDS_OUT>
 __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16_t *lut,
                                              const Bits<LDS_IN> &r, uint64_t gbit, uint64_t b0,
-                                             uint64_t b1, uint8_t *lvl, double *ebs, uint64_t lbase) {
+                                             uint64_t b1, uint8_t *lvl, double *ebs, uint64_t lbase,
+                                             uint32_t nclear16) {
     const int lane = lane_id();
     const uint32_t T = D.team;
     const uint32_t q = (uint32_t)lane % T;
@@ -365,7 +426,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
     uint64_t own0 = 0, own1 = 0;
     uint32_t cx = E, ga = 0, gb = 0, ynext = E;
     bool found = false;
-    if (act) cx = follow_chain<LDS_IN, true>(r, x, sq, sn, ga, own0, own1);
+    uint8_t *cum = lvl + (uint32_t)lane * kCumSlots;
+    if (act) cx = follow_chain<LDS_IN, true>(r, x, sq, sn, ga, own0, own1, cum);
     if (act && last) found = true;
     // phase B against the next lane's window
     const uint64_t nxt0 = __shfl_down(own0, 1, (int)T);
@@ -395,7 +457,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
         }
         if (fix) {
             uint64_t d0 = 0, d1 = 0;
-            cx = follow_chain<LDS_IN, false>(r, x, px, sn, ga, d0, d1);
+            cx = follow_chain<LDS_IN, false>(r, x, px, sn, ga, d0, d1, nullptr);
             if (last) {
                 found = true;
                 ynext = E;
@@ -416,9 +478,11 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
         else if (repaired) ystart = rstart;
         else ystart = py;
     }
-    // gaps of the records before the sync point (same speculative chain)
+    // gaps of the records before the sync point: from the phase A table, else
+    // by following the same speculative chain again
     uint32_t gpre = 0;
-    if (act && q >= 1 && !repaired) {
+    if (act && q >= 1 && !repaired && !cum_lookup(cum, own0, own1, ystart - sq, gpre)) {
+        gpre = 0;
         uint32_t p = sq;
         while (p < ystart) chain_step(r, x, p, gpre);
     }
@@ -432,8 +496,13 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
     const uint32_t basej = incl - G;
 
     if (LDS_OUT) {
+        // the gap-prefix tables are done with: clear the group's level bytes
+        wave_sync();
+        uint4 *l4 = reinterpret_cast<uint4 *>(lvl);
+        for (uint32_t i = (uint32_t)lane; i < nclear16; i += 64) l4[i] = make_uint4(0u, 0u, 0u, 0u);
+        wave_sync();
         if (act) {
-            uint8_t *lb = lvl + (c0 - lbase);
+            const uint32_t i0 = (uint32_t)(c0 - lbase);
             uint32_t p = ystart;
             uint32_t jj = basej - 1u;
             while (p < ynext) {
@@ -442,7 +511,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
                 if (!nq) break;
                 jj += gap;
                 if (jj >= (uint32_t)len) break;
-                lb[jj] = (uint8_t)((neg << 7) | k);
+                lvl[level_slot(i0 + jj)] = (uint8_t)((neg << 7) | k);
                 p = nq;
             }
         }
@@ -489,7 +558,8 @@ __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t
         const uint64_t qa = A >> 2, qb = (B + 3) >> 2;
         for (uint64_t qd = qa + lane; qd < qb; qd += 64) {
             const uint64_t a = qd << 2;
-            const uint32_t word = lw[(a - lbase) >> 2];
+            const uint32_t dq = (uint32_t)((a - lbase) >> 2);
+            const uint32_t word = lw[dq + (dq >> 4)];
             float v[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -510,10 +580,12 @@ __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t
 }
 
 // Dynamic LDS: the record table, then per wave the staged stream words, the
-// group's level bytes and the per-bucket dequantization factors.
+// group's level bytes (in level_slot order) and the per-bucket dequantization
+// factors.
 constexpr size_t kStageBytes = (size_t)(kStageWords + kStagePad) * 8;
-constexpr size_t kLevelBytes = (size_t)kGroupCoords + 16;
+constexpr size_t kLevelBytes = ((size_t)kGroupCoords + 16 + ((kGroupCoords + 16) >> 4) + 15) & ~(size_t)15;
 constexpr size_t kWaveLdsBytes = kStageBytes + kLevelBytes + 64 * 8;
+static_assert(kStageBytes % 16 == 0 && kLevelBytes % 16 == 0, "LDS carve-out alignment");
 
 constexpr size_t decode_lds_bytes() {
     return sizeof(RecordLut) + (size_t)kWaves * kWaveLdsBytes;
@@ -560,34 +632,24 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeParams D) {
             }
         }
         const uint64_t lbase = bucket_first<RAGGED>(D, b0) & ~(uint64_t)3;
-        if (D.lds_out) {
-            const uint64_t lend = bucket_first<RAGGED>(D, b1);
-            const uint32_t nq16 = (uint32_t)((lend - lbase + 15) >> 4);
-            uint4 *l4 = reinterpret_cast<uint4 *>(lvl);
-            for (uint32_t i = (uint32_t)lane; i < nq16; i += 64) l4[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
-        // staged words and cleared levels are used by other lanes of this wave
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint32_t span = D.lds_out ? (uint32_t)(bucket_first<RAGGED>(D, b1) - lbase) : 0u;
+        const uint32_t nclear16 = (level_slot(span + 3) + 15) >> 4;
+        // staged words are read by other lanes of this wave
+        wave_sync();
         Bits<true> rl{reinterpret_cast<const uint32_t *>(stage), 0u};
         Bits<false> rg{reinterpret_cast<const uint32_t *>(D.in + w0),
                        (uint32_t)(2 * (total_words - w0)) - 1u};
         if (D.lds_out) {
-            if (in_lds) decode_group<RAGGED, true, true>(D, lut, rl, w0 * 64, b0, b1, lvl, ebs, lbase);
-            else decode_group<RAGGED, false, true>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (in_lds) decode_group<RAGGED, true, true>(D, lut, rl, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
+            else decode_group<RAGGED, false, true>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
+            wave_sync();
             store_group<RAGGED>(D, lvl, ebs, lbase, b0, b1);
         } else {
-            if (in_lds) decode_group<RAGGED, true, false>(D, lut, rl, w0 * 64, b0, b1, lvl, ebs, lbase);
-            else decode_group<RAGGED, false, false>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase);
+            if (in_lds) decode_group<RAGGED, true, false>(D, lut, rl, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
+            else decode_group<RAGGED, false, false>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
         }
         // the LDS buffers are reused by the next group of this wave
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_sync();
     }
 }
 
