@@ -60,9 +60,10 @@ struct DecodeParams {
 };
 
 // ---- record table -------------------------------------------------------
-// Entry for the next 12 stream bits: bits 0-3 record length (0: the record is
-// longer than 12 bits or has a gap or level above 16), bits 4-7 gap - 1, bits
-// 8-15 the level byte sign << 7 | k. Computed at compile time.
+// Entry for the next 12 stream bits, indexed with the first of them in bit 0:
+// bits 0-3 record length (0: the record is longer than 12 bits or has a gap or
+// level above 16), bits 4-7 gap - 1, bits 8-15 the level byte sign << 7 | k.
+// Computed at compile time.
 struct alignas(16) RecordLut {
     uint16_t e[1 << kLutBits];
 };
@@ -94,10 +95,16 @@ constexpr int lut_omega(LutCursor &c) {
     }
 }
 
+constexpr uint32_t reverse_bits(uint32_t v, int n) {
+    uint32_t r = 0;
+    for (int b = 0; b < n; ++b) r |= ((v >> b) & 1u) << (n - 1 - b);
+    return r;
+}
+
 constexpr RecordLut make_record_lut() {
     RecordLut t{};
     for (uint32_t i = 0; i < (1u << kLutBits); ++i) {
-        LutCursor c{i, 0};
+        LutCursor c{reverse_bits(i, kLutBits), 0};  // the cursor reads the first bit from the top
         uint16_t e = 0;
         const int gap = lut_omega(c);
         if (gap > 0) {
@@ -115,28 +122,40 @@ constexpr RecordLut make_record_lut() {
 __constant__ RecordLut kRecordLut = make_record_lut();
 
 // ---- bit access -----------------------------------------------------------
-// Bit positions are relative to the first stream word of the wave's bucket
-// group; a group spans fewer than 2^31 bits (buckets of at most 2^24
-// coordinates). LDS mode: dword h of the staged copy holds stream bits
-// [32h, 32h + 32) most significant first (the halves of each 64-bit word
-// swapped), followed by kStagePad zero words, so no bound check is needed.
-// Global mode: the stream's own words (bits [32h, 32h + 32) are dword h ^ 1),
-// dwords past `hlast` read as zero.
+// Bit positions fit 32 bits (a group spans fewer than 2^31 bits: buckets of at
+// most 2^24 coordinates). LDS mode: a position is an LDS bit address; the
+// wave's staged copy of the group's stream words sits bit-reversed, so that
+// the dword at byte address 4h holds stream bits [32h, 32h + 32) with the first
+// in bit 0, and kStagePad zero words follow it, so no bound check is needed.
+// Global mode: positions count from the group's first stream word (bits
+// [32h, 32h + 32) are dword h ^ 1, first bit on top); dwords past `hlast` read
+// as zero.
+typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
+
+// LDS byte address of a pointer into LDS.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 template <bool LDS>
 struct Bits {
     const uint32_t *src;
     uint32_t hlast;
 
-    __device__ __forceinline__ uint32_t dw(uint32_t h) const {
-        if (LDS) return src[h];
-        return h <= hlast ? src[h ^ 1u] : 0u;
-    }
-    // The 64 stream bits from bit p on, most significant first; at least the
-    // first 33 of them lie within the two dwords read.
+    // The 64 stream bits from bit p on, stream bit p in bit 0; at least the
+    // first 33 of them lie within the two dwords read (zeros above).
     __device__ __forceinline__ uint64_t at(uint32_t p) const {
         const uint32_t h = p >> 5;
-        const uint64_t w = ((uint64_t)dw(h) << 32) | (uint64_t)dw(h + 1u);
-        return w << (p & 31u);
+        uint64_t w;
+        if (LDS) {
+            const lds_cu32 *lds = (const lds_cu32 *)(uintptr_t)0;
+            w = ((uint64_t)lds[h + 1u] << 32) | (uint64_t)lds[h];
+        } else {
+            const uint32_t a = h <= hlast ? src[h ^ 1u] : 0u;
+            const uint32_t b = h + 1u <= hlast ? src[(h + 1u) ^ 1u] : 0u;
+            w = ((uint64_t)__builtin_bitreverse32(b) << 32) | (uint64_t)__builtin_bitreverse32(a);
+        }
+        return w >> (p & 31u);
     }
 };
 
@@ -151,14 +170,14 @@ template <bool LDS>
 __device__ __forceinline__ uint32_t omega_at(const Bits<LDS> &r, uint32_t &p, uint32_t maxbits) {
     uint32_t N = 1;
     while (true) {
-        const uint64_t w = r.at(p);
-        if ((w >> 63) == 0) {
+        const uint32_t w = (uint32_t)r.at(p);
+        if ((w & 1u) == 0) {
             p += 1u;
             return N;
         }
         const uint32_t g = N + 1u;
         if (g > maxbits) return 0;
-        N = (uint32_t)(w >> (64u - g));
+        N = __builtin_bitreverse32(w) >> (32u - g);
         p += g;
     }
 }
@@ -172,7 +191,7 @@ __device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const Record
     uint32_t q = p;
     gap = omega_at(r, q, x.gbits);
     if (gap == 0) return 0;
-    neg = (uint32_t)(r.at(q) >> 63);
+    neg = (uint32_t)r.at(q) & 1u;
     q += 1u;
     k = omega_at(r, q, x.kbits);
     if (k == 0 || k > x.s) return 0;
@@ -185,7 +204,7 @@ __device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const Record
 // speculative chain only has to be a deterministic function of its start.
 template <bool LDS>
 __device__ __forceinline__ uint32_t lut_at(const Bits<LDS> &r, const RecordCtx &x, uint32_t p) {
-    return x.lut[(uint32_t)(r.at(p) >> (64 - kLutBits))];
+    return x.lut[(uint32_t)r.at(p) & ((1u << kLutBits) - 1u)];
 }
 
 // One step of a chain: past the record at p adding its gap to sum, or one bit
@@ -403,7 +422,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
         c0 = bucket_first<RAGGED>(D, b);
         len = bucket_first<RAGGED>(D, b + 1) - c0;
         if (E >= A + 32u && len > 0) {
-            const float norm = __uint_as_float((uint32_t)(r.at(A) >> 32));
+            const float norm = __uint_as_float(__builtin_bitreverse32((uint32_t)r.at(A)));
             e_b = (double)norm / (double)D.s;
             const uint32_t Lp = E - (A + 32u);
             if (Lp > 0) {
@@ -579,22 +598,23 @@ __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t
     }
 }
 
-// Dynamic LDS: the record table, then per wave the staged stream words, the
-// group's level bytes (in level_slot order) and the per-bucket dequantization
-// factors.
+// Dynamic LDS: per wave the staged stream words, the group's level bytes (in
+// level_slot order) and the per-bucket dequantization factors; then the record
+// table.
 constexpr size_t kStageBytes = (size_t)(kStageWords + kStagePad) * 8;
 constexpr size_t kLevelBytes = ((size_t)kGroupCoords + 16 + ((kGroupCoords + 16) >> 4) + 15) & ~(size_t)15;
 constexpr size_t kWaveLdsBytes = kStageBytes + kLevelBytes + 64 * 8;
 static_assert(kStageBytes % 16 == 0 && kLevelBytes % 16 == 0, "LDS carve-out alignment");
 
-constexpr size_t decode_lds_bytes() {
-    return sizeof(RecordLut) + (size_t)kWaves * kWaveLdsBytes;
-}
+constexpr size_t decode_lds_bytes() { return (size_t)kWaves * kWaveLdsBytes + sizeof(RecordLut); }
 
 template <bool RAGGED>
 __global__ __launch_bounds__(kWG) void decode_kernel(DecodeParams D) {
     extern __shared__ __align__(16) uint64_t dsmem[];
-    uint16_t *lut = reinterpret_cast<uint16_t *>(dsmem);
+    // record table after the waves' regions (a constant offset: folds into the
+    // LDS instructions' offset field)
+    uint16_t *lut = reinterpret_cast<uint16_t *>(reinterpret_cast<unsigned char *>(dsmem) +
+                                                 (size_t)kWaves * kWaveLdsBytes);
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(kRecordLut.e);
         uint4 *dst = reinterpret_cast<uint4 *>(lut);
@@ -604,8 +624,8 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeParams D) {
 
     const int lane = lane_id();
     const int wv = wave_id();
-    unsigned char *wbase = reinterpret_cast<unsigned char *>(dsmem) + sizeof(RecordLut) +
-                           (size_t)wv * kWaveLdsBytes;
+    const uint32_t wofs = (uint32_t)wv * (uint32_t)kWaveLdsBytes;  // wave's bytes in dsmem
+    unsigned char *wbase = reinterpret_cast<unsigned char *>(dsmem) + wofs;
     uint64_t *stage = reinterpret_cast<uint64_t *>(wbase);
     uint8_t *lvl = wbase + kStageBytes;
     double *ebs = reinterpret_cast<double *>(wbase + kStageBytes + kLevelBytes);
@@ -625,27 +645,27 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeParams D) {
         const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
         const bool in_lds = nw <= (uint64_t)kStageWords;
         if (in_lds) {
-            // halves swapped: dword 2i = bits [64i, 64i + 32) of the group
-            for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64) {
-                const uint64_t w = i < nw ? D.in[w0 + i] : 0ull;
-                stage[i] = (w << 32) | (w >> 32);
-            }
+            // bit-reversed words: stream bit 64 i + t of the group in bit t of word i
+            for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64)
+                stage[i] = i < nw ? __builtin_bitreverse64(D.in[w0 + i]) : 0ull;
         }
         const uint64_t lbase = bucket_first<RAGGED>(D, b0) & ~(uint64_t)3;
         const uint32_t span = D.lds_out ? (uint32_t)(bucket_first<RAGGED>(D, b1) - lbase) : 0u;
         const uint32_t nclear16 = (level_slot(span + 3) + 15) >> 4;
         // staged words are read by other lanes of this wave
         wave_sync();
-        Bits<true> rl{reinterpret_cast<const uint32_t *>(stage), 0u};
+        // LDS positions are LDS bit addresses: the group's bit 0 is the first bit of stage
+        Bits<true> rl{nullptr, 0u};
+        const uint64_t lgbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
         Bits<false> rg{reinterpret_cast<const uint32_t *>(D.in + w0),
                        (uint32_t)(2 * (total_words - w0)) - 1u};
         if (D.lds_out) {
-            if (in_lds) decode_group<RAGGED, true, true>(D, lut, rl, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
+            if (in_lds) decode_group<RAGGED, true, true>(D, lut, rl, lgbit, b0, b1, lvl, ebs, lbase, nclear16);
             else decode_group<RAGGED, false, true>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
             wave_sync();
             store_group<RAGGED>(D, lvl, ebs, lbase, b0, b1);
         } else {
-            if (in_lds) decode_group<RAGGED, true, false>(D, lut, rl, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
+            if (in_lds) decode_group<RAGGED, true, false>(D, lut, rl, lgbit, b0, b1, lvl, ebs, lbase, nclear16);
             else decode_group<RAGGED, false, false>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
         }
         // the LDS buffers are reused by the next group of this wave
