@@ -74,8 +74,8 @@ size_t quantize_lds_bytes(const EncodePlan &p) { return EncodeLayout(0, 0, p.K).
 // Workgroups of a kernel that fit on the current device at once (cached per
 // kernel, LDS size and device; safe to call from several host threads).
 template <typename K>
-uint32_t resident_blocks(K kernel, size_t lds) {
-    struct Entry { const void *k; size_t lds; int dev; uint32_t blocks; };
+uint32_t resident_blocks(K kernel, size_t lds, int block = kWG) {
+    struct Entry { const void *k; size_t lds; int block; int dev; uint32_t blocks; };
     static std::mutex mu;
     static Entry cache[32];
     static int used = 0;
@@ -84,15 +84,16 @@ uint32_t resident_blocks(K kernel, size_t lds) {
     {
         std::lock_guard<std::mutex> g(mu);
         for (int i = 0; i < used; ++i)
-            if (cache[i].k == (const void *)kernel && cache[i].lds == lds && cache[i].dev == dev)
+            if (cache[i].k == (const void *)kernel && cache[i].lds == lds && cache[i].block == block &&
+                cache[i].dev == dev)
                 return cache[i].blocks;
     }
     int cus = 0, per_cu = 0;
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWG, lds);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds);
     const uint32_t blocks = (uint32_t)std::max(1, cus) * (uint32_t)std::max(1, per_cu);
     std::lock_guard<std::mutex> g(mu);
-    if (used < 32) cache[used++] = Entry{(const void *)kernel, lds, dev, blocks};
+    if (used < 32) cache[used++] = Entry{(const void *)kernel, lds, block, dev, blocks};
     return blocks;
 }
 
@@ -217,11 +218,11 @@ qsgd_status decode_impl(const uint64_t *in, const uint64_t *offsets, uint64_t n,
     D.tpw = tpw;
     D.lds_out = lds_out ? 1u : 0u;
     const uint64_t groups = (nb + tpw - 1) / tpw;
-    const uint64_t want = (groups + kWaves - 1) / kWaves;
+    const uint64_t want = (groups + kDecWaves - 1) / kDecWaves;
     const size_t lds = decode_lds_bytes();
     auto launch = [&](auto kernel) {
-        const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, resident_blocks(kernel, lds));
-        hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), lds, stream, D);
+        const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, resident_blocks(kernel, lds, kDecWG));
+        hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kDecWG), lds, stream, D);
     };
     if (bstart) launch(decode_kernel<true>);
     else launch(decode_kernel<false>);

@@ -41,7 +41,9 @@ namespace qsgd {
 
 constexpr int kLutBits = 12;
 constexpr int kSyncWin = 128;       // bits
-constexpr int kStageWords = 384;    // 64-bit stream words staged per wave
+constexpr int kDecWaves = 8;        // waves per decode workgroup
+constexpr int kDecWG = 64 * kDecWaves;
+constexpr int kStageWords = 320;    // 64-bit stream words staged per wave
 constexpr int kStagePad = 4;        // zero words after the staged stream
 constexpr int kGroupCoords = 4096;  // coordinates of a group whose levels are staged in LDS
 
@@ -60,12 +62,18 @@ struct DecodeParams {
 };
 
 // ---- record table -------------------------------------------------------
-// Entry for the next 12 stream bits, indexed with the first of them in bit 0:
-// bits 0-3 record length (0: the record is longer than 12 bits or has a gap or
-// level above 16), bits 4-7 gap - 1, bits 8-15 the level byte sign << 7 | k.
+// Entry for the next 12 stream bits, indexed with the first of them in bit 0.
+// It decodes the first record, and the second one if it also ends within the
+// 12 bits, when each has gap and level at most 16:
+//   bits  0-3   total length of the decoded records (0: take the general path)
+//   bits  4-7   length of the first record (== total: one record)
+//   bits  8-11  gap - 1 of the first record
+//   bits 12-19  level byte sign << 7 | k of the first record
+//   bits 20-23  gap - 1 of the second record
+//   bits 24-31  level byte of the second record
 // Computed at compile time.
 struct alignas(16) RecordLut {
-    uint16_t e[1 << kLutBits];
+    uint32_t e[1 << kLutBits];
 };
 
 struct LutCursor {
@@ -95,6 +103,17 @@ constexpr int lut_omega(LutCursor &c) {
     }
 }
 
+// One record at the cursor: (gap - 1) | level byte << 4, or -1.
+constexpr int lut_record(LutCursor &c) {
+    const int gap = lut_omega(c);
+    if (gap <= 0) return -1;
+    const int sg = lut_take(c, 1);
+    if (sg < 0) return -1;
+    const int k = lut_omega(c);
+    if (k <= 0) return -1;
+    return (gap - 1) | (((sg << 7) | k) << 4);
+}
+
 constexpr uint32_t reverse_bits(uint32_t v, int n) {
     uint32_t r = 0;
     for (int b = 0; b < n; ++b) r |= ((v >> b) & 1u) << (n - 1 - b);
@@ -105,14 +124,14 @@ constexpr RecordLut make_record_lut() {
     RecordLut t{};
     for (uint32_t i = 0; i < (1u << kLutBits); ++i) {
         LutCursor c{reverse_bits(i, kLutBits), 0};  // the cursor reads the first bit from the top
-        uint16_t e = 0;
-        const int gap = lut_omega(c);
-        if (gap > 0) {
-            const int sg = lut_take(c, 1);
-            if (sg >= 0) {
-                const int k = lut_omega(c);
-                if (k > 0) e = (uint16_t)(c.pos | ((gap - 1) << 4) | (((sg << 7) | k) << 8));
-            }
+        uint32_t e = 0;
+        const int r1 = lut_record(c);
+        if (r1 >= 0) {
+            const uint32_t l1 = (uint32_t)c.pos;
+            e = l1 | (l1 << 4) | ((uint32_t)r1 << 8);
+            LutCursor c2 = c;
+            const int r2 = lut_record(c2);
+            if (r2 >= 0) e = (e & ~15u) | (uint32_t)c2.pos | ((uint32_t)r2 << 20);
         }
         t.e[i] = e;
     }
@@ -160,7 +179,7 @@ struct Bits {
 };
 
 struct RecordCtx {
-    const uint16_t *lut;
+    const uint32_t *lut;
     uint32_t gbits, kbits, s;
 };
 
@@ -198,10 +217,12 @@ __device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const Record
     return q;
 }
 
-// Table entry of the 12 stream bits at p (0: take record_slow). The table
-// covers records of at most 12 bits with gap, k <= 16; it does not check k <= s
-// or gap <= bucket length: on the true chain those hold anyway, and a
-// speculative chain only has to be a deterministic function of its start.
+// Table entry of the 12 stream bits at p (length 0: take record_slow). The
+// table covers records of at most 12 bits with gap, k <= 16; it does not check
+// k <= s or gap <= bucket length: on the true chain those hold anyway, and a
+// speculative chain only has to be a deterministic function of its start. A
+// two-record entry is the same as two one-record steps, so every walker of a
+// chain visits the same positions.
 template <bool LDS>
 __device__ __forceinline__ uint32_t lut_at(const Bits<LDS> &r, const RecordCtx &x, uint32_t p) {
     return x.lut[(uint32_t)r.at(p) & ((1u << kLutBits) - 1u)];
@@ -214,8 +235,8 @@ __device__ __forceinline__ void chain_step(const Bits<LDS> &r, const RecordCtx &
                                            uint32_t &sum) {
     const uint32_t e = lut_at(r, x, p);
     if (e & 15u) {
-        p += e & 15u;
-        sum += ((e >> 4) & 15u) + 1u;
+        p += (e >> 4) & 15u;
+        sum += ((e >> 8) & 15u) + 1u;
     } else {
         uint32_t gap, neg, k;
         const uint32_t q = record_slow(r, x, p, gap, neg, k);
@@ -231,10 +252,10 @@ __device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const RecordCt
                                               uint32_t &gap, uint32_t &neg, uint32_t &k) {
     const uint32_t e = lut_at(r, x, p);
     if (e & 15u) {
-        gap = ((e >> 4) & 15u) + 1u;
-        k = (e >> 8) & 127u;
-        neg = (e >> 15) & 1u;
-        return p + (e & 15u);
+        gap = ((e >> 8) & 15u) + 1u;
+        k = (e >> 12) & 127u;
+        neg = (e >> 19) & 1u;
+        return p + ((e >> 4) & 15u);
     }
     return record_slow(r, x, p, gap, neg, k);
 }
@@ -249,7 +270,8 @@ constexpr uint32_t kCumSlots = 48;
 // that position (the exit), with the gap sum of the records passed. MARK: sets
 // bit (p - start) of own0:own1 for each chain position p in [start, start + 128)
 // and stores in cum[i] the gap sum before the i-th of them (saturated at 255;
-// the last slot collects the positions past kCumSlots - 2).
+// the last slot collects the positions past kCumSlots - 2). Two-record table
+// entries advance two records at once when the second starts before sn.
 template <bool LDS, bool MARK>
 __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const RecordCtx &x, uint32_t start,
                                                  uint32_t sn, uint32_t &ga, uint64_t &own0,
@@ -257,22 +279,51 @@ __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const Recor
     uint32_t p = start, sum = 0;
     if (MARK) {
         uint32_t i = 0;
+        // one step from p: returns the step's chain positions relative to p
+        auto step = [&]() -> uint64_t {
+            const uint32_t e = lut_at(r, x, p);
+            cum[i] = (uint8_t)(sum < 255u ? sum : 255u);
+            uint64_t m = 1ull;
+            if (e & 15u) {
+                const uint32_t len1 = (e >> 4) & 15u;
+                const uint32_t s1 = sum + ((e >> 8) & 15u) + 1u;
+                const bool two = len1 < (e & 15u) && p + len1 < sn;
+                cum[i + 1u < kCumSlots ? i + 1u : kCumSlots - 1u] = (uint8_t)(s1 < 255u ? s1 : 255u);
+                m |= (uint64_t)two << len1;
+                sum = two ? s1 + ((e >> 20) & 15u) + 1u : s1;
+                p += two ? (e & 15u) : len1;
+                i += two ? 2u : 1u;
+            } else {
+                chain_step(r, x, p, sum);
+                i += 1u;
+            }
+            i = i < kCumSlots ? i : kCumSlots - 1u;
+            return m;
+        };
         const uint32_t l1 = sn < start + 64u ? sn : start + 64u;
         while (p < l1) {
-            own0 |= 1ull << (p - start);
-            cum[i] = (uint8_t)(sum < 255u ? sum : 255u);
-            i = i + 1u < kCumSlots ? i + 1u : kCumSlots - 1u;
-            chain_step(r, x, p, sum);
+            const uint32_t rel = p - start;
+            const uint64_t m = step();
+            own0 |= m << rel;
+            own1 |= (m >> 1) >> (63u - rel);  // a second position past 64
         }
         const uint32_t l2 = sn < start + 128u ? sn : start + 128u;
         while (p < l2) {
-            own1 |= 1ull << (p - start - 64u);
-            cum[i] = (uint8_t)(sum < 255u ? sum : 255u);
-            i = i + 1u < kCumSlots ? i + 1u : kCumSlots - 1u;
+            const uint32_t rel = p - start - 64u;
+            own1 |= step() << rel;  // positions past 128 are not noted
+        }
+    }
+    while (p < sn) {
+        const uint32_t e = lut_at(r, x, p);
+        if (e & 15u) {
+            const uint32_t len1 = (e >> 4) & 15u;
+            const bool two = len1 < (e & 15u) && p + len1 < sn;
+            sum += ((e >> 8) & 15u) + 1u + (two ? ((e >> 20) & 15u) + 1u : 0u);
+            p += two ? (e & 15u) : len1;
+        } else {
             chain_step(r, x, p, sum);
         }
     }
-    while (p < sn) chain_step(r, x, p, sum);
     ga = sum;
     return p;
 }
@@ -297,29 +348,41 @@ __device__ __forceinline__ bool cum_lookup(const uint8_t *cum, uint64_t own0, ui
 // Phase B: continues the chain from its exit x0 (>= sn) until it lands on a
 // position noted by the next lane (nxt0:nxt1, relative to sn) or on E. Gives up
 // 128 bits past sn, past E, or at a record that does not parse.
+__device__ __forceinline__ bool meet_stop(uint32_t p, uint32_t sn, uint32_t E, uint64_t nxt0,
+                                          uint64_t nxt1, bool &found) {
+    if (p == E) { found = true; return true; }
+    const uint32_t rel = p - sn;
+    if (rel >= (uint32_t)kSyncWin || p > E) return true;
+    const uint64_t m = rel < 64u ? nxt0 : nxt1;
+    if ((m >> (rel & 63u)) & 1u) { found = true; return true; }
+    return false;
+}
+
 template <bool LDS>
 __device__ __forceinline__ bool extend_chain(const Bits<LDS> &r, const RecordCtx &x, uint32_t x0,
                                              uint32_t sn, uint32_t E, uint64_t nxt0, uint64_t nxt1,
                                              uint32_t &y, uint32_t &gb) {
     uint32_t p = x0, sum = 0;
     bool found = false;
-    while (true) {
-        if (p == E) {
-            found = true;
-            break;
+    while (!meet_stop(p, sn, E, nxt0, nxt1, found)) {
+        const uint32_t e = lut_at(r, x, p);
+        if (e & 15u) {
+            const uint32_t p1 = p + ((e >> 4) & 15u);
+            sum += ((e >> 8) & 15u) + 1u;
+            p = p1;
+            // take the second record too unless its start already ends the walk
+            bool f1 = false;
+            if ((e & 15u) > ((e >> 4) & 15u) && !meet_stop(p1, sn, E, nxt0, nxt1, f1)) {
+                sum += ((e >> 20) & 15u) + 1u;
+                p = p1 + ((e & 15u) - ((e >> 4) & 15u));
+            }
+        } else {
+            uint32_t gap, neg, k;
+            const uint32_t q = record_slow(r, x, p, gap, neg, k);
+            if (!q) break;
+            p = q;
+            sum += gap;
         }
-        const uint32_t rel = p - sn;
-        if (rel >= (uint32_t)kSyncWin || p > E) break;
-        const uint64_t m = rel < 64u ? nxt0 : nxt1;
-        if ((m >> (rel & 63u)) & 1u) {
-            found = true;
-            break;
-        }
-        uint32_t gap, neg, k;
-        const uint32_t q = record_at(r, x, p, gap, neg, k);
-        if (!q) break;
-        p = q;
-        sum += gap;
     }
     y = found ? p : E;
     gb = sum;
@@ -401,7 +464,7 @@ __device__ __forceinline__ uint32_t level_slot(uint32_t i) { return i + ((i >> 6
 // ebs[team]; otherwise every
 // lane writes its own output range with a QuadWriter.
 template <bool RAGGED, bool LDS_IN, bool LDS_OUT>
-__device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16_t *lut,
+__device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32_t *lut,
                                              const Bits<LDS_IN> &r, uint64_t gbit, uint64_t b0,
                                              uint64_t b1, uint8_t *lvl, double *ebs, uint64_t lbase,
                                              uint32_t nclear16) {
@@ -521,17 +584,34 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint16
         for (uint32_t i = (uint32_t)lane; i < nclear16; i += 64) l4[i] = make_uint4(0u, 0u, 0u, 0u);
         wave_sync();
         if (act) {
-            const uint32_t i0 = (uint32_t)(c0 - lbase);
+            // t: the coordinate's index in the group's level bytes
+            uint32_t tix = (uint32_t)(c0 - lbase) + basej - 1u;
+            const uint32_t tend = (uint32_t)(c0 - lbase) + (uint32_t)len;
             uint32_t p = ystart;
-            uint32_t jj = basej - 1u;
             while (p < ynext) {
-                uint32_t gap, neg, k;
-                const uint32_t nq = record_at(r, x, p, gap, neg, k);
-                if (!nq) break;
-                jj += gap;
-                if (jj >= (uint32_t)len) break;
-                lvl[level_slot(i0 + jj)] = (uint8_t)((neg << 7) | k);
-                p = nq;
+                const uint32_t e = lut_at(r, x, p);
+                if (e & 15u) {
+                    const uint32_t len1 = (e >> 4) & 15u;
+                    tix += ((e >> 8) & 15u) + 1u;
+                    if (tix >= tend) break;
+                    lvl[level_slot(tix)] = (uint8_t)(e >> 12);
+                    if (len1 < (e & 15u) && p + len1 < ynext) {
+                        tix += ((e >> 20) & 15u) + 1u;
+                        if (tix >= tend) break;
+                        lvl[level_slot(tix)] = (uint8_t)(e >> 24);
+                        p += e & 15u;
+                    } else {
+                        p += len1;
+                    }
+                } else {
+                    uint32_t gap, neg, k;
+                    const uint32_t nq = record_slow(r, x, p, gap, neg, k);
+                    if (!nq) break;
+                    tix += gap;
+                    if (tix >= tend) break;
+                    lvl[level_slot(tix)] = (uint8_t)((neg << 7) | k);
+                    p = nq;
+                }
             }
         }
         return;
@@ -606,19 +686,19 @@ constexpr size_t kLevelBytes = ((size_t)kGroupCoords + 16 + ((kGroupCoords + 16)
 constexpr size_t kWaveLdsBytes = kStageBytes + kLevelBytes + 64 * 8;
 static_assert(kStageBytes % 16 == 0 && kLevelBytes % 16 == 0, "LDS carve-out alignment");
 
-constexpr size_t decode_lds_bytes() { return (size_t)kWaves * kWaveLdsBytes + sizeof(RecordLut); }
+constexpr size_t decode_lds_bytes() { return (size_t)kDecWaves * kWaveLdsBytes + sizeof(RecordLut); }
 
 template <bool RAGGED>
-__global__ __launch_bounds__(kWG) void decode_kernel(DecodeParams D) {
+__global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     extern __shared__ __align__(16) uint64_t dsmem[];
     // record table after the waves' regions (a constant offset: folds into the
     // LDS instructions' offset field)
-    uint16_t *lut = reinterpret_cast<uint16_t *>(reinterpret_cast<unsigned char *>(dsmem) +
-                                                 (size_t)kWaves * kWaveLdsBytes);
+    uint32_t *lut = reinterpret_cast<uint32_t *>(reinterpret_cast<unsigned char *>(dsmem) +
+                                                 (size_t)kDecWaves * kWaveLdsBytes);
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(kRecordLut.e);
         uint4 *dst = reinterpret_cast<uint4 *>(lut);
-        for (uint32_t i = threadIdx.x; i < sizeof(RecordLut) / 16; i += kWG) dst[i] = src[i];
+        for (uint32_t i = threadIdx.x; i < sizeof(RecordLut) / 16; i += kDecWG) dst[i] = src[i];
     }
     __syncthreads();
 
@@ -634,8 +714,8 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeParams D) {
     const uint64_t total_bits = D.offsets[D.nb];
     const uint64_t total_words = (total_bits + 63) >> 6;
 
-    for (uint64_t g = (uint64_t)blockIdx.x * kWaves + (uint64_t)wv; g < ngroups;
-         g += (uint64_t)gridDim.x * kWaves) {
+    for (uint64_t g = (uint64_t)blockIdx.x * kDecWaves + (uint64_t)wv; g < ngroups;
+         g += (uint64_t)gridDim.x * kDecWaves) {
         const uint64_t b0 = g * tpw;
         const uint64_t b1 = b0 + tpw < D.nb ? b0 + tpw : D.nb;
         const uint64_t A0 = D.offsets[b0], E1 = D.offsets[b1];
