@@ -78,7 +78,9 @@ uint32_t qsgd_max_bucket(void);
 /* Number of uint64 words the `out` buffer of qsgd_encode must hold for (n, s, d):
  * a worst-case stream bound, 32 nb + n (2.5 + |omega(s)|) bits (|omega(g)| <=
  * 1.5 g bounds the gap codes of a bucket by 1.5 times its length), followed by
- * the encoder's workspace (two words per tile and a work counter). */
+ * the encoder's workspace: one slot per tile of at most 4096 coordinates, sized
+ * by the same bound for the tile, and the tiles' bit counts (about as large
+ * again as the stream bound). */
 uint64_t qsgd_encode_capacity_words(uint64_t n, uint32_t s, uint32_t d);
 
 /*

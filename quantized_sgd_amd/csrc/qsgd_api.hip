@@ -42,7 +42,7 @@ struct EncodePlan {
     uint64_t ntiles = 0;
     uint64_t stream_words = 0;  // capacity reserved for the stream
     uint64_t ws_words = 0;      // workspace words after the stream
-    uint32_t obuf_words = 0;
+    uint32_t obuf_words = 0;    // words of a tile's bit string bound, + 1 (also its slot size)
     bool table = false;         // record codes from the LDS table (s <= kTabS)
     size_t lds_bytes = 0;
 };
@@ -57,13 +57,12 @@ EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool align
     const uint64_t twice_bits = 64 * nb + n * (5 + 2 * Ls);
     p.stream_words = (twice_bits + 127) / 128 + 1;
     p.stream_words = (p.stream_words + 31) & ~(uint64_t)31;
-    p.ws_words = 2 * p.ntiles + 1;
-    // the tile's word window: records of at most 12 + Ls bits besides the
-    // pending first gaps (at most |omega(d)| bits each, one per thread), 32 bits
-    // per bucket norm, a spare word at each end
-    const uint64_t Ld = host_omega_len(std::max<uint32_t>(d, 1));
-    const uint64_t tile_bits = (uint64_t)kTC * (12 + Ls) + 32ull * p.K + (uint64_t)kWG * Ld;
-    p.obuf_words = (uint32_t)((tile_bits + 63) / 64 + 3);
+    // a tile's bit string: the same bound for its K buckets and at most 4096
+    // coordinates, plus one spare word (a two-word read at the string's end)
+    const uint64_t tile_twice_bits = 64ull * p.K + (uint64_t)kTC * (5 + 2 * Ls);
+    p.obuf_words = (uint32_t)((tile_twice_bits + 127) / 128 + 1);
+    // workspace: one slot per tile, then the tiles' lengths (uint32)
+    p.ws_words = p.ntiles * p.obuf_words + (p.ntiles + 1) / 2;
     p.table = s <= kTabS;
     p.lds_bytes = EncodeLayout(p.obuf_words, p.table ? code_table_entries(s) : 0u, p.K).total;
     return p;
@@ -165,30 +164,41 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     QsgdParams P{};
     P.v = v; P.n = n; P.nb = nb; P.bstart = bstart; P.seed = seed; P.s = s; P.d = d;
     P.K = p.K; P.ntiles = (uint32_t)p.ntiles;
-    P.out = out; P.out_bits = out_bits; P.offsets = offsets;
-    P.status = out + p.stream_words;
-    P.carry = P.status + p.ntiles;
-    P.ticket = reinterpret_cast<uint32_t *>(P.carry + p.ntiles);
+    P.offsets = offsets;
+    P.slots = out + p.stream_words;
+    P.tile_bits = reinterpret_cast<uint32_t *>(P.slots + p.ntiles * p.obuf_words);
     P.obuf_words = p.obuf_words;
-    const uint32_t init_blocks = (uint32_t)std::min<uint64_t>((p.ntiles + 255) / 256, 1024);
-    hipLaunchKernelGGL(encode_init_kernel, dim3(std::max<uint32_t>(init_blocks, 1)), dim3(256), 0,
-                       stream, P.status, P.carry, P.ticket, (uint32_t)p.ntiles);
+    // pass 1: every tile into its slot
     if (use_aligned(bstart, s, d)) {
         const size_t lds = aligned_encode_lds_bytes(p.obuf_words, s);
         const uint32_t blocks =
             (uint32_t)std::min<uint64_t>(p.ntiles, resident_blocks(encode_aligned_kernel, lds));
         hipLaunchKernelGGL(encode_aligned_kernel, dim3(blocks), dim3(kWG), lds, stream, P, log2u(d));
-        return launch_status();
-    }
-    auto launch = [&](auto kernel) {
-        const uint32_t blocks = (uint32_t)std::min<uint64_t>(p.ntiles, resident_blocks(kernel, p.lds_bytes));
-        hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), p.lds_bytes, stream, P);
-    };
-    if (ragged) {
-        if (p.table) launch(encode_kernel<true, true>); else launch(encode_kernel<true, false>);
     } else {
-        if (p.table) launch(encode_kernel<false, true>); else launch(encode_kernel<false, false>);
+        auto launch = [&](auto kernel) {
+            const uint32_t blocks =
+                (uint32_t)std::min<uint64_t>(p.ntiles, resident_blocks(kernel, p.lds_bytes));
+            hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), p.lds_bytes, stream, P);
+        };
+        if (ragged) {
+            if (p.table) launch(encode_kernel<true, true>); else launch(encode_kernel<true, false>);
+        } else {
+            if (p.table) launch(encode_kernel<false, true>); else launch(encode_kernel<false, false>);
+        }
     }
+    if (hipGetLastError() != hipSuccess) return QSGD_ERR_LAUNCH;
+    // pass 2: tile offsets, the stream words, absolute bucket offsets
+    FinishParams F{};
+    F.out = out; F.slots = P.slots; F.tile_bits = P.tile_bits; F.offsets = offsets;
+    F.out_bits = out_bits; F.nb = nb; F.ntiles = (uint32_t)p.ntiles; F.slot_words = p.obuf_words;
+    F.K = p.K;
+    const uint32_t fblocks = (uint32_t)std::min<uint64_t>(p.ntiles, 1024);
+    F.chunk = (uint32_t)((p.ntiles + fblocks - 1) / fblocks);
+    if (F.chunk > (uint32_t)kFinishTiles) {
+        F.chunk = kFinishTiles;
+    }
+    const uint32_t fgrid = (uint32_t)((p.ntiles + F.chunk - 1) / F.chunk);
+    hipLaunchKernelGGL(encode_finish_kernel, dim3(fgrid), dim3(kWG), 0, stream, F);
     return launch_status();
 }
 

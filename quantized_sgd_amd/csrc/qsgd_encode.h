@@ -1,11 +1,12 @@
-// Quantize kernel and the fused single-pass encode kernel.
+// Quantize kernel and the two-pass encode.
 //
 // Page "QSGD (Quantized Stochastic Gradient Descent) with Elias Coding":
 // definition paragraph (Q_s and the Elias-coded tuple of norm, signs, non-zero
 // gaps and levels) and the claim on Elias coding (F = 32 bit norm).
 //
-// Encode, per tile (a run of whole buckets, <= 4096 coordinates, one workgroup;
-// workgroups are persistent and take tiles in order from a work counter):
+// Encode pass 1, per tile (a run of whole buckets, <= 4096 coordinates, one
+// workgroup; persistent workgroups take tiles blockIdx.x, blockIdx.x + gridDim.x,
+// ..., so no workgroup ever waits for another):
 //   1. load v once from HBM, per-bucket norms, Philox rounding (qsgd_front.h);
 //   2. each thread looks up the code of every coordinate's record -- the 32-bit
 //      norm at a bucket start, and omega(gap) | sign | omega(k) per non-zero --
@@ -14,15 +15,14 @@
 //      of a thread's first non-zero, when its origin lies in an earlier thread,
 //      is resolved after an exclusive max-scan of "last marker" positions;
 //   3. an exclusive sum-scan of per-thread bit counts gives each thread's offset
-//      in the tile and the tile's size T;
-//   4. decoupled lookback over earlier tiles' status words (agent-scope atomics,
-//      flag and value packed in one 64-bit word) gives the tile's stream offset;
-//   5. every record is OR-ed into the tile's 64-bit words in LDS at its final
-//      bit position, and the words are stored with coalesced 8-byte stores. The
-//      word shared with the previous tile is completed with that tile's
-//      published "carry" (its partial last word); the tile's own partial last
-//      word is published the same way for the next tile.
-// Every output word is written by exactly one tile; v is read once.
+//      in the tile and the tile's length T;
+//   4. every record is OR-ed into the tile's 64-bit words in LDS at its offset
+//      from the tile's first bit; the words go to the tile's slot in the
+//      workspace, T to tile_bits, and the bucket offsets (tile-relative) to the
+//      offsets array.
+// Encode pass 2 (encode_finish_kernel): tile offsets by prefix sums of T, each
+// stream word gathered from the slots of the tiles it covers (every word
+// written once), bucket offsets made absolute.
 #pragma once
 
 #include "qsgd_front.h"
@@ -151,106 +151,10 @@ __global__ __launch_bounds__(kWG) void quantize_kernel(QsgdParams P) {
     for (uint32_t b = threadIdx.x; b < t.K; b += kWG) P.norms[t.b0 + b] = L.f.nrm[b];
 }
 
-__global__ void encode_init_kernel(uint64_t *status, uint64_t *carry, uint32_t *ticket, uint32_t ntiles) {
-    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-    const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t t = i; t < ntiles; t += stride) {
-        status[t] = 0;
-        carry[t] = 0;
-    }
-    if (i == 0) *ticket = 0;
-}
-
 __global__ void encode_empty_kernel(uint64_t *out_bits, uint64_t *offsets) {
     if (threadIdx.x == 0 && blockIdx.x == 0) {
         *out_bits = 0;
         offsets[0] = 0;
-    }
-}
-
-constexpr uint64_t kFlagAgg = 1ull << 62;
-constexpr uint64_t kFlagIncl = 2ull << 62;
-constexpr uint64_t kValMask = (1ull << 62) - 1;
-
-// Decoupled lookback (Merrill and Garland, single-pass prefix scan), run by wave
-// 0 of the tile's workgroup: publishes the tile's bit count T as an aggregate,
-// sums the predecessors' values back to the nearest inclusive one (lane l
-// inspects tile - 1 - l, 64 tiles per step) and publishes the inclusive value.
-// Returns the tile's exclusive stream offset, uniform across the wave. Waits
-// only in wave-uniform control flow.
-__device__ __forceinline__ uint64_t tile_lookback(const QsgdParams &P, uint32_t tile, uint32_t T) {
-    const int lane = lane_id();
-    if (lane == 0) st_agent(&P.status[tile], (tile == 0 ? kFlagIncl : kFlagAgg) | (uint64_t)T);
-    uint64_t excl = 0;
-    int64_t i = (int64_t)tile - 1;
-    while (i >= 0) {
-        const int64_t idx = i - lane;
-        const uint64_t w = idx >= 0 ? ld_agent(&P.status[idx]) : kFlagIncl;
-        const uint64_t f = w & ~kValMask;
-        const uint64_t incl = __ballot(f == kFlagIncl);
-        const uint64_t zero = __ballot(f == 0);
-        // lanes up to (and including) the nearest inclusive one, if all ready
-        const int pfx = incl ? __builtin_ctzll(incl) : 63;
-        const uint64_t need = (pfx == 63) ? ~0ull : ((2ull << pfx) - 1ull);
-        if ((zero & need) != 0) {
-            __builtin_amdgcn_s_sleep(1);
-            continue;
-        }
-        uint64_t v = (lane <= pfx) ? (w & kValMask) : 0ull;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-        excl += v;
-        if (incl) break;
-        i -= 64;
-    }
-    excl = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(excl >> 32)) << 32) |
-           (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)excl);
-    if (lane == 0 && tile != 0) st_agent(&P.status[tile], kFlagIncl | (excl + (uint64_t)T));
-    return excl;
-}
-
-// Stores the tile's W words (stream bits [base - head, base + T), head = base
-// mod 64): interior words by all threads, the edge words by wave 0. The word
-// shared with the previous tile is completed with that tile's published carry
-// (its partial last word, bit 0 = ready); the tile's own partial last word is
-// published the same way unless it is the last tile.
-__device__ __forceinline__ void store_tile(const QsgdParams &P, const uint64_t *obuf, uint32_t tile,
-                                           uint64_t base, uint32_t T, uint32_t W, int wave, int lane,
-                                           bool last) {
-    uint64_t *dst = P.out + (base >> 6);
-    for (uint32_t w = 1 + threadIdx.x; w + 1 < W; w += kWG) dst[w] = obuf[w];
-    if (wave != 0) return;
-    const bool head_shared = (base & 63u) != 0;
-    const bool tail_partial = ((base + T) & 63u) != 0;
-    if (W > 1) {
-        if (tail_partial && !last) {
-            if (lane == 0) st_agent(&P.carry[tile], obuf[W - 1] | 1ull);
-        } else {
-            if (lane == 0) {
-                dst[W - 1] = obuf[W - 1];
-                st_agent(&P.carry[tile], 1ull);
-            }
-        }
-    }
-    uint64_t hw = obuf[0];
-    if (head_shared) {
-        uint64_t cw;
-        while (true) {
-            cw = ld_agent(&P.carry[tile - 1]);
-            if (__builtin_amdgcn_readfirstlane((uint32_t)cw) & 1u) break;
-            __builtin_amdgcn_s_sleep(1);
-        }
-        hw |= cw & ~1ull;
-    }
-    if (lane == 0) {
-        if (W > 1) {
-            dst[0] = hw;
-        } else if (tail_partial && !last) {
-            st_agent(&P.carry[tile], hw | 1ull);
-        } else {
-            dst[0] = hw;
-            st_agent(&P.carry[tile], 1ull);
-        }
     }
 }
 
@@ -281,8 +185,6 @@ __device__ __forceinline__ uint32_t record_entry(const uint32_t *rt, uint32_t g,
 template <bool RAGGED, bool TABLE>
 __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ uint32_t sh_tile;
-    __shared__ uint64_t sh_base;
     __shared__ int sh_mx[kWaves];
     __shared__ uint32_t sh_bits[kWaves];
 
@@ -294,21 +196,8 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
     // the wave index as a scalar, so that branches on it are uniform to the compiler
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
 
-    for (;;) {
-        // Every wait and every single-lane section below sits in wave-uniform
-        // control flow (decisions on readfirstlane values): a lane-divergent
-        // spin loop inside this persistent loop lets the compiler run the next
-        // iteration's barrier for some lanes of wave 0 before the waiting lane
-        // has left, which desynchronises the workgroup's barriers.
-        if (wave == 0) {
-            uint32_t tk = 0;
-            if (lane == 0) tk = atomicAdd(P.ticket, 1u);
-            tk = __builtin_amdgcn_readfirstlane(tk);
-            if (lane == 0) sh_tile = tk;
-        }
-        __syncthreads();  // also separates this tile's LDS use from the previous one
-        const uint32_t tile = __builtin_amdgcn_readfirstlane(sh_tile);
-        if (tile >= P.ntiles) break;
+    for (uint32_t tile = blockIdx.x; tile < P.ntiles; tile += gridDim.x) {
+        __syncthreads();  // separates this tile's LDS use from the previous one
         const Tile t = tile_geometry<RAGGED>(P, tile);
         fill_bucket_starts<RAGGED>(P, t, L.f);
         ThreadCoords c;
@@ -378,25 +267,12 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
         if (lane == 0) off = 0;
         off += bpre;
 
-        // ---- decoupled lookback: stream offset of this tile ----
-        if (wave == 0) {
-            const uint64_t excl = tile_lookback(P, tile, T);
-            if (lane == 0) sh_base = excl;
-        }
-        __syncthreads();
-        const uint64_t base = sh_base;
-        const uint32_t head = (uint32_t)(base & 63u);
-        const uint32_t W = (head + T + 63u) >> 6;
-        for (uint32_t w = threadIdx.x; w < W; w += kWG) L.obuf[w] = 0;
-        const bool last = (tile == P.ntiles - 1);
-        if (last && j == 0) {
-            P.offsets[P.nb] = base + T;
-            *P.out_bits = base + T;
-        }
+        const uint32_t W = (T + 63u) >> 6;
+        for (uint32_t w = threadIdx.x; w <= W; w += kWG) L.obuf[w] = 0;
         __syncthreads();
 
-        // ---- phase 2: OR every record into the tile's words at its position ----
-        uint32_t p = head + off;
+        // ---- phase 2: OR every record into the tile's words at its offset ----
+        uint32_t p = off;
         if (Lp) or_bits(L.obuf, p, pc << (64u - Lp), Lp);
         p += Lp;
         int kb = c.kf;
@@ -405,7 +281,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
         for (int q = 0; q < kCPT; ++q) {
             if ((lv.bst >> q) & 1u) {
                 ++kb;
-                P.offsets[t.b0 + kb] = base - head + p;
+                P.offsets[t.b0 + kb] = p;
                 or_bits(L.obuf, p, (uint64_t)__float_as_uint(L.f.nrm[kb]) << 32, 32u);
                 p += 32u;
             }
@@ -418,18 +294,21 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
         }
         __syncthreads();
 
-        store_tile(P, L.obuf, tile, base, T, W, wave, lane, last);
+        // ---- the tile's words to its slot ----
+        uint64_t *slot = P.slots + (uint64_t)tile * P.obuf_words;
+        for (uint32_t w = threadIdx.x; w < W; w += kWG) slot[w] = L.obuf[w];
+        if (j == 0) P.tile_bits[tile] = T;
     }
 }
 
-// Aligned fast path, front half: loads the thread's 16 coordinates from g0 (0
-// past n) and returns its bucket's norm RN32(sqrt(sum of squares)). The sum:
-// fp64 fma per thread in index order, an xor butterfly over the bucket's lanes
-// (both operands of every addition are the same pair on each lane, so all lanes
-// get the same bits), and for G > 64 the bucket's waves added in wave order
-// through red[kWaves] (ends with a barrier in that case; G is uniform).
-__device__ __forceinline__ float aligned_front(const QsgdParams &P, uint64_t g0, uint32_t G,
-                                               double *red, float (&x)[kCPT]) {
+// Aligned fast path, front half. aligned_load: the thread's 16 coordinates
+// from g0 (0 past n). aligned_norm: the bucket norm RN32(sqrt(sum of squares))
+// of the thread's bucket. The sum: fp64 fma per thread in index order, an xor
+// butterfly over the bucket's lanes (both operands of every addition are the
+// same pair on each lane, so all lanes get the same bits), and for G > 64 the
+// bucket's waves added in wave order through red[kWaves] (ends with a barrier
+// in that case; G is uniform).
+__device__ __forceinline__ void aligned_load(const QsgdParams &P, uint64_t g0, float (&x)[kCPT]) {
     if (g0 + kCPT <= P.n) {
         const float4 *src = reinterpret_cast<const float4 *>(P.v + g0);
 #pragma unroll
@@ -444,6 +323,9 @@ __device__ __forceinline__ float aligned_front(const QsgdParams &P, uint64_t g0,
 #pragma unroll
         for (int q = 0; q < kCPT; ++q) x[q] = g0 + q < P.n ? P.v[g0 + q] : 0.0f;
     }
+}
+
+__device__ __forceinline__ float aligned_norm(const float (&x)[kCPT], uint32_t G, double *red) {
     double acc = 0.0;
 #pragma unroll
     for (int q = 0; q < kCPT; ++q) {
@@ -474,7 +356,8 @@ __global__ __launch_bounds__(kWG) void quantize_aligned_kernel(QsgdParams P, uin
     const uint32_t tile = blockIdx.x;
     const uint64_t g0 = (uint64_t)tile * kTC + (uint64_t)(j * kCPT);
     float x[kCPT];
-    const float norm = aligned_front(P, g0, G, sh_red, x);
+    aligned_load(P, g0, x);
+    const float norm = aligned_norm(x, G, sh_red);
     const double cb = norm == 0.0f ? 0.0 : (double)P.s / (double)norm;
     if ((j & (G - 1)) == 0 && g0 < P.n) P.norms[g0 >> log2d] = norm;
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
@@ -503,36 +386,67 @@ __global__ __launch_bounds__(kWG) void quantize_aligned_kernel(QsgdParams P, uin
     }
 }
 
-// Encode fast path for buckets of d = 2^m coordinates, 16 <= d <= 4096, one
-// vector, s <= kTabS. Tile t is the 4096 coordinates from 4096 t (4096 / d whole
-// buckets); the G = d / 16 threads of a bucket are consecutive, so each thread's
-// 16 coordinates lie in one bucket and thread j starts a bucket iff j mod G = 0.
-// Coordinates past n read as 0, which quantize to level 0 and add nothing to a
-// norm. Per tile:
-//   - bucket sums of squares: fp64 per thread in index order, then an xor
-//     butterfly over the bucket's lanes and, for d > 1024, the bucket's waves in
-//     wave order through LDS; every thread of a bucket ends with the same sum;
-//   - levels and record codes as in the general kernel;
-//   - each thread packs its bit string (norm or pending first gap, then its
-//     records) into a 64-bit register and ORs full registers into the tile's
-//     LDS words, so a thread usually issues two LDS atomics per tile.
+// Encode pass 1, fast path for buckets of d = 2^m coordinates, 16 <= d <= 4096,
+// one vector, s <= kTabS. Tile t is the 4096 coordinates from 4096 t (4096 / d
+// whole buckets); the G = d / 16 threads of a bucket are consecutive, so each
+// thread's 16 coordinates lie in one bucket and thread j starts a bucket iff
+// j mod G = 0. Coordinates past n read as 0, which quantize to level 0 and add
+// nothing to a norm. Per tile:
+//   - the workgroup's next tile (tile + gridDim.x) is copied into LDS with
+//     direct global-to-LDS loads while this one is processed;
+//   - bucket norms (aligned_norm), levels and record codes as in the general
+//     kernel; each thread packs its records into two 64-bit registers
+//     (coordinates 0-7 and 8-15) while it codes them;
+//   - exclusive max-scan of markers (origin of each thread's pending first gap)
+//     and sum-scan of bit counts;
+//   - each thread ORs its bit string (norm or pending first gap, then its two
+//     record registers) into the tile's LDS words at its offset, and the words
+//     go to the tile's slot.
 __host__ __device__ constexpr size_t aligned_encode_lds_bytes(uint32_t obuf_words, uint32_t s) {
-    return align16((size_t)obuf_words * 8) + align16((size_t)code_table_entries(s) * 4);
+    return align16((size_t)obuf_words * 8) + align16((size_t)code_table_entries(s) * 4) +
+           (size_t)kTC * 4;
+}
+
+// Starts copying the 4096 coordinates of a whole tile from v[g] into LDS
+// pbuf[0, 4096) with direct global-to-LDS loads: wave w copies the 4 KB its own
+// threads use (thread j's 16 coordinates land at pbuf[16 j]), so a wave only
+// has to wait for its own loads (vmcnt) before reading them.
+__device__ __forceinline__ void tile_prefetch_lds(const float *v, uint64_t g, float *pbuf, int wave,
+                                                  int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t o = (uint32_t)wave * 1024u + (uint32_t)i * 256u;
+        __builtin_amdgcn_global_load_lds(v + g + o + 4u * (uint32_t)lane,
+                                         (__attribute__((address_space(3))) void *)(pbuf + o), 16, 0, 0);
+    }
+}
+
+// A tile's results (aligned path): its words to its slot, each thread clearing
+// the LDS words it copied; its length; its tile-relative bucket offsets.
+__device__ __forceinline__ void store_tile_slot(const QsgdParams &P, uint64_t *obuf, uint32_t tile,
+                                                uint32_t T, bool bstart, uint32_t off, uint32_t log2d) {
+    const uint32_t W = (T + 63u) >> 6;
+    uint64_t *slot = P.slots + (uint64_t)tile * P.obuf_words;
+    for (uint32_t w = threadIdx.x; w < W; w += kWG) {
+        slot[w] = obuf[w];
+        obuf[w] = 0;
+    }
+    if (threadIdx.x == 0) P.tile_bits[tile] = T;
+    if (bstart) P.offsets[((uint64_t)tile << (12 - log2d)) + (threadIdx.x >> (log2d - 4))] = off;
 }
 
 __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint32_t log2d) {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ uint32_t sh_tile;
-    __shared__ uint64_t sh_base;
     __shared__ int sh_mx[kWaves];
     __shared__ uint32_t sh_bits[kWaves];
     __shared__ double sh_red[kWaves];
 
-    // dynamic LDS: [obuf][rt] (aligned_encode_lds_bytes)
-    EncodeLds L{};
-    L.obuf = reinterpret_cast<uint64_t *>(smem);
-    L.rt = reinterpret_cast<uint32_t *>(smem + align16((size_t)P.obuf_words * 8));
-    build_code_table(L.rt, P.s);
+    // dynamic LDS: [obuf][rt][pbuf] (aligned_encode_lds_bytes)
+    uint64_t *obuf = reinterpret_cast<uint64_t *>(smem);
+    uint32_t *rt = reinterpret_cast<uint32_t *>(smem + align16((size_t)P.obuf_words * 8));
+    float *pbuf = reinterpret_cast<float *>(smem + align16((size_t)P.obuf_words * 8) +
+                                            align16((size_t)code_table_entries(P.s) * 4));
+    build_code_table(rt, P.s);
     const int j = (int)threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
@@ -540,30 +454,43 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
     const int x0 = j * kCPT;
     const bool first_of_bucket = (j & (G - 1)) == 0;
-    uint32_t Wprev = P.obuf_words;  // words to clear before the first tile
+    // the previous tile's results go out after the next tile's first barrier,
+    // before that tile's prefetch is issued, so the wait for the prefetch never
+    // waits for these stores
+    uint32_t prev_tile = 0xffffffffu, prev_T = 0, prev_off = 0;
+    bool prev_bstart = false;
 
-    for (;;) {
-        // waits and single-lane sections stay in wave-uniform control flow
-        if (wave == 0) {
-            uint32_t tk = 0;
-            if (lane == 0) tk = atomicAdd(P.ticket, 1u);
-            tk = __builtin_amdgcn_readfirstlane(tk);
-            if (lane == 0) sh_tile = tk;
-        }
-        __syncthreads();  // also separates this tile's LDS use from the previous one
-        const uint32_t tile = __builtin_amdgcn_readfirstlane(sh_tile);
-        if (tile >= P.ntiles) break;
-        for (uint32_t w = threadIdx.x; w < Wprev; w += kWG) L.obuf[w] = 0;
+    // whole tiles are prefetched into pbuf; a partial tile is loaded directly
+    uint32_t cur = blockIdx.x;
+    bool pref = cur < P.ntiles && (uint64_t)cur * kTC + kTC <= P.n;
+    if (pref) tile_prefetch_lds(P.v, (uint64_t)cur * kTC, pbuf, wave, lane);
 
+    for (; cur < P.ntiles; cur += gridDim.x) {
+        const uint32_t tile = cur;
         const uint64_t g0 = (uint64_t)tile * kTC + (uint64_t)x0;
         float x[kCPT];
-        const float norm = aligned_front(P, g0, G, sh_red, x);
+        if (pref) {
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's prefetch has landed
+            const float4 *src = reinterpret_cast<const float4 *>(pbuf + x0);
+#pragma unroll
+            for (int q = 0; q < kCPT / 4; ++q) {
+                const float4 f = src[q];
+                x[4 * q + 0] = f.x;
+                x[4 * q + 1] = f.y;
+                x[4 * q + 2] = f.z;
+                x[4 * q + 3] = f.w;
+            }
+        } else {
+            aligned_load(P, g0, x);
+        }
+        const float norm = aligned_norm(x, G, sh_red);
         const double cb = norm == 0.0f ? 0.0 : (double)P.s / (double)norm;
         const bool bstart = first_of_bucket && g0 < P.n;
 
-        // ---- levels and record codes; records packed into two 64-bit
-        // registers (coordinates 0-7 and 8-15), right-aligned ----
-        uint32_t ec[kCPT];
+        // ---- levels and record codes; records packed right-aligned into two
+        // 64-bit registers (coordinates 0-7 and 8-15); levels kept as bytes
+        // sign << 7 | k for the rare half longer than 64 bits ----
+        uint32_t lvb[kCPT / 4] = {0, 0, 0, 0};
         uint64_t racc[2] = {0, 0};
         uint32_t rlen[2] = {0, 0};
         int prev = x0 - 1;
@@ -586,8 +513,8 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
                 const uint32_t k = qlevel(x[q], cb, w[e]);
                 const uint32_t neg = __float_as_uint(x[q]) >> 31;
                 const uint32_t gg = have ? (uint32_t)(xi - prev) : 0u;
-                const uint32_t ent = L.rt[code_index(gg, k, neg)];
-                ec[q] = ent;
+                const uint32_t ent = rt[code_index(gg, k, neg)];
+                lvb[g] |= ((neg << 7) | k) << (8 * e);
                 const uint32_t len = ent & 31u;
                 racc[q >> 3] = (racc[q >> 3] << len) | (uint64_t)(ent >> 5);
                 rlen[q >> 3] += len;
@@ -604,6 +531,17 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         const int mi = wave_incl_scan(marker, [](int a, int b) { return a > b ? a : b; });
         if (lane == 63) sh_mx[wave] = mi;
         __syncthreads();
+        // the previous tile's words to its slot (each thread clears the words it
+        // copied), then start loading the next tile (this wave has read its
+        // part of pbuf)
+        if (prev_tile != 0xffffffffu) {
+            store_tile_slot(P, obuf, prev_tile, prev_T, prev_bstart, prev_off, log2d);
+        } else {
+            for (uint32_t w = threadIdx.x; w < P.obuf_words; w += kWG) obuf[w] = 0;
+        }
+        const uint32_t nxt = cur + gridDim.x;
+        const bool pref_next = nxt < P.ntiles && (uint64_t)nxt * kTC + kTC <= P.n;
+        if (pref_next) tile_prefetch_lds(P.v, (uint64_t)nxt * kTC, pbuf, wave, lane);
         int mpre = INT_MIN;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
@@ -630,50 +568,149 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         if (lane == 0) off = 0;
         off += bpre;
 
-        // ---- decoupled lookback: stream offset of this tile ----
-        if (wave == 0) {
-            const uint64_t excl = tile_lookback(P, tile, T);
-            if (lane == 0) sh_base = excl;
-        }
-        __syncthreads();
-        const uint64_t base = sh_base;
-        const uint32_t head = (uint32_t)(base & 63u);
-        const uint32_t W = (head + T + 63u) >> 6;
-        const bool last = (tile == P.ntiles - 1);
-        if (last && j == 0) {
-            P.offsets[P.nb] = base + T;
-            *P.out_bits = base + T;
-        }
-
-        // ---- phase 2: OR the thread's pieces into the tile's words ----
-        uint32_t p = head + off;
+        // ---- OR the thread's pieces into the tile's words ----
+        uint32_t p = off;
         if (bstart) {
-            P.offsets[((uint64_t)tile << (12 - log2d)) + ((uint32_t)j >> (log2d - 4))] = base + off;
-            or_bits(L.obuf, p, (uint64_t)__float_as_uint(norm) << 32, 32u);
+            or_bits(obuf, p, (uint64_t)__float_as_uint(norm) << 32, 32u);
             p += 32u;
         } else if (Lp) {
-            or_bits(L.obuf, p, pc << (64u - Lp), Lp);
+            or_bits(obuf, p, pc << (64u - Lp), Lp);
             p += Lp;
         }
-#pragma unroll
         for (int h = 0; h < 2; ++h) {
             if (rlen[h] <= 64u) {
-                if (rlen[h]) or_bits(L.obuf, p, racc[h] << (64u - rlen[h]), rlen[h]);
+                if (rlen[h]) or_bits(obuf, p, racc[h] << (64u - rlen[h]), rlen[h]);
                 p += rlen[h];
             } else {
-                // more than 64 bits in this half: one record at a time
-#pragma unroll
-                for (int q = 8 * h; q < 8 * h + 8; ++q) {
-                    const uint32_t len = ec[q] & 31u;
-                    if (len) or_bits(L.obuf, p, (uint64_t)(ec[q] >> 5) << (64u - len), len);
-                    p += len;
+                // more than 64 bits in this half: its records one at a time,
+                // the gaps followed from the thread's first coordinate
+                int pv = x0 - 1;
+                bool hv = bstart;
+#pragma unroll 1
+                for (int q = 0; q < 8 * h + 8; ++q) {
+                    const uint32_t wv = lvb[0] * (q < 4) + lvb[1] * (q >= 4 && q < 8) +
+                                        lvb[2] * (q >= 8 && q < 12) + lvb[3] * (q >= 12);
+                    const uint32_t b8 = (wv >> (8 * (q & 3))) & 255u;
+                    const uint32_t k = b8 & 127u;
+                    if (q >= 8 * h) {
+                        const uint32_t gg = hv ? (uint32_t)(x0 + q - pv) : 0u;
+                        const uint32_t ent = rt[code_index(gg, k, b8 >> 7)];
+                        const uint32_t len = ent & 31u;
+                        if (len) or_bits(obuf, p, (uint64_t)(ent >> 5) << (64u - len), len);
+                        p += len;
+                    }
+                    pv = k ? x0 + q : pv;
+                    hv = hv || k != 0u;
                 }
             }
         }
+        prev_tile = tile;
+        prev_T = T;
+        prev_off = off;
+        prev_bstart = bstart;
+        pref = pref_next;
+    }
+    if (prev_tile != 0xffffffffu) {
         __syncthreads();
+        store_tile_slot(P, obuf, prev_tile, prev_T, prev_bstart, prev_off, log2d);
+    }
+}
 
-        store_tile(P, L.obuf, tile, base, T, W, wave, lane, last);
-        Wprev = W;
+// Encode pass 2. Workgroup w takes tiles [t0, t1) (a contiguous share): the
+// stream offset of t0 is the sum of all earlier tiles' lengths, then a block
+// scan gives its tiles' offsets. Stream word i (bits [64 i, 64 i + 64)) is
+// written by the workgroup of the tile holding bit 64 i, gathered from that
+// tile's slot and, past its end, from the next tiles' slots. The tiles' bucket
+// offsets get the tile offset added; the last tile also writes offsets[nb] and
+// out_bits.
+struct FinishParams {
+    uint64_t *out;
+    const uint64_t *slots;
+    const uint32_t *tile_bits;
+    uint64_t *offsets;
+    uint64_t *out_bits;
+    uint64_t nb;
+    uint32_t ntiles;
+    uint32_t slot_words;
+    uint32_t K;        // buckets per tile
+    uint32_t chunk;    // tiles per workgroup
+};
+
+constexpr int kFinishTiles = 256;  // tiles per finish workgroup at most
+
+// The `take` (1..64) bits of tile tt's string from bit rel on, at the top of
+// the result.
+__device__ __forceinline__ uint64_t slot_bits(const FinishParams &F, uint32_t tt, uint32_t rel,
+                                              uint32_t take) {
+    const uint64_t *s = F.slots + (uint64_t)tt * F.slot_words;
+    const uint32_t wi = rel >> 6, sh = rel & 63u;
+    uint64_t x = s[wi] << sh;
+    if (sh) x |= s[wi + 1] >> (64u - sh);
+    return take >= 64u ? x : (x & ~(~0ull >> take));
+}
+
+__global__ __launch_bounds__(kWG) void encode_finish_kernel(FinishParams F) {
+    __shared__ uint64_t sh_base[kFinishTiles + 1];
+    __shared__ uint64_t sh_red[kWaves];
+    __shared__ uint64_t sh_scan[kWaves];
+    const uint32_t t0 = blockIdx.x * F.chunk;
+    const uint32_t t1 = t0 + F.chunk < F.ntiles ? t0 + F.chunk : F.ntiles;
+    if (t0 >= t1) return;
+    const int j = (int)threadIdx.x;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+
+    // stream offset of t0
+    uint64_t acc = 0;
+    for (uint32_t t = (uint32_t)j; t < t0; t += kWG) acc += F.tile_bits[t];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) sh_red[wave] = acc;
+    __syncthreads();
+    uint64_t pre = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) pre += sh_red[w];
+    // offsets of this share's tiles (chunk <= kFinishTiles <= kWG)
+    const uint32_t m = t1 - t0;
+    const uint64_t mine = (uint32_t)j < m ? (uint64_t)F.tile_bits[t0 + j] : 0ull;
+    uint64_t total = 0;
+    const uint64_t ex = block_excl_scan(mine, [](uint64_t a, uint64_t b) { return a + b; }, (uint64_t)0,
+                                        sh_scan, total);
+    if ((uint32_t)j < m) sh_base[j] = pre + ex;
+    if (j == 0) sh_base[m] = pre + total;  // end of the share
+    __syncthreads();
+
+    // stream words whose first bit lies in each tile
+    for (uint32_t i = 0; i < m; ++i) {
+        const uint64_t b = sh_base[i], e = sh_base[i + 1];
+        const uint64_t w0 = (b + 63) >> 6, w1 = (e + 63) >> 6;
+        for (uint64_t w = w0 + (uint64_t)j; w < w1; w += kWG) {
+            uint32_t tt = t0 + i;
+            uint32_t rel = (uint32_t)((w << 6) - b);
+            uint32_t Tt = (uint32_t)(e - b);
+            uint64_t v = 0;
+            uint32_t have = 0;
+            while (true) {
+                const uint32_t avail = Tt - rel;
+                const uint32_t take = 64u - have < avail ? 64u - have : avail;
+                v |= slot_bits(F, tt, rel, take) >> have;
+                have += take;
+                if (have >= 64u) break;
+                ++tt;
+                if (tt >= F.ntiles) break;
+                rel = 0;
+                Tt = F.tile_bits[tt];
+            }
+            F.out[w] = v;
+        }
+        // bucket offsets of this tile
+        const uint64_t b0 = (uint64_t)(t0 + i) * F.K;
+        const uint64_t b1 = b0 + F.K < F.nb ? b0 + F.K : F.nb;
+        for (uint64_t bb = b0 + (uint64_t)j; bb < b1; bb += kWG) F.offsets[bb] += b;
+    }
+    if (t1 == F.ntiles && j == 0) {
+        F.offsets[F.nb] = sh_base[m];
+        *F.out_bits = sh_base[m];
     }
 }
 

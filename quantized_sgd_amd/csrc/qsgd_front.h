@@ -28,14 +28,13 @@ struct QsgdParams {
     // quantize outputs
     int32_t *levels;
     float *norms;
-    // encode outputs and workspace
-    uint64_t *out;
-    uint64_t *out_bits;
+    // encode outputs (bucket offsets are tile-relative after the first pass)
     uint64_t *offsets;
-    uint64_t *status;   // [ntiles] lookback words (flag:2 | value:62)
-    uint64_t *carry;    // [ntiles] partial last word of each tile, bit 0 = ready
-    uint32_t *ticket;   // work counter
-    uint32_t obuf_words;   // LDS words for the tile's output window
+    // encode workspace: each tile's bit string from bit 0 of its slot, and its
+    // length in bits
+    uint64_t *slots;       // [ntiles][obuf_words]
+    uint32_t *tile_bits;   // [ntiles]
+    uint32_t obuf_words;   // words of a tile's bit string bound (+1 spare)
 };
 
 // LDS carved out of the dynamic shared memory block for the front half.
