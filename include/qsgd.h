@@ -96,10 +96,11 @@ qsgd_status qsgd_quantize(const float *v, uint64_t n, uint32_t s, uint32_t d, ui
 
 /*
  * qsgd_encode: quantize and Elias-omega encode v into one bitstream (same page,
- * definition paragraph and claim on Elias coding), in a single pass over v.
- *   out                 [qsgd_encode_capacity_words(n, s, d)] uint64 output: the
- *                       stream in words [0, ceil(out_bits/64)); the words after it
- *                       are workspace and hold unspecified values afterwards.
+ * definition paragraph and claim on Elias coding), reading v once.
+ *   out                 [qsgd_encode_capacity_words(n, s, d)] uint64 output,
+ *                       16-byte aligned: the stream in words [0, ceil(out_bits/64));
+ *                       the words after it are workspace and hold unspecified
+ *                       values afterwards.
  *   out_bits            [1] uint64 output: stream length in bits.
  *   bucket_bit_offsets  [ceil(n/d) + 1] uint64 output: start bit of each bucket;
  *                       the last entry equals out_bits.

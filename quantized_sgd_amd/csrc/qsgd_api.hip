@@ -17,6 +17,9 @@ using namespace qsgd;
 
 namespace {
 
+constexpr uint32_t kMaxRuns = 4096;    // pass-1 workgroups at most (run totals in the workspace)
+constexpr uint32_t kFinishChunk = 4;   // tiles per pass-2 workgroup
+
 uint32_t host_omega_len(uint64_t N) {  // Elias omega codeword length
     uint32_t L = 1;
     while (N > 1) {
@@ -43,6 +46,7 @@ struct EncodePlan {
     uint64_t stream_words = 0;  // capacity reserved for the stream
     uint64_t ws_words = 0;      // workspace words after the stream
     uint32_t obuf_words = 0;    // words of a tile's bit string bound, + 1 (also its slot size)
+    uint64_t slot_region_words = 0;
     bool table = false;         // record codes from the LDS table (s <= kTabS)
     size_t lds_bytes = 0;
 };
@@ -61,8 +65,10 @@ EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool align
     // coordinates, plus one spare word (a two-word read at the string's end)
     const uint64_t tile_twice_bits = 64ull * p.K + (uint64_t)kTC * (5 + 2 * Ls);
     p.obuf_words = (uint32_t)((tile_twice_bits + 127) / 128 + 1);
-    // workspace: one slot per tile, then the tiles' lengths (uint32)
-    p.ws_words = p.ntiles * p.obuf_words + (p.ntiles + 1) / 2;
+    // workspace: one slot per tile, then the tiles' lengths (uint32, 16-byte
+    // aligned when out is)
+    p.slot_region_words = (p.ntiles * p.obuf_words + 1) & ~(uint64_t)1;
+    p.ws_words = p.slot_region_words + (p.ntiles + 1) / 2 + kMaxRuns;
     p.table = s <= kTabS;
     p.lds_bytes = EncodeLayout(p.obuf_words, p.table ? code_table_entries(s) : 0u, p.K).total;
     return p;
@@ -156,7 +162,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
         hipLaunchKernelGGL(encode_empty_kernel, dim3(1), dim3(64), 0, stream, out_bits, offsets);
         return launch_status();
     }
-    if (!v || !out) return QSGD_ERR_INVALID_ARG;
+    if (!v || !out || !aligned16(out)) return QSGD_ERR_INVALID_ARG;
     const bool ragged = bstart != nullptr;
     EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0));
     if (p.K == 0) return QSGD_ERR_UNSUPPORTED;
@@ -166,18 +172,25 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     P.K = p.K; P.ntiles = (uint32_t)p.ntiles;
     P.offsets = offsets;
     P.slots = out + p.stream_words;
-    P.tile_bits = reinterpret_cast<uint32_t *>(P.slots + p.ntiles * p.obuf_words);
+    P.tile_bits = reinterpret_cast<uint32_t *>(P.slots + p.slot_region_words);
+    P.run_bits = P.slots + p.slot_region_words + (p.ntiles + 1) / 2;
     P.obuf_words = p.obuf_words;
+    // pass 1 grid: at most the resident workgroups (and kMaxRuns), each taking a
+    // run of consecutive tiles
+    auto runs_for = [&](uint32_t resident) {
+        const uint64_t g = std::min<uint64_t>(std::min<uint64_t>(p.ntiles, resident), kMaxRuns);
+        P.run = (uint32_t)(p.ntiles / g);
+        P.rem = (uint32_t)(p.ntiles - (uint64_t)P.run * g);
+        return (uint32_t)g;
+    };
     // pass 1: every tile into its slot
     if (use_aligned(bstart, s, d)) {
         const size_t lds = aligned_encode_lds_bytes(p.obuf_words, s);
-        const uint32_t blocks =
-            (uint32_t)std::min<uint64_t>(p.ntiles, resident_blocks(encode_aligned_kernel, lds));
+        const uint32_t blocks = runs_for(resident_blocks(encode_aligned_kernel, lds));
         hipLaunchKernelGGL(encode_aligned_kernel, dim3(blocks), dim3(kWG), lds, stream, P, log2u(d));
     } else {
         auto launch = [&](auto kernel) {
-            const uint32_t blocks =
-                (uint32_t)std::min<uint64_t>(p.ntiles, resident_blocks(kernel, p.lds_bytes));
+            const uint32_t blocks = runs_for(resident_blocks(kernel, p.lds_bytes));
             hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), p.lds_bytes, stream, P);
         };
         if (ragged) {
@@ -190,13 +203,10 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     // pass 2: tile offsets, the stream words, absolute bucket offsets
     FinishParams F{};
     F.out = out; F.slots = P.slots; F.tile_bits = P.tile_bits; F.offsets = offsets;
+    F.run_bits = P.run_bits; F.run = P.run; F.rem = P.rem;
     F.out_bits = out_bits; F.nb = nb; F.ntiles = (uint32_t)p.ntiles; F.slot_words = p.obuf_words;
     F.K = p.K;
-    const uint32_t fblocks = (uint32_t)std::min<uint64_t>(p.ntiles, 1024);
-    F.chunk = (uint32_t)((p.ntiles + fblocks - 1) / fblocks);
-    if (F.chunk > (uint32_t)kFinishTiles) {
-        F.chunk = kFinishTiles;
-    }
+    F.chunk = kFinishChunk;
     const uint32_t fgrid = (uint32_t)((p.ntiles + F.chunk - 1) / F.chunk);
     hipLaunchKernelGGL(encode_finish_kernel, dim3(fgrid), dim3(kWG), 0, stream, F);
     return launch_status();

@@ -5,8 +5,8 @@
 // gaps and levels) and the claim on Elias coding (F = 32 bit norm).
 //
 // Encode pass 1, per tile (a run of whole buckets, <= 4096 coordinates, one
-// workgroup; persistent workgroups take tiles blockIdx.x, blockIdx.x + gridDim.x,
-// ..., so no workgroup ever waits for another):
+// workgroup; workgroup b takes the tiles [b run, (b + 1) run) in order, so no
+// workgroup ever waits for another, and publishes their total length):
 //   1. load v once from HBM, per-bucket norms, Philox rounding (qsgd_front.h);
 //   2. each thread looks up the code of every coordinate's record -- the 32-bit
 //      norm at a bucket start, and omega(gap) | sign | omega(k) per non-zero --
@@ -20,9 +20,9 @@
 //      from the tile's first bit; the words go to the tile's slot in the
 //      workspace, T to tile_bits, and the bucket offsets (tile-relative) to the
 //      offsets array.
-// Encode pass 2 (encode_finish_kernel): tile offsets by prefix sums of T, each
-// stream word gathered from the slots of the tiles it covers (every word
-// written once), bucket offsets made absolute.
+// Encode pass 2 (encode_finish_kernel): tile offsets by prefix sums of the run
+// totals and tile lengths, each stream word gathered from the slots of the
+// tiles it covers (every word written once), bucket offsets made absolute.
 #pragma once
 
 #include "qsgd_front.h"
@@ -196,7 +196,9 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
     // the wave index as a scalar, so that branches on it are uniform to the compiler
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
 
-    for (uint32_t tile = blockIdx.x; tile < P.ntiles; tile += gridDim.x) {
+    const uint32_t tend = run_first(blockIdx.x + 1, P.run, P.rem);
+    uint64_t run_total = 0;
+    for (uint32_t tile = run_first(blockIdx.x, P.run, P.rem); tile < tend; ++tile) {
         __syncthreads();  // separates this tile's LDS use from the previous one
         const Tile t = tile_geometry<RAGGED>(P, tile);
         fill_bucket_starts<RAGGED>(P, t, L.f);
@@ -298,7 +300,9 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
         uint64_t *slot = P.slots + (uint64_t)tile * P.obuf_words;
         for (uint32_t w = threadIdx.x; w < W; w += kWG) slot[w] = L.obuf[w];
         if (j == 0) P.tile_bits[tile] = T;
+        run_total += T;
     }
+    if (threadIdx.x == 0) P.run_bits[blockIdx.x] = run_total;
 }
 
 // Aligned fast path, front half. aligned_load: the thread's 16 coordinates
@@ -461,11 +465,13 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
     bool prev_bstart = false;
 
     // whole tiles are prefetched into pbuf; a partial tile is loaded directly
-    uint32_t cur = blockIdx.x;
-    bool pref = cur < P.ntiles && (uint64_t)cur * kTC + kTC <= P.n;
+    const uint32_t tend = run_first(blockIdx.x + 1, P.run, P.rem);
+    uint64_t run_total = 0;
+    uint32_t cur = run_first(blockIdx.x, P.run, P.rem);
+    bool pref = cur < tend && (uint64_t)cur * kTC + kTC <= P.n;
     if (pref) tile_prefetch_lds(P.v, (uint64_t)cur * kTC, pbuf, wave, lane);
 
-    for (; cur < P.ntiles; cur += gridDim.x) {
+    for (; cur < tend; ++cur) {
         const uint32_t tile = cur;
         const uint64_t g0 = (uint64_t)tile * kTC + (uint64_t)x0;
         float x[kCPT];
@@ -539,8 +545,8 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         } else {
             for (uint32_t w = threadIdx.x; w < P.obuf_words; w += kWG) obuf[w] = 0;
         }
-        const uint32_t nxt = cur + gridDim.x;
-        const bool pref_next = nxt < P.ntiles && (uint64_t)nxt * kTC + kTC <= P.n;
+        const uint32_t nxt = cur + 1;
+        const bool pref_next = nxt < tend && (uint64_t)nxt * kTC + kTC <= P.n;
         if (pref_next) tile_prefetch_lds(P.v, (uint64_t)nxt * kTC, pbuf, wave, lane);
         int mpre = INT_MIN;
 #pragma unroll
@@ -606,6 +612,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         }
         prev_tile = tile;
         prev_T = T;
+        run_total += T;
         prev_off = off;
         prev_bstart = bstart;
         pref = pref_next;
@@ -614,6 +621,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         __syncthreads();
         store_tile_slot(P, obuf, prev_tile, prev_T, prev_bstart, prev_off, log2d);
     }
+    if (threadIdx.x == 0) P.run_bits[blockIdx.x] = run_total;
 }
 
 // Encode pass 2. Workgroup w takes tiles [t0, t1) (a contiguous share): the
@@ -627,6 +635,8 @@ struct FinishParams {
     uint64_t *out;
     const uint64_t *slots;
     const uint32_t *tile_bits;
+    const uint64_t *run_bits;  // pass 1's run totals
+    uint32_t run, rem;         // pass 1's runs (run_first)
     uint64_t *offsets;
     uint64_t *out_bits;
     uint64_t nb;
@@ -660,9 +670,12 @@ __global__ __launch_bounds__(kWG) void encode_finish_kernel(FinishParams F) {
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
 
-    // stream offset of t0
+    // stream offset of t0: the totals of the pass-1 runs before t0's run, then
+    // the lengths of the tiles of that run before t0
+    const uint32_t r0 = run_of(t0, F.run, F.rem);
     uint64_t acc = 0;
-    for (uint32_t t = (uint32_t)j; t < t0; t += kWG) acc += F.tile_bits[t];
+    for (uint32_t i = (uint32_t)j; i < r0; i += kWG) acc += F.run_bits[i];
+    for (uint32_t t = run_first(r0, F.run, F.rem) + (uint32_t)j; t < t0; t += kWG) acc += F.tile_bits[t];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if (lane == 0) sh_red[wave] = acc;
@@ -680,34 +693,53 @@ __global__ __launch_bounds__(kWG) void encode_finish_kernel(FinishParams F) {
     if (j == 0) sh_base[m] = pre + total;  // end of the share
     __syncthreads();
 
-    // stream words whose first bit lies in each tile
-    for (uint32_t i = 0; i < m; ++i) {
-        const uint64_t b = sh_base[i], e = sh_base[i + 1];
-        const uint64_t w0 = (b + 63) >> 6, w1 = (e + 63) >> 6;
-        for (uint64_t w = w0 + (uint64_t)j; w < w1; w += kWG) {
-            uint32_t tt = t0 + i;
-            uint32_t rel = (uint32_t)((w << 6) - b);
-            uint32_t Tt = (uint32_t)(e - b);
-            uint64_t v = 0;
-            uint32_t have = 0;
-            while (true) {
-                const uint32_t avail = Tt - rel;
-                const uint32_t take = 64u - have < avail ? 64u - have : avail;
-                v |= slot_bits(F, tt, rel, take) >> have;
-                have += take;
-                if (have >= 64u) break;
-                ++tt;
-                if (tt >= F.ntiles) break;
-                rel = 0;
-                Tt = F.tile_bits[tt];
+    // every stream word whose first bit lies in this share's tiles, four per
+    // thread at a time with their slot loads issued together; a thread's words
+    // increase, so its tile index only moves forward
+    const uint64_t wbeg = (sh_base[0] + 63) >> 6, wend = (sh_base[m] + 63) >> 6;
+    uint32_t i = 0;
+    for (uint64_t wb = wbeg; wb < wend; wb += 4 * kWG) {
+        uint32_t tt[4], rel[4], Tt[4];
+        uint64_t a[4], b[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint64_t w = wb + (uint64_t)j + (uint64_t)k * kWG;
+            const uint64_t g = (w < wend ? w : wend - 1) << 6;
+            while (sh_base[i + 1] <= g) ++i;
+            tt[k] = t0 + i;
+            rel[k] = (uint32_t)(g - sh_base[i]);
+            Tt[k] = (uint32_t)(sh_base[i + 1] - sh_base[i]);
+            const uint64_t *s = F.slots + (uint64_t)tt[k] * F.slot_words + (rel[k] >> 6);
+            a[k] = s[0];
+            b[k] = s[1];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint64_t w = wb + (uint64_t)j + (uint64_t)k * kWG;
+            if (w >= wend) break;
+            const uint32_t sh = rel[k] & 63u;
+            uint64_t v = a[k] << sh;
+            if (sh) v |= b[k] >> (64u - sh);
+            if (Tt[k] - rel[k] < 64u) {
+                // the word runs past its tile: the rest from the next tiles
+                uint32_t have = Tt[k] - rel[k];
+                v &= ~(~0ull >> have);
+                uint32_t t2 = tt[k];
+                while (have < 64u && ++t2 < F.ntiles) {
+                    const uint32_t T2 = t2 < t1 ? (uint32_t)(sh_base[t2 - t0 + 1] - sh_base[t2 - t0])
+                                                : F.tile_bits[t2];
+                    const uint32_t take = 64u - have < T2 ? 64u - have : T2;
+                    v |= slot_bits(F, t2, 0u, take) >> have;
+                    have += take;
+                }
             }
             F.out[w] = v;
         }
-        // bucket offsets of this tile
-        const uint64_t b0 = (uint64_t)(t0 + i) * F.K;
-        const uint64_t b1 = b0 + F.K < F.nb ? b0 + F.K : F.nb;
-        for (uint64_t bb = b0 + (uint64_t)j; bb < b1; bb += kWG) F.offsets[bb] += b;
     }
+    // bucket offsets of this share's tiles
+    const uint64_t bb0 = (uint64_t)t0 * F.K;
+    const uint64_t bb1 = (uint64_t)t1 * F.K < F.nb ? (uint64_t)t1 * F.K : F.nb;
+    for (uint64_t b = bb0 + (uint64_t)j; b < bb1; b += kWG) F.offsets[b] += sh_base[(b - bb0) / F.K];
     if (t1 == F.ntiles && j == 0) {
         F.offsets[F.nb] = sh_base[m];
         *F.out_bits = sh_base[m];

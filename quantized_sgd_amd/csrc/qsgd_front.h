@@ -34,8 +34,22 @@ struct QsgdParams {
     // length in bits
     uint64_t *slots;       // [ntiles][obuf_words]
     uint32_t *tile_bits;   // [ntiles]
+    uint64_t *run_bits;    // [gridDim.x] total bits of each workgroup's run of tiles
     uint32_t obuf_words;   // words of a tile's bit string bound (+1 spare)
+    uint32_t run, rem;     // workgroup b takes run_first(b) .. run_first(b + 1) - 1
 };
+
+// Runs of consecutive tiles: the first `rem` workgroups take run + 1 tiles, the
+// others run tiles.
+__host__ __device__ __forceinline__ uint32_t run_first(uint32_t b, uint32_t run, uint32_t rem) {
+    return b * run + (b < rem ? b : rem);
+}
+
+// The run that holds tile t.
+__host__ __device__ __forceinline__ uint32_t run_of(uint32_t t, uint32_t run, uint32_t rem) {
+    const uint32_t big = (run + 1) * rem;
+    return t < big ? t / (run + 1) : rem + (t - big) / run;
+}
 
 // LDS carved out of the dynamic shared memory block for the front half.
 struct FrontLds {

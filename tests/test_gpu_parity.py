@@ -137,6 +137,10 @@ def test_invalid_arguments():
         q.quantize(v, (1 << 24) + 1, 16, 1)
     with pytest.raises(q.QsgdError):
         q.quantize(v[1:], 4, 16, 1)  # misaligned
+    cap = q.encode_capacity_words(64, 4, 16)
+    out = torch.empty(cap + 1, dtype=torch.int64, device="cuda")
+    with pytest.raises(q.QsgdError):
+        q.encode(v, 4, 16, 1, out=out[1:])  # out misaligned
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 5])
