@@ -7,9 +7,9 @@ Several copies of the input and output buffers are rotated so that no step
 finds its input in the 256 MB Infinity Cache.
 
 Prints one JSON line: value = whole-job round-trip throughput 4n bytes of fp32
-gradient / (encode + decode time) in GB/s, plus per-direction rates, the
-roofline object of the dominant kernel and the oracle's CPU rate on a bounded
-sample.
+gradient / (encode + decode time) in GB/s, plus per-direction rates and HBM
+fractions, bits per coordinate, the roofline object of the dominant kernel and
+the oracle's CPU rate on a bounded sample.
 """
 from __future__ import annotations
 
@@ -182,7 +182,7 @@ def main():
     dominant = "encode" if enc_avg >= dec_avg else "decode"
     ach = enc_gbps if dominant == "encode" else dec_gbps
     res = {
-        "metric": "QSGD encode+decode round-trip GB/s of fp32 gradient on 1 MI355X",
+        "metric": "QSGD encode/decode GB/s of fp32 gradient on 1 MI355X; % HBM peak; bits/coord",
         "value": round(gbytes / ((enc_avg + dec_avg) * 1e-3), 3),
         "unit": "GB/s",
         "n_gpus": 1,
