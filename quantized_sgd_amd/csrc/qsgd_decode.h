@@ -46,6 +46,7 @@ constexpr int kDecWG = 64 * kDecWaves;
 constexpr int kStageWords = 320;    // 64-bit stream words staged per wave
 constexpr int kStagePad = 4;        // zero words after the staged stream
 constexpr int kGroupCoords = 4096;  // coordinates of a group whose levels are staged in LDS
+constexpr uint32_t kLevelSpare = kGroupCoords + 16;  // level byte for out-of-range writes
 
 struct DecodeParams {
     const uint64_t *in;
@@ -263,33 +264,36 @@ __device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const RecordCt
 __device__ __forceinline__ uint32_t bitlen32(uint32_t x) { return 32u - (uint32_t)__clz(x); }
 
 // Slots of a lane's gap-prefix table (bytes, in the wave's level buffer while
-// the chains are being synchronised).
-constexpr uint32_t kCumSlots = 48;
+// the chains are being synchronised); positions past the table are not looked up.
+constexpr uint32_t kCumSlots = 64;
 
 // Phase A: follows a chain from `start` to its first position >= sn and returns
 // that position (the exit), with the gap sum of the records passed. MARK: sets
 // bit (p - start) of own0:own1 for each chain position p in [start, start + 128)
-// and stores in cum[i] the gap sum before the i-th of them (saturated at 255;
-// the last slot collects the positions past kCumSlots - 2). Two-record table
-// entries advance two records at once when the second starts before sn.
+// and stores in cum[i] the low byte of the gap sum before the i-th of them
+// (i < kCumSlots - 1; cum_top: the gap sum after the last noted position, so a
+// table entry is exact when cum_top < 256). Two-record table entries advance
+// two records at once when the second starts before the current limit (the
+// end of the 64-bit mark word being filled, or sn).
 template <bool LDS, bool MARK>
 __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const RecordCtx &x, uint32_t start,
                                                  uint32_t sn, uint32_t &ga, uint64_t &own0,
-                                                 uint64_t &own1, uint8_t *cum) {
+                                                 uint64_t &own1, uint8_t *cum, uint32_t &cum_top) {
     uint32_t p = start, sum = 0;
     if (MARK) {
         uint32_t i = 0;
-        // one step from p: returns the step's chain positions relative to p
-        auto step = [&]() -> uint64_t {
+        // one step from p below lim: returns the step's chain positions
+        // relative to p (bit 0, and bit len1 for a second record)
+        auto step = [&](uint32_t lim) -> uint32_t {
             const uint32_t e = lut_at(r, x, p);
-            cum[i] = (uint8_t)(sum < 255u ? sum : 255u);
-            uint64_t m = 1ull;
+            cum[i] = (uint8_t)sum;
+            uint32_t m = 1u;
             if (e & 15u) {
                 const uint32_t len1 = (e >> 4) & 15u;
                 const uint32_t s1 = sum + ((e >> 8) & 15u) + 1u;
-                const bool two = len1 < (e & 15u) && p + len1 < sn;
-                cum[i + 1u < kCumSlots ? i + 1u : kCumSlots - 1u] = (uint8_t)(s1 < 255u ? s1 : 255u);
-                m |= (uint64_t)two << len1;
+                const bool two = len1 < (e & 15u) && p + len1 < lim;
+                cum[i + 1u] = (uint8_t)s1;
+                m = ((uint32_t)two << len1) | 1u;
                 sum = two ? s1 + ((e >> 20) & 15u) + 1u : s1;
                 p += two ? (e & 15u) : len1;
                 i += two ? 2u : 1u;
@@ -297,21 +301,20 @@ __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const Recor
                 chain_step(r, x, p, sum);
                 i += 1u;
             }
-            i = i < kCumSlots ? i : kCumSlots - 1u;
+            i = i < kCumSlots - 2u ? i : kCumSlots - 2u;
             return m;
         };
         const uint32_t l1 = sn < start + 64u ? sn : start + 64u;
         while (p < l1) {
             const uint32_t rel = p - start;
-            const uint64_t m = step();
-            own0 |= m << rel;
-            own1 |= (m >> 1) >> (63u - rel);  // a second position past 64
+            own0 |= (uint64_t)step(l1) << rel;
         }
         const uint32_t l2 = sn < start + 128u ? sn : start + 128u;
         while (p < l2) {
             const uint32_t rel = p - start - 64u;
-            own1 |= step() << rel;  // positions past 128 are not noted
+            own1 |= (uint64_t)step(l2) << rel;
         }
+        cum_top = sum;
     }
     while (p < sn) {
         const uint32_t e = lut_at(r, x, p);
@@ -330,19 +333,19 @@ __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const Recor
 
 // Gap sum of a lane's speculative chain before its position y, from the table
 // follow_chain<MARK> filled; false if the table cannot tell (y not a noted
-// position, past the table, or a saturated entry).
-__device__ __forceinline__ bool cum_lookup(const uint8_t *cum, uint64_t own0, uint64_t own1,
-                                           uint32_t rel, uint32_t &g) {
-    if (rel >= 128u) return false;
+// position, past the table, or sums past a byte).
+__device__ __forceinline__ bool cum_lookup(const uint8_t *cum, uint32_t cum_top, uint64_t own0,
+                                           uint64_t own1, uint32_t rel, uint32_t &g) {
+    if (rel >= 128u || cum_top > 255u) return false;
     const uint64_t m = rel < 64u ? own0 : own1;
     if (((m >> (rel & 63u)) & 1u) == 0) return false;
     const uint32_t i = rel < 64u
                            ? (uint32_t)__popcll(own0 & ((1ull << rel) - 1ull))
                            : (uint32_t)__popcll(own0) +
                                  (uint32_t)__popcll(own1 & ((1ull << (rel - 64u)) - 1ull));
-    if (i >= kCumSlots - 1u) return false;
+    if (i >= kCumSlots - 2u) return false;
     g = cum[i];
-    return g < 255u;
+    return true;
 }
 
 // Phase B: continues the chain from its exit x0 (>= sn) until it lands on a
@@ -451,16 +454,11 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// LDS slot of level byte i of a group: one spare dword after every 16, so the
-// lanes of a team, which write at about 64-byte strides, hit different banks,
-// while the conversion pass still reads consecutive dwords (dword q of the
-// levels sits at q + q / 16).
-__device__ __forceinline__ uint32_t level_slot(uint32_t i) { return i + ((i >> 6) << 2); }
 
 // Decodes the buckets [b0, b1) of one wave group; `r` reads the group's stream,
 // bit 0 being stream bit `gbit`. LDS_OUT: each record's level byte (sign << 7 |
 // k) goes to the group's LDS buffer `lvl` (index = coordinate - lbase, cleared
-// by the caller, slot level_slot(index)) and each bucket's RN64(norm / s) to
+// by the caller) and each bucket's RN64(norm / s) to
 // ebs[team]; otherwise every
 // lane writes its own output range with a QuadWriter.
 template <bool RAGGED, bool LDS_IN, bool LDS_OUT>
@@ -509,7 +507,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
     uint32_t cx = E, ga = 0, gb = 0, ynext = E;
     bool found = false;
     uint8_t *cum = lvl + (uint32_t)lane * kCumSlots;
-    if (act) cx = follow_chain<LDS_IN, true>(r, x, sq, sn, ga, own0, own1, cum);
+    uint32_t cum_top = 0;
+    if (act) cx = follow_chain<LDS_IN, true>(r, x, sq, sn, ga, own0, own1, cum, cum_top);
     if (act && last) found = true;
     // phase B against the next lane's window
     const uint64_t nxt0 = __shfl_down(own0, 1, (int)T);
@@ -539,7 +538,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
         }
         if (fix) {
             uint64_t d0 = 0, d1 = 0;
-            cx = follow_chain<LDS_IN, false>(r, x, px, sn, ga, d0, d1, nullptr);
+            uint32_t dtop = 0;
+            cx = follow_chain<LDS_IN, false>(r, x, px, sn, ga, d0, d1, nullptr, dtop);
             if (last) {
                 found = true;
                 ynext = E;
@@ -563,7 +563,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
     // gaps of the records before the sync point: from the phase A table, else
     // by following the same speculative chain again
     uint32_t gpre = 0;
-    if (act && q >= 1 && !repaired && !cum_lookup(cum, own0, own1, ystart - sq, gpre)) {
+    if (act && q >= 1 && !repaired && !cum_lookup(cum, cum_top, own0, own1, ystart - sq, gpre)) {
         gpre = 0;
         uint32_t p = sq;
         while (p < ystart) chain_step(r, x, p, gpre);
@@ -584,7 +584,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
         for (uint32_t i = (uint32_t)lane; i < nclear16; i += 64) l4[i] = make_uint4(0u, 0u, 0u, 0u);
         wave_sync();
         if (act) {
-            // t: the coordinate's index in the group's level bytes
+            // tix: the record's index in the group's level bytes; indices past the
+            // bucket (only in a malformed stream) go to a spare byte
             uint32_t tix = (uint32_t)(c0 - lbase) + basej - 1u;
             const uint32_t tend = (uint32_t)(c0 - lbase) + (uint32_t)len;
             uint32_t p = ystart;
@@ -593,23 +594,18 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
                 if (e & 15u) {
                     const uint32_t len1 = (e >> 4) & 15u;
                     tix += ((e >> 8) & 15u) + 1u;
-                    if (tix >= tend) break;
-                    lvl[level_slot(tix)] = (uint8_t)(e >> 12);
-                    if (len1 < (e & 15u) && p + len1 < ynext) {
-                        tix += ((e >> 20) & 15u) + 1u;
-                        if (tix >= tend) break;
-                        lvl[level_slot(tix)] = (uint8_t)(e >> 24);
-                        p += e & 15u;
-                    } else {
-                        p += len1;
-                    }
+                    lvl[tix < tend ? tix : kLevelSpare] = (uint8_t)(e >> 12);
+                    const bool two = len1 < (e & 15u) && p + len1 < ynext;
+                    const uint32_t t2 = tix + ((e >> 20) & 15u) + 1u;
+                    lvl[two && t2 < tend ? t2 : kLevelSpare] = (uint8_t)(e >> 24);
+                    tix = two ? t2 : tix;
+                    p += two ? (e & 15u) : len1;
                 } else {
                     uint32_t gap, neg, k;
                     const uint32_t nq = record_slow(r, x, p, gap, neg, k);
                     if (!nq) break;
                     tix += gap;
-                    if (tix >= tend) break;
-                    lvl[level_slot(tix)] = (uint8_t)((neg << 7) | k);
+                    lvl[tix < tend ? tix : kLevelSpare] = (uint8_t)((neg << 7) | k);
                     p = nq;
                 }
             }
@@ -657,8 +653,7 @@ __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t
         const uint64_t qa = A >> 2, qb = (B + 3) >> 2;
         for (uint64_t qd = qa + lane; qd < qb; qd += 64) {
             const uint64_t a = qd << 2;
-            const uint32_t dq = (uint32_t)((a - lbase) >> 2);
-            const uint32_t word = lw[dq + (dq >> 4)];
+            const uint32_t word = lw[(a - lbase) >> 2];
             float v[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -678,11 +673,11 @@ __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t
     }
 }
 
-// Dynamic LDS: per wave the staged stream words, the group's level bytes (in
-// level_slot order) and the per-bucket dequantization factors; then the record
+// Dynamic LDS: per wave the staged stream words, the group's level bytes and
+// the per-bucket dequantization factors; then the record
 // table.
 constexpr size_t kStageBytes = (size_t)(kStageWords + kStagePad) * 8;
-constexpr size_t kLevelBytes = ((size_t)kGroupCoords + 16 + ((kGroupCoords + 16) >> 4) + 15) & ~(size_t)15;
+constexpr size_t kLevelBytes = (size_t)kGroupCoords + 32;
 constexpr size_t kWaveLdsBytes = kStageBytes + kLevelBytes + 64 * 8;
 static_assert(kStageBytes % 16 == 0 && kLevelBytes % 16 == 0, "LDS carve-out alignment");
 
@@ -731,7 +726,7 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
         }
         const uint64_t lbase = bucket_first<RAGGED>(D, b0) & ~(uint64_t)3;
         const uint32_t span = D.lds_out ? (uint32_t)(bucket_first<RAGGED>(D, b1) - lbase) : 0u;
-        const uint32_t nclear16 = (level_slot(span + 3) + 15) >> 4;
+        const uint32_t nclear16 = (span + 3 + 15) >> 4;
         // staged words are read by other lanes of this wave
         wave_sync();
         // LDS positions are LDS bit addresses: the group's bit 0 is the first bit of stage
