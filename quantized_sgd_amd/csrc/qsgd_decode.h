@@ -641,35 +641,39 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
 
 // Writes the group's buckets from the LDS level bytes: RN32(k * RN64(norm / s))
 // with the byte's sign (+0.0f for k = 0), 16-byte stores for whole aligned
-// quads of a bucket, single floats for quads that a bucket boundary cuts.
+// quads of a bucket, single floats for quads that a bucket boundary cuts. The
+// value of each of the 256 level bytes is tabulated per bucket in `tbl` first.
 template <bool RAGGED>
 __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t *lvl, const double *ebs,
-                                            uint64_t lbase, uint64_t b0, uint64_t b1) {
+                                            float *tbl, uint64_t lbase, uint64_t b0, uint64_t b1) {
     const uint32_t lane = (uint32_t)lane_id();
     const uint32_t *lw = reinterpret_cast<const uint32_t *>(lvl);
     for (uint64_t b = b0; b < b1; ++b) {
         const uint64_t A = bucket_first<RAGGED>(D, b), B = bucket_first<RAGGED>(D, b + 1);
         const double e = ebs[b - b0];
+#pragma unroll
+        for (uint32_t t = lane; t < 256u; t += 64u) {
+            const float m = (float)((double)(t & 127u) * e);
+            tbl[t] = __uint_as_float(__float_as_uint(m) | ((t & 128u) << 24));
+        }
+        wave_sync();
         const uint64_t qa = A >> 2, qb = (B + 3) >> 2;
         for (uint64_t qd = qa + lane; qd < qb; qd += 64) {
             const uint64_t a = qd << 2;
             const uint32_t word = lw[(a - lbase) >> 2];
-            float v[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint32_t byte = (word >> (8 * t)) & 0xffu;
-                const float m = (float)((double)(byte & 127u) * e);
-                v[t] = __uint_as_float(__float_as_uint(m) | ((byte & 128u) << 24));
-            }
+            const float v0 = tbl[word & 0xffu], v1 = tbl[(word >> 8) & 0xffu];
+            const float v2 = tbl[(word >> 16) & 0xffu], v3 = tbl[word >> 24];
             if (a >= A && a + 4 <= B) {
-                *reinterpret_cast<float4 *>(D.v_hat + a) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4 *>(D.v_hat + a) = make_float4(v0, v1, v2, v3);
             } else {
-                if (a >= A && a < B) D.v_hat[a] = v[0];
-                if (a + 1 >= A && a + 1 < B) D.v_hat[a + 1] = v[1];
-                if (a + 2 >= A && a + 2 < B) D.v_hat[a + 2] = v[2];
-                if (a + 3 >= A && a + 3 < B) D.v_hat[a + 3] = v[3];
+                if (a >= A && a < B) D.v_hat[a] = v0;
+                if (a + 1 >= A && a + 1 < B) D.v_hat[a + 1] = v1;
+                if (a + 2 >= A && a + 2 < B) D.v_hat[a + 2] = v2;
+                if (a + 3 >= A && a + 3 < B) D.v_hat[a + 3] = v3;
             }
         }
+        // the table is rebuilt for the next bucket
+        wave_sync();
     }
 }
 
@@ -680,6 +684,9 @@ constexpr size_t kStageBytes = (size_t)(kStageWords + kStagePad) * 8;
 constexpr size_t kLevelBytes = (size_t)kGroupCoords + 32;
 constexpr size_t kWaveLdsBytes = kStageBytes + kLevelBytes + 64 * 8;
 static_assert(kStageBytes % 16 == 0 && kLevelBytes % 16 == 0, "LDS carve-out alignment");
+static_assert(kStageBytes >= 256 * sizeof(float), "the value table reuses the stage");
+// two workgroups per CU (160 KB of LDS)
+static_assert(2 * ((size_t)kDecWaves * kWaveLdsBytes + 16384) <= 160 * 1024, "decode LDS budget");
 
 constexpr size_t decode_lds_bytes() { return (size_t)kDecWaves * kWaveLdsBytes + sizeof(RecordLut); }
 
@@ -738,7 +745,7 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
             if (in_lds) decode_group<RAGGED, true, true>(D, lut, rl, lgbit, b0, b1, lvl, ebs, lbase, nclear16);
             else decode_group<RAGGED, false, true>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
             wave_sync();
-            store_group<RAGGED>(D, lvl, ebs, lbase, b0, b1);
+            store_group<RAGGED>(D, lvl, ebs, reinterpret_cast<float *>(stage), lbase, b0, b1);
         } else {
             if (in_lds) decode_group<RAGGED, true, false>(D, lut, rl, lgbit, b0, b1, lvl, ebs, lbase, nclear16);
             else decode_group<RAGGED, false, false>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
