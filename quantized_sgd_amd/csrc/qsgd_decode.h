@@ -267,6 +267,35 @@ __device__ __forceinline__ uint32_t bitlen32(uint32_t x) { return 32u - (uint32_
 // the chains are being synchronised); positions past the table are not looked up.
 constexpr uint32_t kCumSlots = 64;
 
+// Steps at the start of a guessed chain that skip a bit at a table miss.
+#ifndef QSGD_GUESS_STEPS
+#define QSGD_GUESS_STEPS 6
+#endif
+constexpr int kGuessSteps = QSGD_GUESS_STEPS;
+
+// The first steps of a chain whose start is only a guess at a record boundary.
+// Such a start lands on bits that are not a record start as often as not, and
+// those often miss the table; so for kGuessSteps steps a table miss moves one
+// bit on instead of decoding a long record. follow_chain notes no position
+// during these steps, so another chain can only meet this one where it follows
+// the exact rule, and both continue alike from there.
+template <bool LDS>
+__device__ __forceinline__ void guess_steps(const Bits<LDS> &r, const RecordCtx &x, uint32_t &p,
+                                            uint32_t sn, uint32_t &sum) {
+#pragma unroll
+    for (int i = 0; i < kGuessSteps; ++i) {
+        const uint32_t e = lut_at(r, x, p);
+        const uint32_t len1 = (e >> 4) & 15u;
+        const bool two = len1 < (e & 15u) && p + len1 < sn;
+        const uint32_t adv = (e & 15u) == 0 ? 1u : two ? (e & 15u) : len1;
+        const uint32_t g =
+            (e & 15u) == 0 ? 0u : ((e >> 8) & 15u) + 1u + (two ? ((e >> 20) & 15u) + 1u : 0u);
+        const bool go = p < sn;
+        sum += go ? g : 0u;
+        p += go ? adv : 0u;
+    }
+}
+
 // Phase A: follows a chain from `start` to its first position >= sn and returns
 // that position (the exit), with the gap sum of the records passed. MARK: sets
 // bit (p - start) of own0:own1 for each chain position p in [start, start + 128)
@@ -278,8 +307,10 @@ constexpr uint32_t kCumSlots = 64;
 template <bool LDS, bool MARK>
 __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const RecordCtx &x, uint32_t start,
                                                  uint32_t sn, uint32_t &ga, uint64_t &own0,
-                                                 uint64_t &own1, uint8_t *cum, uint32_t &cum_top) {
+                                                 uint64_t &own1, uint8_t *cum, uint32_t &cum_top,
+                                                 bool guess = false) {
     uint32_t p = start, sum = 0;
+    if (MARK && guess) guess_steps(r, x, p, sn, sum);
     if (MARK) {
         uint32_t i = 0;
         // one step from p below lim: returns the step's chain positions
@@ -508,7 +539,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
     bool found = false;
     uint8_t *cum = lvl + (uint32_t)lane * kCumSlots;
     uint32_t cum_top = 0;
-    if (act) cx = follow_chain<LDS_IN, true>(r, x, sq, sn, ga, own0, own1, cum, cum_top);
+    if (act) cx = follow_chain<LDS_IN, true>(r, x, sq, sn, ga, own0, own1, cum, cum_top, q != 0);
     if (act && last) found = true;
     // phase B against the next lane's window
     const uint64_t nxt0 = __shfl_down(own0, 1, (int)T);
@@ -566,6 +597,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
     if (act && q >= 1 && !repaired && !cum_lookup(cum, cum_top, own0, own1, ystart - sq, gpre)) {
         gpre = 0;
         uint32_t p = sq;
+        guess_steps(r, x, p, sn, gpre);
         while (p < ystart) chain_step(r, x, p, gpre);
     }
     const uint32_t G = act ? ga + gb - gpre : 0u;
