@@ -265,7 +265,8 @@ __device__ __forceinline__ uint32_t bitlen32(uint32_t x) { return 32u - (uint32_
 
 // Slots of a lane's gap-prefix table (bytes, in the wave's level buffer while
 // the chains are being synchronised); positions past the table are not looked up.
-constexpr uint32_t kCumSlots = 64;
+// An odd count keeps the lanes' tables in different LDS banks.
+constexpr uint32_t kCumSlots = 63;
 
 // Steps at the start of a guessed chain that skip a bit at a table miss.
 #ifndef QSGD_GUESS_STEPS
