@@ -53,10 +53,11 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
 __device__ __forceinline__ uint32_t qlevel(float v, double c, uint32_t w) {
     const float a = fabsf(v);
     const float r = (float)((double)a * c);
-    const float l = floorf(r);
-    const float p = r - l;
+    // r >= 0: truncation is the floor, and fract gives r - floor(r) exactly
+    const uint32_t l = (uint32_t)r;
+    const float p = __builtin_amdgcn_fractf(r);
     const float u = (float)(w >> 8) * 0x1p-24f;
-    return (uint32_t)l + (u < p ? 1u : 0u);
+    return l + (u < p ? 1u : 0u);
 }
 
 // Elias omega codeword of N >= 1 (Elias 1975), right-aligned: a final 0 bit, and

@@ -494,9 +494,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         const bool bstart = first_of_bucket && g0 < P.n;
 
         // ---- levels and record codes; records packed right-aligned into two
-        // 64-bit registers (coordinates 0-7 and 8-15); levels kept as bytes
-        // sign << 7 | k for the rare half longer than 64 bits ----
-        uint32_t lvb[kCPT / 4] = {0, 0, 0, 0};
+        // 64-bit registers (coordinates 0-7 and 8-15) ----
         uint64_t racc[2] = {0, 0};
         uint32_t rlen[2] = {0, 0};
         int prev = x0 - 1;
@@ -520,7 +518,6 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
                 const uint32_t neg = __float_as_uint(x[q]) >> 31;
                 const uint32_t gg = have ? (uint32_t)(xi - prev) : 0u;
                 const uint32_t ent = rt[code_index(gg, k, neg)];
-                lvb[g] |= ((neg << 7) | k) << (8 * e);
                 const uint32_t len = ent & 31u;
                 racc[q >> 3] = (racc[q >> 3] << len) | (uint64_t)(ent >> 5);
                 rlen[q >> 3] += len;
@@ -588,19 +585,23 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
                 if (rlen[h]) or_bits(obuf, p, racc[h] << (64u - rlen[h]), rlen[h]);
                 p += rlen[h];
             } else {
-                // more than 64 bits in this half: its records one at a time,
-                // the gaps followed from the thread's first coordinate
+                // more than 64 bits in this half (rare): its records one at a
+                // time, the levels drawn again from v and the gaps followed from
+                // the thread's first coordinate
                 int pv = x0 - 1;
                 bool hv = bstart;
 #pragma unroll 1
                 for (int q = 0; q < 8 * h + 8; ++q) {
-                    const uint32_t wv = lvb[0] * (q < 4) + lvb[1] * (q >= 4 && q < 8) +
-                                        lvb[2] * (q >= 8 && q < 12) + lvb[3] * (q >= 12);
-                    const uint32_t b8 = (wv >> (8 * (q & 3))) & 255u;
-                    const uint32_t k = b8 & 127u;
+                    const uint64_t gi = g0 + (uint64_t)q;
+                    uint32_t w[4];
+                    uint32_t k0 = key0, k1 = key1;
+                    asm volatile("" : "+s"(k0), "+s"(k1));
+                    philox4x32_10((uint32_t)(gi >> 2), (uint32_t)(gi >> 34), k0, k1, w);
+                    const float xv = gi < P.n ? P.v[gi] : 0.0f;
+                    const uint32_t k = qlevel(xv, cb, w[q & 3]);
                     if (q >= 8 * h) {
                         const uint32_t gg = hv ? (uint32_t)(x0 + q - pv) : 0u;
-                        const uint32_t ent = rt[code_index(gg, k, b8 >> 7)];
+                        const uint32_t ent = rt[code_index(gg, k, __float_as_uint(xv) >> 31)];
                         const uint32_t len = ent & 31u;
                         if (len) or_bits(obuf, p, (uint64_t)(ent >> 5) << (64u - len), len);
                         p += len;

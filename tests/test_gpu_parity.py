@@ -52,6 +52,15 @@ def test_mixed_edge_values(n, d, s, seed):
     check_parity(v, s, d, seed)
 
 
+@pytest.mark.parametrize("n,d,s,seed", [(4096 + 37, 16, 64, 41), (20000, 64, 64, 42), (3000, 32, 50, 43)])
+def test_long_records_per_thread(n, d, s, seed):
+    # near-constant magnitudes put the levels near s / sqrt(d): records of 9-15
+    # bits, so the records of 8 consecutive coordinates pass 64 bits
+    rng = np.random.default_rng(seed)
+    v = (rng.choice([-1.0, 1.0], n) * (1.0 + 0.01 * rng.standard_normal(n))).astype(np.float32)
+    check_parity(v, s, d, seed)
+
+
 def test_zero_buckets_and_spikes():
     n, d = 40000, 512
     v = np.zeros(n, np.float32)
