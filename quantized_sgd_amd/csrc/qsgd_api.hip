@@ -18,7 +18,7 @@ using namespace qsgd;
 namespace {
 
 constexpr uint32_t kMaxRuns = 4096;    // pass-1 workgroups at most (run totals in the workspace)
-constexpr uint32_t kFinishChunk = 4;   // tiles per pass-2 workgroup
+constexpr uint32_t kFinishChunk = 8;   // tiles per pass-2 workgroup
 
 uint32_t host_omega_len(uint64_t N) {  // Elias omega codeword length
     uint32_t L = 1;
