@@ -123,6 +123,40 @@ qsgd_status qsgd_encode(const float *v, uint64_t n, uint32_t s, uint32_t d, uint
 qsgd_status qsgd_decode(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
                         uint32_t s, uint32_t d, float *v_hat, hipStream_t stream);
 
+/* ---- decode-accumulate: the receiving side of a gradient exchange ----------
+ * In data-parallel SGD every node sends its quantized gradient and each
+ * receiver sums the gradients it gets (page "QSGD: Communication-Efficient SGD
+ * via Gradient Quantization and Encoding", abstract: nodes communicate
+ * quantized gradient updates; page "QSGD (Quantized Stochastic Gradient Descent)
+ * with Elias Coding", claim on multi-GPU bucketed training). The pages do not
+ * fix how the sum is formed; this library's reading: for every coordinate i,
+ *     acc_i <- (((acc_i + v_hat_0,i) + v_hat_1,i) + ... + v_hat_{k-1},i)
+ * in fp32 (round to nearest even, one rounding per addition), in stream order,
+ * where v_hat_j is what qsgd_decode returns for stream j (its +0.0f zeros
+ * included, so an acc_i of -0.0f becomes +0.0f). Zero acc first for the plain sum.
+ */
+
+/* Largest number of streams one decode-accumulate call takes (32). */
+uint32_t qsgd_max_streams(void);
+
+/*
+ * qsgd_decode_accumulate: adds the decodes of k streams to acc in one pass over
+ * acc (each workgroup decodes all k streams of a group of buckets in turn).
+ *   in                  HOST array of k DEVICE pointers: stream words of each
+ *                       stream, written by qsgd_encode with the same n, s, d.
+ *   bucket_bit_offsets  HOST array of k DEVICE pointers: each stream's
+ *                       [ceil(n/d) + 1] bucket offsets.
+ *   k                   number of streams, 0..qsgd_max_streams() (0: nothing is
+ *                       enqueued); more is QSGD_ERR_INVALID_ARG, as is a NULL
+ *                       array or entry.
+ *   acc                 [n] fp32 input and output, 16-byte aligned; must not
+ *                       overlap any stream or offset table.
+ * The pointer arrays are read during the call only.
+ */
+qsgd_status qsgd_decode_accumulate(const uint64_t *const *in, const uint64_t *const *bucket_bit_offsets,
+                                   uint32_t k, uint64_t n, uint32_t s, uint32_t d, float *acc,
+                                   hipStream_t stream);
+
 /* ---- ragged batches: several tensors in one flat buffer --------------------
  * Buckets restart at every tensor boundary (per-tensor quantization); the
  * Philox index of a coordinate is its flat index in the concatenation. The
@@ -155,6 +189,10 @@ qsgd_status qsgd_encode_ragged(const float *v, uint64_t n, const uint64_t *bucke
 qsgd_status qsgd_decode_ragged(const uint64_t *in, const uint64_t *bucket_bit_offsets,
                                uint64_t n, const uint64_t *bucket_start, uint64_t nb,
                                uint32_t s, uint32_t d, float *v_hat, hipStream_t stream);
+qsgd_status qsgd_decode_accumulate_ragged(const uint64_t *const *in,
+                                          const uint64_t *const *bucket_bit_offsets, uint32_t k,
+                                          uint64_t n, const uint64_t *bucket_start, uint64_t nb,
+                                          uint32_t s, uint32_t d, float *acc, hipStream_t stream);
 
 #ifdef __cplusplus
 }

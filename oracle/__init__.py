@@ -77,6 +77,9 @@ def lib():
         L.or_decode.argtypes = [_u64p, ctypes.c_uint64, _u64p, _u64p, ctypes.c_uint64,
                                 ctypes.c_uint32, _f32p]
         L.or_decode.restype = ctypes.c_int
+        L.or_decode_accumulate.argtypes = [ctypes.c_void_p, _u64p, ctypes.c_void_p, ctypes.c_uint64,
+                                           _u64p, ctypes.c_uint64, ctypes.c_uint32, _f32p, _f32p]
+        L.or_decode_accumulate.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -218,6 +221,27 @@ def decode(words, offsets, bstart, s: int):
     rc = lib().or_decode(_p(words, _u64p), nwords, _p(offsets, _u64p), _p(bstart, _u64p),
                          len(bstart) - 1, s, _p(out, _f32p))
     return int(rc), out[: int(bstart[-1])]
+
+
+def decode_accumulate(streams, bstart, s: int, acc):
+    """streams: list of (words, offsets). Returns (status, acc + the decodes added
+    in list order, one fp32 addition per stream and coordinate)."""
+    bstart = np.ascontiguousarray(bstart, dtype=np.uint64)
+    n = int(bstart[-1])
+    out = np.array(acc, dtype=np.float32, copy=True)
+    if n == 0:
+        return OK, out
+    ws = [np.ascontiguousarray(w, dtype=np.uint64) if len(w) else np.zeros(1, np.uint64) for w, _ in streams]
+    nwords = np.array([len(w) for w, _ in streams] or [0], dtype=np.uint64)
+    offs = [np.ascontiguousarray(o, dtype=np.uint64) for _, o in streams]
+    k = len(streams)
+    wp = (ctypes.c_void_p * max(k, 1))(*[w.ctypes.data for w in ws])
+    op = (ctypes.c_void_p * max(k, 1))(*[o.ctypes.data for o in offs])
+    scratch = np.zeros(n, dtype=np.float32)
+    rc = lib().or_decode_accumulate(ctypes.addressof(wp), _p(nwords, _u64p), ctypes.addressof(op), k,
+                                    _p(bstart, _u64p), len(bstart) - 1, s, _p(out, _f32p),
+                                    _p(scratch, _f32p))
+    return int(rc), out
 
 
 def compress(v, bstart, s: int, seed: int, norms=None):

@@ -322,3 +322,20 @@ int or_decode(const uint64_t *words, uint64_t nwords, const uint64_t *offsets,
     }
     return OR_OK;
 }
+
+/* Receiving side of a gradient exchange: each node sums the quantized gradients
+ * it receives (page "QSGD: Communication-Efficient SGD via Gradient Quantization
+ * and Encoding", abstract: nodes communicate quantized gradient updates). The
+ * pages do not say how the sum is formed; reading: decode stream j, then add it
+ * to acc coordinate by coordinate in fp32, for j = 0, 1, ..., k-1 in turn. */
+int or_decode_accumulate(const uint64_t *const *words, const uint64_t *nwords,
+                         const uint64_t *const *offsets, uint64_t k, const uint64_t *bstart,
+                         uint64_t nb, uint32_t s, float *acc, float *scratch) {
+    const uint64_t n = bstart[nb];
+    for (uint64_t j = 0; j < k; ++j) {
+        int rc = or_decode(words[j], nwords[j], offsets[j], bstart, nb, s, scratch);
+        if (rc != OR_OK) return rc;
+        for (uint64_t i = 0; i < n; ++i) acc[i] = acc[i] + scratch[i];
+    }
+    return OR_OK;
+}

@@ -101,6 +101,14 @@ int or_encode(const int32_t *levels, const float *norms, const uint64_t *bstart,
 int or_decode(const uint64_t *words, uint64_t nwords, const uint64_t *offsets,
               const uint64_t *bstart, uint64_t nb, uint32_t s, float *out);
 
+/* Decode-accumulate of k streams: for j = 0..k-1 in turn, decode stream j
+ * (words[j], nwords[j] words, offsets[j]) into scratch [bstart[nb]] and set
+ * acc[i] = acc[i] + scratch[i] (one fp32 addition) for every coordinate.
+ * Returns the first decode error (acc then holds the streams before it). */
+int or_decode_accumulate(const uint64_t *const *words, const uint64_t *nwords,
+                         const uint64_t *const *offsets, uint64_t k, const uint64_t *bstart,
+                         uint64_t nb, uint32_t s, float *acc, float *scratch);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "QsgdError", "lib", "num_buckets", "encode_capacity_words", "quantize", "encode",
     "decode", "RaggedLayout", "quantize_ragged", "encode_ragged", "decode_ragged",
-    "max_bucket",
+    "max_bucket", "max_streams", "decode_accumulate", "decode_accumulate_ragged",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,8 +67,13 @@ def lib():
         L.qsgd_quantize_ragged.argtypes = [_vp, _u64, _vp, _u64, _u32, _u32, _u64, _vp, _vp, _vp]
         L.qsgd_encode_ragged.argtypes = [_vp, _u64, _vp, _u64, _u32, _u32, _u64, _vp, _vp, _vp, _vp]
         L.qsgd_decode_ragged.argtypes = [_vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp, _vp]
+        L.qsgd_max_streams.argtypes = []
+        L.qsgd_max_streams.restype = _u32
+        L.qsgd_decode_accumulate.argtypes = [_vp, _vp, _u32, _u64, _u32, _u32, _vp, _vp]
+        L.qsgd_decode_accumulate_ragged.argtypes = [_vp, _vp, _u32, _u64, _vp, _u64, _u32, _u32, _vp, _vp]
         for name in ("qsgd_quantize", "qsgd_encode", "qsgd_decode", "qsgd_ragged_bucket_table",
-                     "qsgd_quantize_ragged", "qsgd_encode_ragged", "qsgd_decode_ragged"):
+                     "qsgd_quantize_ragged", "qsgd_encode_ragged", "qsgd_decode_ragged",
+                     "qsgd_decode_accumulate", "qsgd_decode_accumulate_ragged"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -156,6 +161,30 @@ def decode(words: torch.Tensor, offsets: torch.Tensor, n: int, s: int, d: int, v
     return v_hat
 
 
+def max_streams() -> int:
+    return int(lib().qsgd_max_streams())
+
+
+def _pointer_arrays(words_list, offsets_list):
+    if len(words_list) != len(offsets_list):
+        raise ValueError("one offsets tensor per stream")
+    k = len(words_list)
+    ins = (ctypes.c_uint64 * max(k, 1))(*[_dev(w, torch.int64, "words") for w in words_list])
+    offs = (ctypes.c_uint64 * max(k, 1))(*[_dev(o, torch.int64, "offsets") for o in offsets_list])
+    return k, ins, offs
+
+
+def decode_accumulate(words_list, offsets_list, n: int, s: int, d: int, acc: torch.Tensor,
+                      stream=None):
+    """acc += the decodes of the streams, added in list order per coordinate
+    (one fp32 rounding per addition); returns acc."""
+    k, ins, offs = _pointer_arrays(words_list, offsets_list)
+    _check(lib().qsgd_decode_accumulate(ctypes.addressof(ins), ctypes.addressof(offs), k, n, s, d,
+                                        _dev(acc, torch.float32, "acc"), _stream(stream)),
+           "qsgd_decode_accumulate")
+    return acc
+
+
 class RaggedLayout:
     """Bucket layout of a batch of tensors laid out back to back in one buffer:
     buckets of at most d coordinates that restart at every tensor."""
@@ -219,3 +248,15 @@ def decode_ragged(words: torch.Tensor, offsets: torch.Tensor, layout: RaggedLayo
                                     s, layout.d, _dev(v_hat, torch.float32, "v_hat"), _stream(stream)),
            "qsgd_decode_ragged")
     return v_hat
+
+
+def decode_accumulate_ragged(words_list, offsets_list, layout: RaggedLayout, s: int, acc: torch.Tensor,
+                             stream=None):
+    """Ragged decode_accumulate."""
+    k, ins, offs = _pointer_arrays(words_list, offsets_list)
+    _check(lib().qsgd_decode_accumulate_ragged(ctypes.addressof(ins), ctypes.addressof(offs), k, layout.n,
+                                               _dev(layout.bucket_start, torch.int64, "bucket_start"),
+                                               layout.nb, s, layout.d, _dev(acc, torch.float32, "acc"),
+                                               _stream(stream)),
+           "qsgd_decode_accumulate_ragged")
+    return acc

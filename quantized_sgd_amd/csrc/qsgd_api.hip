@@ -212,15 +212,26 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     return launch_status();
 }
 
-qsgd_status decode_impl(const uint64_t *in, const uint64_t *offsets, uint64_t n, const uint64_t *bstart,
-                        uint64_t nb, uint32_t s, uint32_t d, float *v_hat, hipStream_t stream) {
+// Decodes one stream into v_hat, or (acc) adds the decodes of the nstreams
+// streams in[k] / offsets[k] to v_hat in stream order.
+qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offsets, uint32_t nstreams,
+                        bool acc, uint64_t n, const uint64_t *bstart, uint64_t nb, uint32_t s,
+                        uint32_t d, float *v_hat, hipStream_t stream) {
     qsgd_status st = check_common(nullptr, s, d);
     if (st != QSGD_OK) return st;
-    if (n == 0 || nb == 0) return QSGD_OK;
-    if (!in || !offsets || !v_hat || !aligned16(v_hat)) return QSGD_ERR_INVALID_ARG;
+    if (nstreams > kMaxStreams || (nstreams && (!in || !offsets))) return QSGD_ERR_INVALID_ARG;
+    if (n == 0 || nb == 0 || nstreams == 0) return QSGD_OK;
+    for (uint32_t k = 0; k < nstreams; ++k)
+        if (!in[k] || !offsets[k]) return QSGD_ERR_INVALID_ARG;
+    if (!v_hat || !aligned16(v_hat)) return QSGD_ERR_INVALID_ARG;
     if (d > (1u << 24)) return QSGD_ERR_UNSUPPORTED;
     DecodeParams D{};
-    D.in = in; D.offsets = offsets; D.bstart = bstart; D.v_hat = v_hat;
+    for (uint32_t k = 0; k < nstreams; ++k) {
+        D.in[k] = in[k];
+        D.offsets[k] = offsets[k];
+    }
+    D.nstreams = nstreams;
+    D.bstart = bstart; D.v_hat = v_hat;
     D.n = n; D.nb = nb; D.s = s; D.d = d;
     // LDS-staged output: whole groups of buckets of at most kGroupCoords
     // coordinates, levels fit int8. Team size: a power of two, about one lane per
@@ -244,8 +255,13 @@ qsgd_status decode_impl(const uint64_t *in, const uint64_t *offsets, uint64_t n,
         const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, resident_blocks(kernel, lds, kDecWG));
         hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kDecWG), lds, stream, D);
     };
-    if (bstart) launch(decode_kernel<true>);
-    else launch(decode_kernel<false>);
+    if (acc) {
+        if (bstart) lds_out ? launch(decode_kernel<true, true, true>) : launch(decode_kernel<true, false, true>);
+        else lds_out ? launch(decode_kernel<false, true, true>) : launch(decode_kernel<false, false, true>);
+    } else {
+        if (bstart) lds_out ? launch(decode_kernel<true, true, false>) : launch(decode_kernel<true, false, false>);
+        else lds_out ? launch(decode_kernel<false, true, false>) : launch(decode_kernel<false, false, false>);
+    }
     return launch_status();
 }
 
@@ -312,7 +328,17 @@ qsgd_status qsgd_encode(const float *v, uint64_t n, uint32_t s, uint32_t d, uint
 
 qsgd_status qsgd_decode(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
                         uint32_t s, uint32_t d, float *v_hat, hipStream_t stream) {
-    return decode_impl(in, bucket_bit_offsets, n, nullptr, qsgd_num_buckets(n, d), s, d, v_hat, stream);
+    return decode_impl(&in, &bucket_bit_offsets, 1, false, n, nullptr, qsgd_num_buckets(n, d), s, d,
+                       v_hat, stream);
+}
+
+uint32_t qsgd_max_streams(void) { return kMaxStreams; }
+
+qsgd_status qsgd_decode_accumulate(const uint64_t *const *in, const uint64_t *const *bucket_bit_offsets,
+                                   uint32_t k, uint64_t n, uint32_t s, uint32_t d, float *acc,
+                                   hipStream_t stream) {
+    return decode_impl(in, bucket_bit_offsets, k, true, n, nullptr, qsgd_num_buckets(n, d), s, d, acc,
+                       stream);
 }
 
 uint64_t qsgd_num_buckets_ragged(const uint64_t *seg_len, uint32_t nseg, uint32_t d) {
@@ -348,7 +374,15 @@ qsgd_status qsgd_decode_ragged(const uint64_t *in, const uint64_t *bucket_bit_of
                                const uint64_t *bucket_start, uint64_t nb, uint32_t s, uint32_t d,
                                float *v_hat, hipStream_t stream) {
     if (!bucket_start && nb) return QSGD_ERR_INVALID_ARG;
-    return decode_impl(in, bucket_bit_offsets, n, bucket_start, nb, s, d, v_hat, stream);
+    return decode_impl(&in, &bucket_bit_offsets, 1, false, n, bucket_start, nb, s, d, v_hat, stream);
+}
+
+qsgd_status qsgd_decode_accumulate_ragged(const uint64_t *const *in,
+                                          const uint64_t *const *bucket_bit_offsets, uint32_t k,
+                                          uint64_t n, const uint64_t *bucket_start, uint64_t nb,
+                                          uint32_t s, uint32_t d, float *acc, hipStream_t stream) {
+    if (!bucket_start && nb) return QSGD_ERR_INVALID_ARG;
+    return decode_impl(in, bucket_bit_offsets, k, true, n, bucket_start, nb, s, d, acc, stream);
 }
 
 }  // extern "C"

@@ -48,9 +48,14 @@ constexpr int kStagePad = 4;        // zero words after the staged stream
 constexpr int kGroupCoords = 4096;  // coordinates of a group whose levels are staged in LDS
 constexpr uint32_t kLevelSpare = kGroupCoords + 16;  // level byte for out-of-range writes
 
+// Streams that one decode-accumulate call sums.
+constexpr uint32_t kMaxStreams = 32;
+
 struct DecodeParams {
-    const uint64_t *in;
-    const uint64_t *offsets;
+    // the streams to decode (one for a plain decode) and their bucket offsets
+    const uint64_t *in[kMaxStreams];
+    const uint64_t *offsets[kMaxStreams];
+    uint32_t nstreams;
     const uint64_t *bstart;  // ragged table or nullptr
     float *v_hat;
     uint64_t n;
@@ -426,7 +431,9 @@ __device__ __forceinline__ bool extend_chain(const Bits<LDS> &r, const RecordCtx
 
 // Writes one lane's output range [lo, hi) in index order, exactly once: values
 // and the zeros between them, 16-byte stores for whole aligned quads inside the
-// range, single floats for the partial quads at its ends.
+// range, single floats for the partial quads at its ends. ACC: adds them to the
+// output instead (the zeros too: -0.0f + +0.0f is +0.0f).
+template <bool ACC>
 struct QuadWriter {
     float *out;
     uint64_t lo, hi, q;
@@ -436,22 +443,31 @@ struct QuadWriter {
         out = o; lo = l; hi = h; q = l >> 2;
         v0 = v1 = v2 = v3 = 0.0f;
     }
+    __device__ __forceinline__ static void put1(float *p, float v) { *p = ACC ? *p + v : v; }
+    __device__ __forceinline__ static void put4(float *p, float4 v) {
+        float4 *p4 = reinterpret_cast<float4 *>(p);
+        if (ACC) {
+            const float4 o = *p4;
+            v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+        }
+        *p4 = v;
+    }
     __device__ __forceinline__ void flush() const {
         const uint64_t a = q << 2;
         if (a >= lo && a + 4 <= hi) {
-            *reinterpret_cast<float4 *>(out + a) = make_float4(v0, v1, v2, v3);
+            put4(out + a, make_float4(v0, v1, v2, v3));
         } else {
-            if (a >= lo && a < hi) out[a] = v0;
-            if (a + 1 >= lo && a + 1 < hi) out[a + 1] = v1;
-            if (a + 2 >= lo && a + 2 < hi) out[a + 2] = v2;
-            if (a + 3 >= lo && a + 3 < hi) out[a + 3] = v3;
+            if (a >= lo && a < hi) put1(out + a, v0);
+            if (a + 1 >= lo && a + 1 < hi) put1(out + a + 1, v1);
+            if (a + 2 >= lo && a + 2 < hi) put1(out + a + 2, v2);
+            if (a + 3 >= lo && a + 3 < hi) put1(out + a + 3, v3);
         }
     }
     // moves to quad nq > q: writes the current quad and the all-zero quads between
     __device__ __forceinline__ void advance(uint64_t nq) {
         flush();
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (uint64_t t = q + 1; t < nq; ++t) *reinterpret_cast<float4 *>(out + (t << 2)) = z;
+        for (uint64_t t = q + 1; t < nq; ++t) put4(out + (t << 2), z);
         q = nq;
         v0 = v1 = v2 = v3 = 0.0f;
     }
@@ -487,14 +503,15 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 
-// Decodes the buckets [b0, b1) of one wave group; `r` reads the group's stream,
-// bit 0 being stream bit `gbit`. LDS_OUT: each record's level byte (sign << 7 |
-// k) goes to the group's LDS buffer `lvl` (index = coordinate - lbase, cleared
-// by the caller) and each bucket's RN64(norm / s) to
-// ebs[team]; otherwise every
-// lane writes its own output range with a QuadWriter.
-template <bool RAGGED, bool LDS_IN, bool LDS_OUT>
-__device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32_t *lut,
+// Decodes the buckets [b0, b1) of one wave group of a stream with bucket
+// offsets `offs`; `r` reads the group's stream, bit 0 being stream bit `gbit`.
+// LDS_OUT: each record's level byte (sign << 7 | k) goes to the group's LDS
+// buffer `lvl` (index = coordinate - lbase, cleared here) and each bucket's
+// RN64(norm / s) to ebs[team]; otherwise every lane writes (ACC: adds) its own
+// output range with a QuadWriter.
+template <bool RAGGED, bool LDS_IN, bool LDS_OUT, bool ACC>
+__device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64_t *offs,
+                                             const uint32_t *lut,
                                              const Bits<LDS_IN> &r, uint64_t gbit, uint64_t b0,
                                              uint64_t b1, uint8_t *lvl, double *ebs, uint64_t lbase,
                                              uint32_t nclear16) {
@@ -510,8 +527,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
     double e_b = 0.0;
     uint32_t nl = 0;
     if (tactive) {
-        A = (uint32_t)(D.offsets[b] - gbit);
-        E = (uint32_t)(D.offsets[b + 1] - gbit);
+        A = (uint32_t)(offs[b] - gbit);
+        E = (uint32_t)(offs[b + 1] - gbit);
         c0 = bucket_first<RAGGED>(D, b);
         len = bucket_first<RAGGED>(D, b + 1) - c0;
         if (E >= A + 32u && len > 0) {
@@ -652,7 +669,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
         if (lo > len) lo = len;
         if (hi > len) hi = len;
         if (hi < lo) hi = lo;
-        QuadWriter w;
+        QuadWriter<ACC> w;
         w.init(D.v_hat, c0 + lo, c0 + hi);
         if (act) {
             uint32_t p = ystart;
@@ -674,9 +691,10 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint32
 
 // Writes the group's buckets from the LDS level bytes: RN32(k * RN64(norm / s))
 // with the byte's sign (+0.0f for k = 0), 16-byte stores for whole aligned
-// quads of a bucket, single floats for quads that a bucket boundary cuts. The
-// value of each of the 256 level bytes is tabulated per bucket in `tbl` first.
-template <bool RAGGED>
+// quads of a bucket, single floats for quads that a bucket boundary cuts (ACC:
+// added to the output). The value of each of the 256 level bytes is tabulated
+// per bucket in `tbl` first.
+template <bool RAGGED, bool ACC>
 __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t *lvl, const double *ebs,
                                             float *tbl, uint64_t lbase, uint64_t b0, uint64_t b1) {
     const uint32_t lane = (uint32_t)lane_id();
@@ -697,12 +715,12 @@ __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t
             const float v0 = tbl[word & 0xffu], v1 = tbl[(word >> 8) & 0xffu];
             const float v2 = tbl[(word >> 16) & 0xffu], v3 = tbl[word >> 24];
             if (a >= A && a + 4 <= B) {
-                *reinterpret_cast<float4 *>(D.v_hat + a) = make_float4(v0, v1, v2, v3);
+                QuadWriter<ACC>::put4(D.v_hat + a, make_float4(v0, v1, v2, v3));
             } else {
-                if (a >= A && a < B) D.v_hat[a] = v0;
-                if (a + 1 >= A && a + 1 < B) D.v_hat[a + 1] = v1;
-                if (a + 2 >= A && a + 2 < B) D.v_hat[a + 2] = v2;
-                if (a + 3 >= A && a + 3 < B) D.v_hat[a + 3] = v3;
+                if (a >= A && a < B) QuadWriter<ACC>::put1(D.v_hat + a, v0);
+                if (a + 1 >= A && a + 1 < B) QuadWriter<ACC>::put1(D.v_hat + a + 1, v1);
+                if (a + 2 >= A && a + 2 < B) QuadWriter<ACC>::put1(D.v_hat + a + 2, v2);
+                if (a + 3 >= A && a + 3 < B) QuadWriter<ACC>::put1(D.v_hat + a + 3, v3);
             }
         }
         // the table is rebuilt for the next bucket
@@ -723,7 +741,11 @@ static_assert(2 * ((size_t)kDecWaves * kWaveLdsBytes + 16384) <= 160 * 1024, "de
 
 constexpr size_t decode_lds_bytes() { return (size_t)kDecWaves * kWaveLdsBytes + sizeof(RecordLut); }
 
-template <bool RAGGED>
+// LDS_OUT: levels staged in LDS (D.lds_out), else each lane writes its range.
+// ACC: the output accumulates the D.nstreams streams in order, per coordinate
+// out = ((out + v_hat_0) + v_hat_1) + ...; the wave takes all streams of a
+// group in turn, so the group's outputs stay in L2 between them.
+template <bool RAGGED, bool LDS_OUT, bool ACC>
 __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     extern __shared__ __align__(16) uint64_t dsmem[];
     // record table after the waves' regions (a constant offset: folds into the
@@ -746,45 +768,50 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     double *ebs = reinterpret_cast<double *>(wbase + kStageBytes + kLevelBytes);
     const uint32_t tpw = D.tpw;
     const uint64_t ngroups = (D.nb + tpw - 1) / tpw;
-    const uint64_t total_bits = D.offsets[D.nb];
-    const uint64_t total_words = (total_bits + 63) >> 6;
 
     for (uint64_t g = (uint64_t)blockIdx.x * kDecWaves + (uint64_t)wv; g < ngroups;
          g += (uint64_t)gridDim.x * kDecWaves) {
         const uint64_t b0 = g * tpw;
         const uint64_t b1 = b0 + tpw < D.nb ? b0 + tpw : D.nb;
-        const uint64_t A0 = D.offsets[b0], E1 = D.offsets[b1];
-        const uint64_t w0 = A0 >> 6;
-        uint64_t w1 = E1 > A0 ? ((E1 + 63) >> 6) : w0;
-        if (w1 > total_words) w1 = total_words;
-        const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
-        const bool in_lds = nw <= (uint64_t)kStageWords;
-        if (in_lds) {
-            // bit-reversed words: stream bit 64 i + t of the group in bit t of word i
-            for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64)
-                stage[i] = i < nw ? __builtin_bitreverse64(D.in[w0 + i]) : 0ull;
-        }
         const uint64_t lbase = bucket_first<RAGGED>(D, b0) & ~(uint64_t)3;
-        const uint32_t span = D.lds_out ? (uint32_t)(bucket_first<RAGGED>(D, b1) - lbase) : 0u;
+        const uint32_t span = LDS_OUT ? (uint32_t)(bucket_first<RAGGED>(D, b1) - lbase) : 0u;
         const uint32_t nclear16 = (span + 3 + 15) >> 4;
-        // staged words are read by other lanes of this wave
-        wave_sync();
-        // LDS positions are LDS bit addresses: the group's bit 0 is the first bit of stage
-        Bits<true> rl{nullptr, 0u};
-        const uint64_t lgbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
-        Bits<false> rg{reinterpret_cast<const uint32_t *>(D.in + w0),
-                       (uint32_t)(2 * (total_words - w0)) - 1u};
-        if (D.lds_out) {
-            if (in_lds) decode_group<RAGGED, true, true>(D, lut, rl, lgbit, b0, b1, lvl, ebs, lbase, nclear16);
-            else decode_group<RAGGED, false, true>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
+        for (uint32_t k = 0; k < (ACC ? D.nstreams : 1u); ++k) {
+            const uint64_t *in = D.in[k];
+            const uint64_t *offs = D.offsets[k];
+            const uint64_t total_words = (offs[D.nb] + 63) >> 6;
+            const uint64_t A0 = offs[b0], E1 = offs[b1];
+            const uint64_t w0 = A0 >> 6;
+            uint64_t w1 = E1 > A0 ? ((E1 + 63) >> 6) : w0;
+            if (w1 > total_words) w1 = total_words;
+            const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
+            const bool in_lds = nw <= (uint64_t)kStageWords;
+            if (in_lds) {
+                // bit-reversed words: stream bit 64 i + t of the group in bit t of word i
+                for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64)
+                    stage[i] = i < nw ? __builtin_bitreverse64(in[w0 + i]) : 0ull;
+            }
+            // staged words are read by other lanes of this wave
             wave_sync();
-            store_group<RAGGED>(D, lvl, ebs, reinterpret_cast<float *>(stage), lbase, b0, b1);
-        } else {
-            if (in_lds) decode_group<RAGGED, true, false>(D, lut, rl, lgbit, b0, b1, lvl, ebs, lbase, nclear16);
-            else decode_group<RAGGED, false, false>(D, lut, rg, w0 * 64, b0, b1, lvl, ebs, lbase, nclear16);
+            // LDS positions are LDS bit addresses: the group's bit 0 is the first bit of stage
+            Bits<true> rl{nullptr, 0u};
+            const uint64_t lgbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
+            Bits<false> rg{reinterpret_cast<const uint32_t *>(in + w0),
+                           (uint32_t)(2 * (total_words - w0)) - 1u};
+            if (in_lds)
+                decode_group<RAGGED, true, LDS_OUT, ACC>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs, lbase,
+                                                         nclear16);
+            else
+                decode_group<RAGGED, false, LDS_OUT, ACC>(D, offs, lut, rg, w0 * 64, b0, b1, lvl, ebs,
+                                                          lbase, nclear16);
+            if (LDS_OUT) {
+                wave_sync();
+                // the staged stream is done with: its space holds the value table
+                store_group<RAGGED, ACC>(D, lvl, ebs, reinterpret_cast<float *>(stage), lbase, b0, b1);
+            }
+            // the LDS buffers are reused by the next stream or group of this wave
+            wave_sync();
         }
-        // the LDS buffers are reused by the next group of this wave
-        wave_sync();
     }
 }
 

@@ -100,6 +100,14 @@ def config5() -> Workload:
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
+def peer_gradient(cfg: int, j: int) -> np.ndarray:
+    """Gradient of worker j for the decode-accumulate workloads (the gradients a
+    receiver sums): same size and value mix as config 2 or 3, worker 0 being the
+    config's own gradient."""
+    n = {2: 25_557_032, 3: 60_192_808}[cfg]
+    return chunked_gaussian(n, cfg + 100 * j)
+
+
 def small_gaussian(n: int, seed: int, scale: float = 1.0) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     return (scale * rng.standard_normal(n)).astype(np.float32)

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(q.LIB_PATH)
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 16
     for name in names:
         assert hasattr(lib, name), name
 
@@ -48,6 +48,23 @@ def test_host_helpers_match_oracle_bucketing():
     assert np.array_equal(tab, oracle.ragged_buckets(seg, 512))
     # a wrong nb is rejected
     assert lib.qsgd_ragged_bucket_table(sl.ctypes.data, len(sl), 512, tab.ctypes.data, nb + 1) == 1
+
+
+def test_decode_accumulate_argument_checks():
+    # rejected (or a no-op) on the host before anything touches a device
+    lib = q.lib()
+    assert lib.qsgd_max_streams() == 32
+    k = 33
+    ptrs = (ctypes.c_uint64 * k)(*([16] * k))
+    addr = ctypes.addressof(ptrs)
+    assert lib.qsgd_decode_accumulate(addr, addr, k, 100, 4, 16, 16, None) == 1    # too many streams
+    assert lib.qsgd_decode_accumulate(None, None, 2, 100, 4, 16, 16, None) == 1    # no pointer arrays
+    zero = (ctypes.c_uint64 * 2)(16, 0)
+    assert lib.qsgd_decode_accumulate(ctypes.addressof(zero), addr, 2, 100, 4, 16, 16, None) == 1  # NULL entry
+    assert lib.qsgd_decode_accumulate(addr, addr, 2, 100, 0, 16, 16, None) == 1    # s == 0
+    assert lib.qsgd_decode_accumulate(addr, addr, 0, 100, 4, 16, 16, None) == 0    # k == 0: nothing to do
+    assert lib.qsgd_decode_accumulate(addr, addr, 2, 0, 4, 16, 16, None) == 0      # n == 0: nothing to do
+    assert lib.qsgd_decode_accumulate(addr, addr, 2, 100, 4, 16, 18, None) == 1    # acc not 16-byte aligned
 
 
 def test_capacity_bounds_oracle_streams():
