@@ -91,6 +91,41 @@ def cpu_baseline(w, max_coords: int, reps: int = 3):
                       f"quantize+encode+decode, median of {reps} runs, {t:.2f} s each"}
 
 
+def decode_accumulate_leg(q, wl, torch, args, v0, n, s, d, seed, nb, stream):
+    """Decode-accumulate of k workers' streams (worker 0: the config's gradient)
+    into one fp32 buffer, timed with HIP events on the launch stream. Algorithmic
+    HBM bytes: the k streams and offset tables read, acc read and written once."""
+    k = args.acc_streams
+    dev = v0.device
+    words, offs, nbits = [], [], 0
+    for j in range(k):
+        vj = v0 if j == 0 else torch.from_numpy(wl.peer_gradient(args.config, j)).to(dev)
+        o, b, f = q.encode(vj, s, d, seed + j)
+        words.append(o)
+        offs.append(f)
+        nbits += int(b.item())
+        del vj
+    acc = torch.zeros(n, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        q.decode_accumulate(words, offs, n, s, d, acc)
+    torch.cuda.synchronize()
+    steps = max(1, args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        q.decode_accumulate(words, offs, n, s, d, acc)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    avg = sum(ms) / steps
+    alg = 8.0 * n + nbits / 8.0 + 8.0 * k * (nb + 1)
+    return {"streams": k, "ms_median": round(ms[len(ms) // 2], 4), "ms_avg": round(avg, 4),
+            "decoded_GBps_fp32": round(4.0 * n * k / (avg * 1e-3) / 1e9, 2),
+            "hbm_GBps_algorithmic": round(alg / (avg * 1e-3) / 1e9, 2),
+            "hbm_frac": round(alg / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes": round(alg)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +135,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--cpu-sample", type=int, default=0, help="coordinates for the oracle (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--acc-streams", type=int, default=4,
+                    help="streams of the decode-accumulate measurement (configs 2, 3; 0: skip)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -210,6 +247,8 @@ def main():
                      "traffic": measured_traffic(dominant),
                      "algorithmic_bytes": round(enc_bytes if dominant == "encode" else dec_bytes)},
     }
+    if args.acc_streams and args.config in (2, 3) and not ragged:
+        res["decode_accumulate"] = decode_accumulate_leg(q, wl, torch, args, vs[0], n, s, d, seed, nb, stream)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
     print(json.dumps(res), flush=True)
