@@ -94,7 +94,8 @@ def cpu_baseline(w, max_coords: int, reps: int = 3):
 def decode_accumulate_leg(q, wl, torch, args, v0, n, s, d, seed, nb, stream):
     """Decode-accumulate of k workers' streams (worker 0: the config's gradient)
     into one fp32 buffer, timed with HIP events on the launch stream. Algorithmic
-    HBM bytes: the k streams and offset tables read, acc read and written once."""
+    HBM bytes (the least any implementation moves): the k streams and offset
+    tables read, acc read and written once."""
     k = args.acc_streams
     dev = v0.device
     words, offs, nbits = [], [], 0

@@ -140,8 +140,10 @@ qsgd_status qsgd_decode(const uint64_t *in, const uint64_t *bucket_bit_offsets, 
 uint32_t qsgd_max_streams(void);
 
 /*
- * qsgd_decode_accumulate: adds the decodes of k streams to acc in one pass over
- * acc (each workgroup decodes all k streams of a group of buckets in turn).
+ * qsgd_decode_accumulate: adds the decodes of k streams to acc in one launch
+ * (each wave decodes all k streams of a group of buckets in turn and adds each
+ * to the group's part of acc: acc is read and written once per stream, the
+ * decoded values never go to memory).
  *   in                  HOST array of k DEVICE pointers: stream words of each
  *                       stream, written by qsgd_encode with the same n, s, d.
  *   bucket_bit_offsets  HOST array of k DEVICE pointers: each stream's

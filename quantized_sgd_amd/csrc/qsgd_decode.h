@@ -744,7 +744,8 @@ constexpr size_t decode_lds_bytes() { return (size_t)kDecWaves * kWaveLdsBytes +
 // LDS_OUT: levels staged in LDS (D.lds_out), else each lane writes its range.
 // ACC: the output accumulates the D.nstreams streams in order, per coordinate
 // out = ((out + v_hat_0) + v_hat_1) + ...; the wave takes all streams of a
-// group in turn, so the group's outputs stay in L2 between them.
+// group in turn, reading, adding to and writing back the group's outputs once
+// per stream.
 template <bool RAGGED, bool LDS_OUT, bool ACC>
 __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     extern __shared__ __align__(16) uint64_t dsmem[];
