@@ -77,6 +77,16 @@ def lib():
         L.or_decode.argtypes = [_u64p, ctypes.c_uint64, _u64p, _u64p, ctypes.c_uint64,
                                 ctypes.c_uint32, _f32p]
         L.or_decode.restype = ctypes.c_int
+        L.or_gamma_length.argtypes = [ctypes.c_uint64]
+        L.or_gamma_length.restype = ctypes.c_uint
+        L.or_gamma_codeword.argtypes = [ctypes.c_uint64, ctypes.c_char_p]
+        L.or_gamma_codeword.restype = ctypes.c_uint
+        L.or_encode_code.argtypes = [_i32p, _f32p, _u64p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
+                                     _u64p, ctypes.c_uint64, _u64p, _u64p]
+        L.or_encode_code.restype = ctypes.c_int
+        L.or_decode_code.argtypes = [_u64p, ctypes.c_uint64, _u64p, _u64p, ctypes.c_uint64,
+                                     ctypes.c_uint32, ctypes.c_int, _f32p]
+        L.or_decode_code.restype = ctypes.c_int
         L.or_decode_accumulate.argtypes = [ctypes.c_void_p, _u64p, ctypes.c_void_p, ctypes.c_uint64,
                                            _u64p, ctypes.c_uint64, ctypes.c_uint32, _f32p, _f32p]
         L.or_decode_accumulate.restype = ctypes.c_int
@@ -176,36 +186,53 @@ def dequantize(levels, norms, bstart, s: int) -> np.ndarray:
     return out
 
 
-def capacity_words(bstart, s: int) -> int:
+OMEGA, GAMMA = 0, 1  # integer codes of the record fields
+
+
+def gamma_length(N: int) -> int:
+    return int(lib().or_gamma_length(N))
+
+
+def gamma_codeword(N: int) -> str:
+    buf = ctypes.create_string_buffer(160)
+    lib().or_gamma_codeword(N, buf)
+    return buf.value.decode()
+
+
+def code_length(N: int, code: int = OMEGA) -> int:
+    return gamma_length(N) if code == GAMMA else omega_length(N)
+
+
+def capacity_words(bstart, s: int, code: int = OMEGA) -> int:
     """A bound on the stream size: 32 bits per bucket plus, per coordinate, one
-    omega code of a gap (at most the longest bucket), a sign and omega(s)."""
+    code of a gap (at most the longest bucket), a sign and the code of s."""
     bstart = np.asarray(bstart, dtype=np.uint64)
     nb = len(bstart) - 1
     n = int(bstart[-1])
     dmax = int(np.max(np.diff(bstart))) if nb else 1
-    bits = 32 * nb + n * (omega_length(max(dmax, 1)) + 1 + omega_length(s))
+    bits = 32 * nb + n * (code_length(max(dmax, 1), code) + 1 + code_length(s, code))
     return bits // 64 + 2
 
 
-def encode(levels, norms, bstart, s: int):
+def encode(levels, norms, bstart, s: int, code: int = OMEGA):
     """Returns (words uint64, offsets uint64[nb+1], out_bits)."""
     levels = np.ascontiguousarray(levels, dtype=np.int32)
     norms = np.ascontiguousarray(norms, dtype=np.float32)
     bstart = np.ascontiguousarray(bstart, dtype=np.uint64)
     nb = len(bstart) - 1
-    cap = capacity_words(bstart, s)
+    cap = capacity_words(bstart, s, code)
     words = np.zeros(cap, dtype=np.uint64)
     offsets = np.zeros(nb + 1, dtype=np.uint64)
     out_bits = np.zeros(1, dtype=np.uint64)
-    rc = lib().or_encode(_p(levels, _i32p), _p(norms, _f32p), _p(bstart, _u64p), nb, s,
-                         _p(words, _u64p), cap, _p(offsets, _u64p), _p(out_bits, _u64p))
+    rc = lib().or_encode_code(_p(levels, _i32p), _p(norms, _f32p), _p(bstart, _u64p), nb, s, code,
+                              _p(words, _u64p), cap, _p(offsets, _u64p), _p(out_bits, _u64p))
     if rc != OK:
         raise ValueError(f"oracle encode failed with status {rc}")
     nbits = int(out_bits[0])
     return words[: (nbits + 63) // 64].copy(), offsets, nbits
 
 
-def decode(words, offsets, bstart, s: int):
+def decode(words, offsets, bstart, s: int, code: int = OMEGA):
     """Returns (status, v_hat float32)."""
     words = np.ascontiguousarray(words, dtype=np.uint64)
     if len(words) == 0:
@@ -218,8 +245,8 @@ def decode(words, offsets, bstart, s: int):
     out = np.zeros(int(bstart[-1]), dtype=np.float32)
     if len(out) == 0:
         out = np.zeros(1, dtype=np.float32)
-    rc = lib().or_decode(_p(words, _u64p), nwords, _p(offsets, _u64p), _p(bstart, _u64p),
-                         len(bstart) - 1, s, _p(out, _f32p))
+    rc = lib().or_decode_code(_p(words, _u64p), nwords, _p(offsets, _u64p), _p(bstart, _u64p),
+                              len(bstart) - 1, s, code, _p(out, _f32p))
     return int(rc), out[: int(bstart[-1])]
 
 
@@ -244,8 +271,8 @@ def decode_accumulate(streams, bstart, s: int, acc):
     return int(rc), out
 
 
-def compress(v, bstart, s: int, seed: int, norms=None):
+def compress(v, bstart, s: int, seed: int, norms=None, code: int = OMEGA):
     """quantize + encode: (levels, norms, words, offsets, out_bits)."""
     levels, nrm = quantize(v, bstart, s, seed, norms=norms)
-    words, offsets, nbits = encode(levels, nrm, bstart, s)
+    words, offsets, nbits = encode(levels, nrm, bstart, s, code)
     return levels, nrm, words, offsets, nbits

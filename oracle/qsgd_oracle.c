@@ -102,6 +102,19 @@ unsigned or_omega_length(uint64_t N) {
     return len;
 }
 
+/* Elias gamma code (same paper as omega): floor(log2 N) zeros, then the binary
+ * form of N, most significant bit first. The page names "Elias recursive
+ * gamma/omega" coding for the gaps and levels. */
+unsigned or_gamma_codeword(uint64_t N, char *out) {
+    unsigned nb = bit_count(N), len = 0;
+    for (unsigned z = 1; z < nb; ++z) out[len++] = '0';
+    for (unsigned b = nb; b-- > 0;) out[len++] = (char)('0' + ((N >> b) & 1u));
+    out[len] = '\0';
+    return len;
+}
+
+unsigned or_gamma_length(uint64_t N) { return 2 * bit_count(N) - 1; }
+
 /* ------------------------------------------------------------------------ */
 /* Buckets: Section 3.3 of the paper (per the claims on the curated page) applies
  * the quantizer independently to blocks of d consecutive coordinates; the last
@@ -234,16 +247,23 @@ static void put_bit(bitwriter *bw, unsigned bit) {
     bw->pos++;
 }
 
-static void put_omega(bitwriter *bw, uint64_t N) {
-    char code[160];
-    unsigned len = or_omega_codeword(N, code);
-    for (unsigned t = 0; t < len; ++t) put_bit(bw, code[t] == '1');
+/* The integer code of a record field: omega (code 0) or gamma (code 1). */
+static void put_code(bitwriter *bw, uint64_t N, int code) {
+    char cw[160];
+    unsigned len = code ? or_gamma_codeword(N, cw) : or_omega_codeword(N, cw);
+    for (unsigned t = 0; t < len; ++t) put_bit(bw, cw[t] == '1');
 }
 
 int or_encode(const int32_t *levels, const float *norms, const uint64_t *bstart,
               uint64_t nb, uint32_t s, uint64_t *words, uint64_t cap_words,
               uint64_t *offsets, uint64_t *out_bits) {
-    if (s == 0) return OR_ERR_ARG;
+    return or_encode_code(levels, norms, bstart, nb, s, 0, words, cap_words, offsets, out_bits);
+}
+
+int or_encode_code(const int32_t *levels, const float *norms, const uint64_t *bstart,
+                   uint64_t nb, uint32_t s, int code, uint64_t *words, uint64_t cap_words,
+                   uint64_t *offsets, uint64_t *out_bits) {
+    if (s == 0 || code < 0 || code > 1) return OR_ERR_ARG;
     bitwriter bw = {words, cap_words * 64, 0, 0};
     memset(words, 0, cap_words * sizeof(uint64_t));
     for (uint64_t b = 0; b < nb; ++b) {
@@ -252,7 +272,7 @@ int or_encode(const int32_t *levels, const float *norms, const uint64_t *bstart,
         uint32_t nbits;
         memcpy(&nbits, &norms[b], sizeof nbits);
         for (int t = 31; t >= 0; --t) put_bit(&bw, (nbits >> t) & 1u);
-        /* each non-zero: omega(gap), sign, omega(k); gaps are 1-based */
+        /* each non-zero: code(gap), sign, code(k); gaps are 1-based */
         int64_t prev = -1;
         for (uint64_t i = bstart[b]; i < bstart[b + 1]; ++i) {
             int32_t q = levels[i];
@@ -260,9 +280,9 @@ int or_encode(const int32_t *levels, const float *norms, const uint64_t *bstart,
             int64_t j = (int64_t)(i - bstart[b]);
             uint32_t k = (uint32_t)(q < 0 ? -q : q);
             if (k > s) return OR_ERR_ARG;
-            put_omega(&bw, (uint64_t)(j - prev));
+            put_code(&bw, (uint64_t)(j - prev), code);
             put_bit(&bw, q < 0 ? 1u : 0u);
-            put_omega(&bw, k);
+            put_code(&bw, k, code);
             prev = j;
         }
     }
@@ -293,9 +313,26 @@ static uint64_t get_omega(bitreader *br) {
     return N;
 }
 
+/* Gamma decoding: count the 0 bits before the first 1; that 1 and the same
+ * number of bits after it are the binary form of N. */
+static uint64_t get_gamma(bitreader *br) {
+    unsigned z = 0;
+    while (!br->bad && !get_bit(br)) {
+        if (++z > 63) { br->bad = 1; return 0; }
+    }
+    uint64_t N = 1;
+    for (unsigned t = 0; t < z; ++t) N = (N << 1) | get_bit(br);
+    return N;
+}
+
 int or_decode(const uint64_t *words, uint64_t nwords, const uint64_t *offsets,
               const uint64_t *bstart, uint64_t nb, uint32_t s, float *out) {
-    if (s == 0) return OR_ERR_ARG;
+    return or_decode_code(words, nwords, offsets, bstart, nb, s, 0, out);
+}
+
+int or_decode_code(const uint64_t *words, uint64_t nwords, const uint64_t *offsets,
+                   const uint64_t *bstart, uint64_t nb, uint32_t s, int code, float *out) {
+    if (s == 0 || code < 0 || code > 1) return OR_ERR_ARG;
     if (offsets[nb] > nwords * 64) return OR_ERR_MALFORMED;
     for (uint64_t b = 0; b < nb; ++b)
         if (offsets[b + 1] < offsets[b]) return OR_ERR_MALFORMED;
@@ -310,9 +347,9 @@ int or_decode(const uint64_t *words, uint64_t nwords, const uint64_t *offsets,
         memcpy(&norm, &nbits, sizeof norm);
         int64_t j = -1;
         while (br.pos < br.end) {
-            uint64_t gap = get_omega(&br);
+            uint64_t gap = code ? get_gamma(&br) : get_omega(&br);
             unsigned neg = get_bit(&br);
-            uint64_t k = get_omega(&br);
+            uint64_t k = code ? get_gamma(&br) : get_omega(&br);
             if (br.bad) return OR_ERR_MALFORMED;
             j += (int64_t)gap;
             if (j >= (int64_t)len || k < 1 || k > s) return OR_ERR_MALFORMED;

@@ -63,6 +63,11 @@ unsigned or_omega_length(uint64_t N);
  * least 130 bytes); returns its length. */
 unsigned or_omega_codeword(uint64_t N, char *out);
 
+/* Elias gamma code (same paper): floor(log2 N) zeros, then N in binary, most
+ * significant bit first; length 2 floor(log2 N) + 1. */
+unsigned or_gamma_length(uint64_t N);
+unsigned or_gamma_codeword(uint64_t N, char *out);
+
 /* Bucket tables: bstart has nb + 1 entries; bucket b covers coordinates
  * [bstart[b], bstart[b+1]). Return nb. A NULL bstart only counts. */
 uint64_t or_uniform_buckets(uint64_t n, uint64_t d, uint64_t *bstart);
@@ -95,11 +100,21 @@ int or_encode(const int32_t *levels, const float *norms, const uint64_t *bstart,
               uint64_t nb, uint32_t s, uint64_t *words, uint64_t cap_words,
               uint64_t *offsets, uint64_t *out_bits);
 
+/* or_encode with the integer code chosen: 0 = Elias omega, 1 = Elias gamma (the
+ * page names "Elias recursive gamma/omega" coding). The stream layout is the
+ * same; only the codewords of gaps and levels change. */
+int or_encode_code(const int32_t *levels, const float *norms, const uint64_t *bstart,
+                   uint64_t nb, uint32_t s, int code, uint64_t *words, uint64_t cap_words,
+                   uint64_t *offsets, uint64_t *out_bits);
+
 /* Decoding and dequantization. Returns OR_ERR_MALFORMED for a stream that does
  * not parse (gap past the bucket, level outside 1..s, record past the bucket's
  * end, offsets not monotone); out is then partially written. */
 int or_decode(const uint64_t *words, uint64_t nwords, const uint64_t *offsets,
               const uint64_t *bstart, uint64_t nb, uint32_t s, float *out);
+/* or_decode with the integer code chosen as in or_encode_code. */
+int or_decode_code(const uint64_t *words, uint64_t nwords, const uint64_t *offsets,
+                   const uint64_t *bstart, uint64_t nb, uint32_t s, int code, float *out);
 
 /* Decode-accumulate of k streams: for j = 0..k-1 in turn, decode stream j
  * (words[j], nwords[j] words, offsets[j]) into scratch [bstart[nb]] and set

@@ -39,7 +39,8 @@ def case_vector(c):
 def test_hand_derived_streams(case):
     v = case_vector(case)
     bst = oracle.uniform_buckets(len(v), case["d"])
-    lev, nrm, words, offs, nbits = oracle.compress(v, bst, case["s"], case["seed"])
+    code = oracle.GAMMA if case.get("code") == "gamma" else oracle.OMEGA
+    lev, nrm, words, offs, nbits = oracle.compress(v, bst, case["s"], case["seed"], code=code)
     assert nbits == case["out_bits"]
     assert list(offs) == case["offsets"]
     got = [f"{int(w):016x}" for w in words]
@@ -49,7 +50,7 @@ def test_hand_derived_streams(case):
         assert len(got) == case["n_words"]
         assert got[: len(case["words_head"])] == case["words_head"]
         assert all(w == "0" * 16 for w in got[len(case["words_head"]):])
-    rc, vh = oracle.decode(words, offs, bst, case["s"])
+    rc, vh = oracle.decode(words, offs, bst, case["s"], code)
     assert rc == oracle.OK
     assert np.array_equal(vh, oracle.dequantize(lev, nrm, bst, case["s"]))
 
