@@ -91,6 +91,55 @@ def cpu_baseline(w, max_coords: int, reps: int = 3):
                       f"quantize+encode+decode, median of {reps} runs, {t:.2f} s each"}
 
 
+def gamma_leg(q, torch, args, v, lay, n, s, d, seed, nb, cap_omega, stream, nbits_omega):
+    """The same workload with Elias-gamma record codes (qsgd_encode_ex /
+    qsgd_decode_ex): call times on the launch stream, bits per coordinate, and
+    the algorithmic-bytes HBM fractions, next to omega's."""
+    dev = v.device
+    G = q.GAMMA
+    ragged = lay is not None
+    cap = lay.capacity_words(s, G) if ragged else q.encode_capacity_words(n, s, d, G)
+    out = torch.empty(cap, dtype=torch.int64, device=dev)
+    bits = torch.empty(1, dtype=torch.int64, device=dev)
+    offs = torch.empty(nb + 1, dtype=torch.int64, device=dev)
+    vh = torch.empty(n, dtype=torch.float32, device=dev)
+
+    def enc():
+        if ragged:
+            q.encode_ragged(v, lay, s, seed, out=out, out_bits=bits, offsets=offs, code=G)
+        else:
+            q.encode(v, s, d, seed, out=out, out_bits=bits, offsets=offs, code=G)
+
+    def dec():
+        if ragged:
+            q.decode_ragged(out, offs, lay, s, v_hat=vh, code=G)
+        else:
+            q.decode(out, offs, n, s, d, v_hat=vh, code=G)
+
+    for _ in range(2):
+        enc()
+        dec()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        enc()
+        ev[i][1].record(stream)
+        dec()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    e_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    d_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    nbits = int(bits.item())
+    alg = 4.0 * n + nbits / 8.0 + 8.0 * (nb + 1)
+    return {"encode_ms_avg": round(e_ms, 4), "decode_ms_avg": round(d_ms, 4),
+            "round_trip_GBps_fp32": round(4.0 * n / ((e_ms + d_ms) * 1e-3) / 1e9, 2),
+            "bits_per_coord": round(nbits / n, 4), "bits_vs_omega": round(nbits / nbits_omega, 4),
+            "encode_hbm_frac": round(alg / (e_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "decode_hbm_frac": round(alg / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def decode_accumulate_leg(q, wl, torch, args, v0, n, s, d, seed, nb, stream):
     """Decode-accumulate of k workers' streams (worker 0: the config's gradient)
     into one fp32 buffer, timed with HIP events on the launch stream. Algorithmic
@@ -136,6 +185,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--cpu-sample", type=int, default=0, help="coordinates for the oracle (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gamma", action="store_true", help="skip the Elias-gamma leg")
     ap.add_argument("--acc-streams", type=int, default=4,
                     help="streams of the decode-accumulate measurement (configs 2, 3; 0: skip)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -248,6 +298,8 @@ def main():
                      "traffic": measured_traffic(dominant),
                      "algorithmic_bytes": round(enc_bytes if dominant == "encode" else dec_bytes)},
     }
+    if not args.no_gamma:
+        res["gamma"] = gamma_leg(q, torch, args, vs[0], lay, n, s, d, seed, nb, cap, stream, nbits)
     if args.acc_streams and args.config in (2, 3) and not ragged:
         res["decode_accumulate"] = decode_accumulate_leg(q, wl, torch, args, vs[0], n, s, d, seed, nb, stream)
     if not args.no_cpu_baseline:

@@ -65,6 +65,12 @@ typedef enum {
     QSGD_ERR_UNSUPPORTED = 3
 } qsgd_status;
 
+/* Integer code of the record fields (gaps and levels). The page names "Elias
+ * recursive gamma/omega" coding; omega is the default of every call without a
+ * code argument. Elias gamma writes N as floor(log2 N) zero bits followed by N
+ * in binary (2 floor(log2 N) + 1 bits); the stream layout is otherwise the same. */
+typedef enum { QSGD_CODE_OMEGA = 0, QSGD_CODE_GAMMA = 1 } qsgd_code;
+
 /* Human-readable name of a status code (static string). */
 const char *qsgd_status_string(qsgd_status status);
 
@@ -122,6 +128,23 @@ qsgd_status qsgd_encode(const float *v, uint64_t n, uint32_t s, uint32_t d, uint
  */
 qsgd_status qsgd_decode(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
                         uint32_t s, uint32_t d, float *v_hat, hipStream_t stream);
+
+/* ---- choice of code (and of uniform or ragged buckets) in one call ----------
+ * bucket_start is the DEVICE bucket table of a ragged batch, or NULL for
+ * uniform buckets of d coordinates (then nb must be ceil(n/d)). Other arguments
+ * as in qsgd_encode / qsgd_decode; a stream must be decoded with the code it
+ * was encoded with. An unknown code is QSGD_ERR_INVALID_ARG. */
+
+/* Capacity of `out` for qsgd_encode_ex (a bound for uniform and ragged layouts
+ * alike); 0 for invalid arguments. */
+uint64_t qsgd_encode_capacity_words_ex(uint64_t n, uint64_t nb, uint32_t s, uint32_t d,
+                                       qsgd_code code);
+qsgd_status qsgd_encode_ex(const float *v, uint64_t n, const uint64_t *bucket_start, uint64_t nb,
+                           uint32_t s, uint32_t d, uint64_t seed, qsgd_code code, uint64_t *out,
+                           uint64_t *out_bits, uint64_t *bucket_bit_offsets, hipStream_t stream);
+qsgd_status qsgd_decode_ex(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
+                           const uint64_t *bucket_start, uint64_t nb, uint32_t s, uint32_t d,
+                           qsgd_code code, float *v_hat, hipStream_t stream);
 
 /* ---- decode-accumulate: the receiving side of a gradient exchange ----------
  * In data-parallel SGD every node sends its quantized gradient and each

@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "QsgdError", "lib", "num_buckets", "encode_capacity_words", "quantize", "encode",
     "decode", "RaggedLayout", "quantize_ragged", "encode_ragged", "decode_ragged",
-    "max_bucket", "max_streams", "decode_accumulate", "decode_accumulate_ragged",
+    "max_bucket", "max_streams", "decode_accumulate", "decode_accumulate_ragged", "OMEGA", "GAMMA",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +30,7 @@ _u32 = ctypes.c_uint32
 _vp = ctypes.c_void_p
 
 QSGD_OK, QSGD_ERR_INVALID_ARG, QSGD_ERR_LAUNCH, QSGD_ERR_UNSUPPORTED = 0, 1, 2, 3
+OMEGA, GAMMA = 0, 1  # integer code of the record fields (qsgd_code)
 
 
 class QsgdError(RuntimeError):
@@ -67,13 +68,18 @@ def lib():
         L.qsgd_quantize_ragged.argtypes = [_vp, _u64, _vp, _u64, _u32, _u32, _u64, _vp, _vp, _vp]
         L.qsgd_encode_ragged.argtypes = [_vp, _u64, _vp, _u64, _u32, _u32, _u64, _vp, _vp, _vp, _vp]
         L.qsgd_decode_ragged.argtypes = [_vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp, _vp]
+        L.qsgd_encode_capacity_words_ex.argtypes = [_u64, _u64, _u32, _u32, ctypes.c_int]
+        L.qsgd_encode_capacity_words_ex.restype = _u64
+        L.qsgd_encode_ex.argtypes = [_vp, _u64, _vp, _u64, _u32, _u32, _u64, ctypes.c_int, _vp, _vp, _vp, _vp]
+        L.qsgd_decode_ex.argtypes = [_vp, _vp, _u64, _vp, _u64, _u32, _u32, ctypes.c_int, _vp, _vp]
         L.qsgd_max_streams.argtypes = []
         L.qsgd_max_streams.restype = _u32
         L.qsgd_decode_accumulate.argtypes = [_vp, _vp, _u32, _u64, _u32, _u32, _vp, _vp]
         L.qsgd_decode_accumulate_ragged.argtypes = [_vp, _vp, _u32, _u64, _vp, _u64, _u32, _u32, _vp, _vp]
         for name in ("qsgd_quantize", "qsgd_encode", "qsgd_decode", "qsgd_ragged_bucket_table",
                      "qsgd_quantize_ragged", "qsgd_encode_ragged", "qsgd_decode_ragged",
-                     "qsgd_decode_accumulate", "qsgd_decode_accumulate_ragged"):
+                     "qsgd_decode_accumulate", "qsgd_decode_accumulate_ragged", "qsgd_encode_ex",
+                     "qsgd_decode_ex"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -107,8 +113,10 @@ def max_bucket() -> int:
     return int(lib().qsgd_max_bucket())
 
 
-def encode_capacity_words(n: int, s: int, d: int) -> int:
-    return int(lib().qsgd_encode_capacity_words(n, s, d))
+def encode_capacity_words(n: int, s: int, d: int, code: int = OMEGA) -> int:
+    if code == OMEGA:
+        return int(lib().qsgd_encode_capacity_words(n, s, d))
+    return int(lib().qsgd_encode_capacity_words_ex(n, num_buckets(n, d), s, d, code))
 
 
 def quantize(v: torch.Tensor, s: int, d: int, seed: int, levels=None, norms=None, stream=None):
@@ -127,12 +135,13 @@ def quantize(v: torch.Tensor, s: int, d: int, seed: int, levels=None, norms=None
 
 
 def encode(v: torch.Tensor, s: int, d: int, seed: int, out=None, out_bits=None, offsets=None,
-           stream=None):
+           stream=None, code: int = OMEGA):
     """Returns (out words, out_bits [1], bucket bit offsets [nb + 1]) as device
-    tensors (uint64 data in int64 tensors). The stream is out[: ceil(bits/64)]."""
+    tensors (uint64 data in int64 tensors). The stream is out[: ceil(bits/64)].
+    code: OMEGA (qsgd_encode) or GAMMA (qsgd_encode_ex)."""
     n = v.numel()
     nb = num_buckets(n, d)
-    cap = encode_capacity_words(n, s, d)
+    cap = encode_capacity_words(n, s, d, code)
     if cap == 0:
         raise QsgdError(QSGD_ERR_UNSUPPORTED, "qsgd_encode_capacity_words")
     if out is None:
@@ -143,21 +152,34 @@ def encode(v: torch.Tensor, s: int, d: int, seed: int, out=None, out_bits=None, 
         out_bits = torch.empty(1, dtype=torch.int64, device=v.device)
     if offsets is None:
         offsets = torch.empty(nb + 1, dtype=torch.int64, device=v.device)
-    _check(lib().qsgd_encode(_dev(v, torch.float32, "v"), n, s, d, seed,
-                             _dev(out, torch.int64, "out"), _dev(out_bits, torch.int64, "out_bits"),
-                             _dev(offsets, torch.int64, "offsets"), _stream(stream)),
-           "qsgd_encode")
+    if code == OMEGA:
+        _check(lib().qsgd_encode(_dev(v, torch.float32, "v"), n, s, d, seed,
+                                 _dev(out, torch.int64, "out"), _dev(out_bits, torch.int64, "out_bits"),
+                                 _dev(offsets, torch.int64, "offsets"), _stream(stream)),
+               "qsgd_encode")
+    else:
+        _check(lib().qsgd_encode_ex(_dev(v, torch.float32, "v"), n, None, nb, s, d, seed, code,
+                                    _dev(out, torch.int64, "out"), _dev(out_bits, torch.int64, "out_bits"),
+                                    _dev(offsets, torch.int64, "offsets"), _stream(stream)),
+               "qsgd_encode_ex")
     return out, out_bits, offsets
 
 
 def decode(words: torch.Tensor, offsets: torch.Tensor, n: int, s: int, d: int, v_hat=None,
-           stream=None):
-    """Decodes a stream written by encode back to Q_s(v) (float32 [n])."""
+           stream=None, code: int = OMEGA):
+    """Decodes a stream written by encode (with the same code) back to Q_s(v)
+    (float32 [n])."""
     if v_hat is None:
         v_hat = torch.empty(n, dtype=torch.float32, device=words.device)
-    _check(lib().qsgd_decode(_dev(words, torch.int64, "words"), _dev(offsets, torch.int64, "offsets"),
-                             n, s, d, _dev(v_hat, torch.float32, "v_hat"), _stream(stream)),
-           "qsgd_decode")
+    if code == OMEGA:
+        _check(lib().qsgd_decode(_dev(words, torch.int64, "words"), _dev(offsets, torch.int64, "offsets"),
+                                 n, s, d, _dev(v_hat, torch.float32, "v_hat"), _stream(stream)),
+               "qsgd_decode")
+    else:
+        _check(lib().qsgd_decode_ex(_dev(words, torch.int64, "words"), _dev(offsets, torch.int64, "offsets"),
+                                    n, None, num_buckets(n, d), s, d, code,
+                                    _dev(v_hat, torch.float32, "v_hat"), _stream(stream)),
+               "qsgd_decode_ex")
     return v_hat
 
 
@@ -203,8 +225,10 @@ class RaggedLayout:
         self.bucket_start_host = table
         self.bucket_start = torch.from_numpy(table.view(np.int64)).to(device)
 
-    def capacity_words(self, s: int) -> int:
-        return int(lib().qsgd_encode_capacity_words_ragged(self.n, self.nb, s, self.d))
+    def capacity_words(self, s: int, code: int = OMEGA) -> int:
+        if code == OMEGA:
+            return int(lib().qsgd_encode_capacity_words_ragged(self.n, self.nb, s, self.d))
+        return int(lib().qsgd_encode_capacity_words_ex(self.n, self.nb, s, self.d, code))
 
 
 def quantize_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, stream=None):
@@ -219,8 +243,8 @@ def quantize_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, st
 
 
 def encode_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, out=None, out_bits=None,
-                  offsets=None, stream=None):
-    cap = layout.capacity_words(s)
+                  offsets=None, stream=None, code: int = OMEGA):
+    cap = layout.capacity_words(s, code)
     if cap == 0:
         raise QsgdError(QSGD_ERR_UNSUPPORTED, "qsgd_encode_capacity_words_ragged")
     if out is None:
@@ -229,24 +253,38 @@ def encode_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, out=
         out_bits = torch.empty(1, dtype=torch.int64, device=v.device)
     if offsets is None:
         offsets = torch.empty(layout.nb + 1, dtype=torch.int64, device=v.device)
-    _check(lib().qsgd_encode_ragged(_dev(v, torch.float32, "v"), layout.n,
+    if code == OMEGA:
+        _check(lib().qsgd_encode_ragged(_dev(v, torch.float32, "v"), layout.n,
+                                        _dev(layout.bucket_start, torch.int64, "bucket_start"), layout.nb,
+                                        s, layout.d, seed, _dev(out, torch.int64, "out"),
+                                        _dev(out_bits, torch.int64, "out_bits"),
+                                        _dev(offsets, torch.int64, "offsets"), _stream(stream)),
+               "qsgd_encode_ragged")
+    else:
+        _check(lib().qsgd_encode_ex(_dev(v, torch.float32, "v"), layout.n,
                                     _dev(layout.bucket_start, torch.int64, "bucket_start"), layout.nb,
-                                    s, layout.d, seed, _dev(out, torch.int64, "out"),
+                                    s, layout.d, seed, code, _dev(out, torch.int64, "out"),
                                     _dev(out_bits, torch.int64, "out_bits"),
                                     _dev(offsets, torch.int64, "offsets"), _stream(stream)),
-           "qsgd_encode_ragged")
+               "qsgd_encode_ex")
     return out, out_bits, offsets
 
 
 def decode_ragged(words: torch.Tensor, offsets: torch.Tensor, layout: RaggedLayout, s: int,
-                  v_hat=None, stream=None):
+                  v_hat=None, stream=None, code: int = OMEGA):
     if v_hat is None:
         v_hat = torch.empty(layout.n, dtype=torch.float32, device=words.device)
-    _check(lib().qsgd_decode_ragged(_dev(words, torch.int64, "words"),
-                                    _dev(offsets, torch.int64, "offsets"), layout.n,
-                                    _dev(layout.bucket_start, torch.int64, "bucket_start"), layout.nb,
-                                    s, layout.d, _dev(v_hat, torch.float32, "v_hat"), _stream(stream)),
-           "qsgd_decode_ragged")
+    bs = _dev(layout.bucket_start, torch.int64, "bucket_start")
+    if code == OMEGA:
+        _check(lib().qsgd_decode_ragged(_dev(words, torch.int64, "words"),
+                                        _dev(offsets, torch.int64, "offsets"), layout.n, bs, layout.nb,
+                                        s, layout.d, _dev(v_hat, torch.float32, "v_hat"), _stream(stream)),
+               "qsgd_decode_ragged")
+    else:
+        _check(lib().qsgd_decode_ex(_dev(words, torch.int64, "words"), _dev(offsets, torch.int64, "offsets"),
+                                    layout.n, bs, layout.nb, s, layout.d, code,
+                                    _dev(v_hat, torch.float32, "v_hat"), _stream(stream)),
+               "qsgd_decode_ex")
     return v_hat
 
 

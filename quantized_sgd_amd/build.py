@@ -23,7 +23,7 @@ def hipcc_command(out: str = LIB, extra=()):
         "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-fno-strict-aliasing",
         "-fno-gpu-flush-denormals-to-zero",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-function",
+        "-Wall", "-Wshadow", "-Wno-unused-function",
         "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
         *extra, "-o", out, *SOURCES,
     ]

@@ -31,6 +31,15 @@ uint32_t host_omega_len(uint64_t N) {  // Elias omega codeword length
     return L;
 }
 
+uint32_t host_code_len(uint32_t code, uint64_t N) {  // codeword length of a record field
+    if (code == QSGD_CODE_GAMMA) {
+        uint32_t b = 0;
+        for (uint64_t x = N; x; x >>= 1) ++b;
+        return 2 * b - 1;
+    }
+    return host_omega_len(N);
+}
+
 // Buckets per tile: whole buckets whose coordinates fit 4096 slots after the
 // tile start is rounded down to a multiple of 16 (no rounding when every bucket
 // start is a multiple of 16).
@@ -51,13 +60,16 @@ struct EncodePlan {
     size_t lds_bytes = 0;
 };
 
-EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool aligned_starts) {
+EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool aligned_starts,
+                     uint32_t code = QSGD_CODE_OMEGA) {
     EncodePlan p;
     p.K = buckets_per_tile(d, aligned_starts);
     if (p.K == 0) return p;
     p.ntiles = (nb + p.K - 1) / p.K;
-    const uint64_t Ls = host_omega_len(s);
-    // stream bound: 32 nb + n (2.5 + Ls) bits, rounded up to words, plus one
+    const uint64_t Ls = host_code_len(code, s);
+    // stream bound: 32 nb + n (2.5 + Ls) bits (both codes spend at most 1.5 g
+    // bits on a gap g, so a bucket's gap codes take at most 1.5 times its
+    // length), rounded up to words, plus one
     const uint64_t twice_bits = 64 * nb + n * (5 + 2 * Ls);
     p.stream_words = (twice_bits + 127) / 128 + 1;
     p.stream_words = (p.stream_words + 31) & ~(uint64_t)31;
@@ -154,9 +166,10 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
 
 qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb, uint32_t s,
                         uint32_t d, uint64_t seed, uint64_t *out, uint64_t *out_bits,
-                        uint64_t *offsets, hipStream_t stream) {
+                        uint64_t *offsets, hipStream_t stream, uint32_t code = QSGD_CODE_OMEGA) {
     qsgd_status st = check_common(v, s, d);
     if (st != QSGD_OK) return st;
+    if (code > QSGD_CODE_GAMMA) return QSGD_ERR_INVALID_ARG;
     if (!out_bits || !offsets) return QSGD_ERR_INVALID_ARG;
     if (n == 0 || nb == 0) {
         hipLaunchKernelGGL(encode_empty_kernel, dim3(1), dim3(64), 0, stream, out_bits, offsets);
@@ -164,7 +177,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     }
     if (!v || !out || !aligned16(out)) return QSGD_ERR_INVALID_ARG;
     const bool ragged = bstart != nullptr;
-    EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0));
+    EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0), code);
     if (p.K == 0) return QSGD_ERR_UNSUPPORTED;
     if (p.lds_bytes > kMaxLds || p.ntiles >= (1ull << 32)) return QSGD_ERR_UNSUPPORTED;
     QsgdParams P{};
@@ -175,6 +188,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     P.tile_bits = reinterpret_cast<uint32_t *>(P.slots + p.slot_region_words);
     P.run_bits = P.slots + p.slot_region_words + (p.ntiles + 1) / 2;
     P.obuf_words = p.obuf_words;
+    P.code = code;
     // pass 1 grid: at most the resident workgroups (and kMaxRuns), each taking a
     // run of consecutive tiles
     auto runs_for = [&](uint32_t resident) {
@@ -216,9 +230,10 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
 // streams in[k] / offsets[k] to v_hat in stream order.
 qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offsets, uint32_t nstreams,
                         bool acc, uint64_t n, const uint64_t *bstart, uint64_t nb, uint32_t s,
-                        uint32_t d, float *v_hat, hipStream_t stream) {
+                        uint32_t d, float *v_hat, hipStream_t stream, uint32_t code = QSGD_CODE_OMEGA) {
     qsgd_status st = check_common(nullptr, s, d);
     if (st != QSGD_OK) return st;
+    if (code > QSGD_CODE_GAMMA) return QSGD_ERR_INVALID_ARG;
     if (nstreams > kMaxStreams || (nstreams && (!in || !offsets))) return QSGD_ERR_INVALID_ARG;
     if (n == 0 || nb == 0 || nstreams == 0) return QSGD_OK;
     for (uint32_t k = 0; k < nstreams; ++k)
@@ -255,12 +270,18 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
         const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, resident_blocks(kernel, lds, kDecWG));
         hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kDecWG), lds, stream, D);
     };
+    // accumulation is served for omega streams; the code is a kernel parameter so
+    // that each kernel holds one record decoder
     if (acc) {
-        if (bstart) lds_out ? launch(decode_kernel<true, true, true>) : launch(decode_kernel<true, false, true>);
-        else lds_out ? launch(decode_kernel<false, true, true>) : launch(decode_kernel<false, false, true>);
+        if (code != QSGD_CODE_OMEGA) return QSGD_ERR_UNSUPPORTED;
+        if (bstart) lds_out ? launch(decode_kernel<true, true, true, 0>) : launch(decode_kernel<true, false, true, 0>);
+        else lds_out ? launch(decode_kernel<false, true, true, 0>) : launch(decode_kernel<false, false, true, 0>);
+    } else if (code == QSGD_CODE_GAMMA) {
+        if (bstart) lds_out ? launch(decode_kernel<true, true, false, 1>) : launch(decode_kernel<true, false, false, 1>);
+        else lds_out ? launch(decode_kernel<false, true, false, 1>) : launch(decode_kernel<false, false, false, 1>);
     } else {
-        if (bstart) lds_out ? launch(decode_kernel<true, true, false>) : launch(decode_kernel<true, false, false>);
-        else lds_out ? launch(decode_kernel<false, true, false>) : launch(decode_kernel<false, false, false>);
+        if (bstart) lds_out ? launch(decode_kernel<true, true, false, 0>) : launch(decode_kernel<true, false, false, 0>);
+        else lds_out ? launch(decode_kernel<false, true, false, 0>) : launch(decode_kernel<false, false, false, 0>);
     }
     return launch_status();
 }
@@ -333,6 +354,33 @@ qsgd_status qsgd_decode(const uint64_t *in, const uint64_t *bucket_bit_offsets, 
 }
 
 uint32_t qsgd_max_streams(void) { return kMaxStreams; }
+
+uint64_t qsgd_encode_capacity_words_ex(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, qsgd_code code) {
+    if (d == 0 || s == 0 || (uint32_t)code > QSGD_CODE_GAMMA) return 0;
+    if (nb == 0) return 1;
+    // the larger of the two tilings (bucket starts on multiples of 16 or not;
+    // buckets of more than 4081 coordinates only tile with aligned starts)
+    EncodePlan a = make_plan(n, nb, s, d, true, code), b = make_plan(n, nb, s, d, false, code);
+    const uint64_t ca = a.K ? a.stream_words + a.ws_words : 0, cb = b.K ? b.stream_words + b.ws_words : 0;
+    return std::max(ca, cb);
+}
+
+qsgd_status qsgd_encode_ex(const float *v, uint64_t n, const uint64_t *bucket_start, uint64_t nb,
+                           uint32_t s, uint32_t d, uint64_t seed, qsgd_code code, uint64_t *out,
+                           uint64_t *out_bits, uint64_t *bucket_bit_offsets, hipStream_t stream) {
+    if (!bucket_start && nb != qsgd_num_buckets(n, d)) return QSGD_ERR_INVALID_ARG;
+    if (bucket_start && nb == 0 && n != 0) return QSGD_ERR_INVALID_ARG;
+    return encode_impl(v, n, bucket_start, nb, s, d, seed, out, out_bits, bucket_bit_offsets, stream,
+                       (uint32_t)code);
+}
+
+qsgd_status qsgd_decode_ex(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
+                           const uint64_t *bucket_start, uint64_t nb, uint32_t s, uint32_t d,
+                           qsgd_code code, float *v_hat, hipStream_t stream) {
+    if (!bucket_start && nb != qsgd_num_buckets(n, d)) return QSGD_ERR_INVALID_ARG;
+    return decode_impl(&in, &bucket_bit_offsets, 1, false, n, bucket_start, nb, s, d, v_hat, stream,
+                       (uint32_t)code);
+}
 
 qsgd_status qsgd_decode_accumulate(const uint64_t *const *in, const uint64_t *const *bucket_bit_offsets,
                                    uint32_t k, uint64_t n, uint32_t s, uint32_t d, float *acc,

@@ -109,13 +109,39 @@ constexpr int lut_omega(LutCursor &c) {
     }
 }
 
+// Elias gamma (Elias 1975) for values up to 16: z zero bits, then the z + 1 bits
+// of N from its leading 1.
+constexpr int lut_gamma(LutCursor &c) {
+    int z = 0;
+    while (true) {
+        const int b = lut_take(c, 1);
+        if (b < 0) return -1;
+        if (b == 1) break;
+        if (++z > 4) return -1;
+    }
+    int N = 1;
+    for (int i = 0; i < z; ++i) {
+        const int b = lut_take(c, 1);
+        if (b < 0) return -1;
+        N = (N << 1) | b;
+    }
+    return N > 16 ? -1 : N;
+}
+
+// A record field (gap or level) in the code of the stream: omega or gamma.
+template <int CODE>
+constexpr int lut_field(LutCursor &c) {
+    return CODE ? lut_gamma(c) : lut_omega(c);
+}
+
 // One record at the cursor: (gap - 1) | level byte << 4, or -1.
+template <int CODE>
 constexpr int lut_record(LutCursor &c) {
-    const int gap = lut_omega(c);
+    const int gap = lut_field<CODE>(c);
     if (gap <= 0) return -1;
     const int sg = lut_take(c, 1);
     if (sg < 0) return -1;
-    const int k = lut_omega(c);
+    const int k = lut_field<CODE>(c);
     if (k <= 0) return -1;
     return (gap - 1) | (((sg << 7) | k) << 4);
 }
@@ -126,17 +152,18 @@ constexpr uint32_t reverse_bits(uint32_t v, int n) {
     return r;
 }
 
+template <int CODE>
 constexpr RecordLut make_record_lut() {
     RecordLut t{};
     for (uint32_t i = 0; i < (1u << kLutBits); ++i) {
         LutCursor c{reverse_bits(i, kLutBits), 0};  // the cursor reads the first bit from the top
         uint32_t e = 0;
-        const int r1 = lut_record(c);
+        const int r1 = lut_record<CODE>(c);
         if (r1 >= 0) {
             const uint32_t l1 = (uint32_t)c.pos;
             e = l1 | (l1 << 4) | ((uint32_t)r1 << 8);
             LutCursor c2 = c;
-            const int r2 = lut_record(c2);
+            const int r2 = lut_record<CODE>(c2);
             if (r2 >= 0) e = (e & ~15u) | (uint32_t)c2.pos | ((uint32_t)r2 << 20);
         }
         t.e[i] = e;
@@ -144,7 +171,9 @@ constexpr RecordLut make_record_lut() {
     return t;
 }
 
-__constant__ RecordLut kRecordLut = make_record_lut();
+// record tables of the omega (code 0) and gamma (code 1) streams
+__constant__ RecordLut kRecordLut = make_record_lut<0>();
+__constant__ RecordLut kRecordLutGamma = make_record_lut<1>();
 
 // ---- bit access -----------------------------------------------------------
 // Bit positions fit 32 bits (a group spans fewer than 2^31 bits: buckets of at
@@ -184,7 +213,10 @@ struct Bits {
     }
 };
 
+// CODE: integer code of the record fields, 0 Elias omega, 1 Elias gamma.
+template <int CODE>
 struct RecordCtx {
+    static constexpr int code = CODE;
     const uint32_t *lut;
     uint32_t gbits, kbits, s;
 };
@@ -207,18 +239,30 @@ __device__ __forceinline__ uint32_t omega_at(const Bits<LDS> &r, uint32_t &p, ui
     }
 }
 
-// One record omega(gap) | sign | omega(k) at bit p by general omega decoding.
+// General Elias gamma decoding from bit p: returns N and advances p, or 0 if N
+// has more than maxbits (<= 25) binary digits.
+template <bool LDS>
+__device__ __forceinline__ uint32_t gamma_at(const Bits<LDS> &r, uint32_t &p, uint32_t maxbits) {
+    const uint32_t w = (uint32_t)r.at(p);
+    const uint32_t z = w ? (uint32_t)__builtin_ctz(w) : 32u;  // zero bits before the leading 1
+    if (z + 1u > maxbits) return 0;
+    const uint32_t v = (uint32_t)r.at(p + z);
+    p += 2u * z + 1u;
+    return __builtin_bitreverse32(v) >> (31u - z);
+}
+
+// One record c(gap) | sign | c(k) at bit p by general decoding of the code c.
 // Returns the position after it, or 0 if it does not parse (a record never
 // ends at 0): a group longer than the bound, or k > s.
-template <bool LDS>
-__device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const RecordCtx &x, uint32_t p,
+template <bool LDS, class X>
+__device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const X &x, uint32_t p,
                                                 uint32_t &gap, uint32_t &neg, uint32_t &k) {
     uint32_t q = p;
-    gap = omega_at(r, q, x.gbits);
+    gap = X::code ? gamma_at(r, q, x.gbits) : omega_at(r, q, x.gbits);
     if (gap == 0) return 0;
     neg = (uint32_t)r.at(q) & 1u;
     q += 1u;
-    k = omega_at(r, q, x.kbits);
+    k = X::code ? gamma_at(r, q, x.kbits) : omega_at(r, q, x.kbits);
     if (k == 0 || k > x.s) return 0;
     return q;
 }
@@ -229,15 +273,15 @@ __device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const Record
 // speculative chain only has to be a deterministic function of its start. A
 // two-record entry is the same as two one-record steps, so every walker of a
 // chain visits the same positions.
-template <bool LDS>
-__device__ __forceinline__ uint32_t lut_at(const Bits<LDS> &r, const RecordCtx &x, uint32_t p) {
+template <bool LDS, class X>
+__device__ __forceinline__ uint32_t lut_at(const Bits<LDS> &r, const X &x, uint32_t p) {
     return x.lut[(uint32_t)r.at(p) & ((1u << kLutBits) - 1u)];
 }
 
 // One step of a chain: past the record at p adding its gap to sum, or one bit
 // on if no record parses there.
-template <bool LDS>
-__device__ __forceinline__ void chain_step(const Bits<LDS> &r, const RecordCtx &x, uint32_t &p,
+template <bool LDS, class X>
+__device__ __forceinline__ void chain_step(const Bits<LDS> &r, const X &x, uint32_t &p,
                                            uint32_t &sum) {
     const uint32_t e = lut_at(r, x, p);
     if (e & 15u) {
@@ -253,8 +297,8 @@ __device__ __forceinline__ void chain_step(const Bits<LDS> &r, const RecordCtx &
 
 // One record of the true chain at p: its end (0 if it does not parse), gap and
 // level byte sign << 7 | k (k <= 127 when the caller uses the byte).
-template <bool LDS>
-__device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const RecordCtx &x, uint32_t p,
+template <bool LDS, class X>
+__device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const X &x, uint32_t p,
                                               uint32_t &gap, uint32_t &neg, uint32_t &k) {
     const uint32_t e = lut_at(r, x, p);
     if (e & 15u) {
@@ -285,8 +329,8 @@ constexpr int kGuessSteps = QSGD_GUESS_STEPS;
 // bit on instead of decoding a long record. follow_chain notes no position
 // during these steps, so another chain can only meet this one where it follows
 // the exact rule, and both continue alike from there.
-template <bool LDS>
-__device__ __forceinline__ void guess_steps(const Bits<LDS> &r, const RecordCtx &x, uint32_t &p,
+template <bool LDS, class X>
+__device__ __forceinline__ void guess_steps(const Bits<LDS> &r, const X &x, uint32_t &p,
                                             uint32_t sn, uint32_t &sum) {
 #pragma unroll
     for (int i = 0; i < kGuessSteps; ++i) {
@@ -310,8 +354,8 @@ __device__ __forceinline__ void guess_steps(const Bits<LDS> &r, const RecordCtx 
 // table entry is exact when cum_top < 256). Two-record table entries advance
 // two records at once when the second starts before the current limit (the
 // end of the 64-bit mark word being filled, or sn).
-template <bool LDS, bool MARK>
-__device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const RecordCtx &x, uint32_t start,
+template <bool LDS, bool MARK, class X>
+__device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const X &x, uint32_t start,
                                                  uint32_t sn, uint32_t &ga, uint64_t &own0,
                                                  uint64_t &own1, uint8_t *cum, uint32_t &cum_top,
                                                  bool guess = false) {
@@ -398,8 +442,8 @@ __device__ __forceinline__ bool meet_stop(uint32_t p, uint32_t sn, uint32_t E, u
     return false;
 }
 
-template <bool LDS>
-__device__ __forceinline__ bool extend_chain(const Bits<LDS> &r, const RecordCtx &x, uint32_t x0,
+template <bool LDS, class X>
+__device__ __forceinline__ bool extend_chain(const Bits<LDS> &r, const X &x, uint32_t x0,
                                              uint32_t sn, uint32_t E, uint64_t nxt0, uint64_t nxt1,
                                              uint32_t &y, uint32_t &gb) {
     uint32_t p = x0, sum = 0;
@@ -509,7 +553,7 @@ __device__ __forceinline__ void wave_sync() {
 // buffer `lvl` (index = coordinate - lbase, cleared here) and each bucket's
 // RN64(norm / s) to ebs[team]; otherwise every lane writes (ACC: adds) its own
 // output range with a QuadWriter.
-template <bool RAGGED, bool LDS_IN, bool LDS_OUT, bool ACC>
+template <bool RAGGED, bool LDS_IN, bool LDS_OUT, bool ACC, int CODE>
 __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64_t *offs,
                                              const uint32_t *lut,
                                              const Bits<LDS_IN> &r, uint64_t gbit, uint64_t b0,
@@ -543,7 +587,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
         }
     }
     if (LDS_OUT && tactive && q == 0) ebs[team] = e_b;
-    const RecordCtx x{lut, tactive ? bitlen32((uint32_t)len) : 1u, bitlen32(D.s), D.s};
+    const RecordCtx<CODE> x{lut, tactive ? bitlen32((uint32_t)len) : 1u, bitlen32(D.s), D.s};
     const uint32_t P0 = A + 32u;
     const uint32_t seg = nl ? ((E - P0) + nl - 1u) / nl : 0u;
     const bool act = q < nl;
@@ -746,7 +790,7 @@ constexpr size_t decode_lds_bytes() { return (size_t)kDecWaves * kWaveLdsBytes +
 // out = ((out + v_hat_0) + v_hat_1) + ...; the wave takes all streams of a
 // group in turn, reading, adding to and writing back the group's outputs once
 // per stream.
-template <bool RAGGED, bool LDS_OUT, bool ACC>
+template <bool RAGGED, bool LDS_OUT, bool ACC, int CODE>
 __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     extern __shared__ __align__(16) uint64_t dsmem[];
     // record table after the waves' regions (a constant offset: folds into the
@@ -754,7 +798,7 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     uint32_t *lut = reinterpret_cast<uint32_t *>(reinterpret_cast<unsigned char *>(dsmem) +
                                                  (size_t)kDecWaves * kWaveLdsBytes);
     {
-        const uint4 *src = reinterpret_cast<const uint4 *>(kRecordLut.e);
+        const uint4 *src = reinterpret_cast<const uint4 *>(CODE ? kRecordLutGamma.e : kRecordLut.e);
         uint4 *dst = reinterpret_cast<uint4 *>(lut);
         for (uint32_t i = threadIdx.x; i < sizeof(RecordLut) / 16; i += kDecWG) dst[i] = src[i];
     }
@@ -800,10 +844,10 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
             Bits<false> rg{reinterpret_cast<const uint32_t *>(in + w0),
                            (uint32_t)(2 * (total_words - w0)) - 1u};
             if (in_lds)
-                decode_group<RAGGED, true, LDS_OUT, ACC>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs, lbase,
+                decode_group<RAGGED, true, LDS_OUT, ACC, CODE>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs, lbase,
                                                          nclear16);
             else
-                decode_group<RAGGED, false, LDS_OUT, ACC>(D, offs, lut, rg, w0 * 64, b0, b1, lvl, ebs,
+                decode_group<RAGGED, false, LDS_OUT, ACC, CODE>(D, offs, lut, rg, w0 * 64, b0, b1, lvl, ebs,
                                                           lbase, nclear16);
             if (LDS_OUT) {
                 wave_sync();

@@ -77,6 +77,18 @@ __device__ __forceinline__ uint64_t omega_code(uint32_t N, uint32_t &len) {
     return code;
 }
 
+// Elias gamma codeword of N >= 1 (Elias 1975), right-aligned: floor(log2 N) zero
+// bits, then N in binary; that is the value N in 2 floor(log2 N) + 1 bits.
+__device__ __forceinline__ uint64_t gamma_code(uint32_t N, uint32_t &len) {
+    len = 2u * (32u - (uint32_t)__clz(N)) - 1u;
+    return N;
+}
+
+// Codeword of a record field (gap or level): Elias omega (code 0) or gamma (1).
+__device__ __forceinline__ uint64_t field_code(uint32_t code, uint32_t N, uint32_t &len) {
+    return code ? gamma_code(N, len) : omega_code(N, len);
+}
+
 __device__ __forceinline__ uint32_t omega_len(uint32_t N) {
     uint32_t L = 1;
     uint32_t m = N;

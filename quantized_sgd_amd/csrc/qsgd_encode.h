@@ -9,7 +9,8 @@
 // workgroup ever waits for another, and publishes their total length):
 //   1. load v once from HBM, per-bucket norms, Philox rounding (qsgd_front.h);
 //   2. each thread looks up the code of every coordinate's record -- the 32-bit
-//      norm at a bucket start, and omega(gap) | sign | omega(k) per non-zero --
+//      norm at a bucket start, and c(gap) | sign | c(k) per non-zero, c the
+//      Elias omega code or (the page names "gamma/omega") the gamma code --
 //      in a table of all records with gap <= 16 and k <= s (gaps inside one
 //      thread's 16 coordinates never exceed 16) and sums their lengths. The gap
 //      of a thread's first non-zero, when its origin lies in an earlier thread,
@@ -30,7 +31,7 @@
 namespace qsgd {
 
 // Record code table for s <= kTabS: entry (code << 5) | length of
-// omega(g) | sign | omega(k) for g in [0, 16] (g = 0: no gap code) and k in
+// c(g) | sign | c(k) (c: the record fields' code; at most 23 bits) for g in [0, 16] (g = 0: no gap code) and k in
 // [0, s] (k = 0: no record, entry 0). Index ((k * 17 + g) << 1) | sign, which
 // needs no integer multiply (k * 17 = (k << 4) + k).
 constexpr uint32_t kTabS = 64;
@@ -42,7 +43,7 @@ __device__ __forceinline__ uint32_t code_index(uint32_t g, uint32_t k, uint32_t 
     return ((((k << 4) + k) + g) << 1) | neg;
 }
 
-__device__ inline void build_code_table(uint32_t *rt, uint32_t s) {
+__device__ inline void build_code_table(uint32_t *rt, uint32_t s, uint32_t fcode) {
     const uint32_t n = code_table_entries(s);
     for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
         const uint32_t neg = i & 1u;
@@ -51,12 +52,12 @@ __device__ inline void build_code_table(uint32_t *rt, uint32_t s) {
         uint32_t e = 0;
         if (k) {
             uint32_t Lk;
-            const uint64_t kc = omega_code(k, Lk);
+            const uint64_t kc = field_code(fcode, k, Lk);
             uint64_t code = ((uint64_t)neg << Lk) | kc;
             uint32_t len = Lk + 1;
             if (g) {
                 uint32_t Lg;
-                const uint64_t gc = omega_code(g, Lg);
+                const uint64_t gc = field_code(fcode, g, Lg);
                 code |= gc << len;
                 len += Lg;
             }
@@ -162,7 +163,7 @@ __global__ void encode_empty_kernel(uint64_t *out_bits, uint64_t *offsets) {
 // arithmetic path. g = 0 means "no gap code" (resolved later).
 template <bool TABLE>
 __device__ __forceinline__ uint32_t record_entry(const uint32_t *rt, uint32_t g, uint32_t k,
-                                                 uint32_t neg, uint64_t &code) {
+                                                 uint32_t neg, uint64_t &code, uint32_t fcode) {
     if (TABLE) {
         const uint32_t e = rt[code_index(g, k, neg)];
         code = e >> 5;
@@ -170,16 +171,16 @@ __device__ __forceinline__ uint32_t record_entry(const uint32_t *rt, uint32_t g,
     }
     if (k == 0) { code = 0; return 0; }
     uint32_t Lk;
-    const uint64_t kc = omega_code(k, Lk);
+    const uint64_t kc = field_code(fcode, k, Lk);
     code = ((uint64_t)neg << Lk) | kc;
     uint32_t len = Lk + 1;
     if (g) {
         uint32_t Lg;
-        const uint64_t gc = omega_code(g, Lg);
+        const uint64_t gc = field_code(fcode, g, Lg);
         code |= gc << len;
         len += Lg;
     }
-    return len;  // <= 11 + 1 + 36 = 48 bits
+    return len;  // omega: <= 11 + 1 + 36 = 48 bits; gamma: <= 9 + 1 + 49 = 59
 }
 
 template <bool RAGGED, bool TABLE>
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
 
     const uint32_t rt_entries = TABLE ? code_table_entries(P.s) : 0u;
     EncodeLds L = carve_encode_lds(smem, P, rt_entries);
-    if (TABLE) build_code_table(L.rt, P.s);
+    if (TABLE) build_code_table(L.rt, P.s, P.code);
     const int j = (int)threadIdx.x;
     const int lane = lane_id();
     // the wave index as a scalar, so that branches on it are uniform to the compiler
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
             const uint32_t k = lv.k[q];
             const uint32_t g = have ? (uint32_t)(x - prev) : 0u;
             uint64_t code;
-            const uint32_t len = record_entry<TABLE>(L.rt, g, k, (lv.neg >> q) & 1u, code);
+            const uint32_t len = record_entry<TABLE>(L.rt, g, k, (lv.neg >> q) & 1u, code, P.code);
             if (TABLE) ec[q] = ((uint32_t)code << 5) | len;
             else { ec[q] = len; ecx[TABLE ? 0 : q] = code; }
             r += len;
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
         mex = mex > mpre ? mex : mpre;
         uint32_t Lp = 0;
         uint64_t pc = 0;
-        if (pendx >= 0) pc = omega_code((uint32_t)(pendx - mex), Lp);
+        if (pendx >= 0) pc = field_code(P.code, (uint32_t)(pendx - mex), Lp);
         const uint32_t bits = r + Lp;
 
         // ---- tile scan of bit counts ----
@@ -450,7 +451,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
     uint32_t *rt = reinterpret_cast<uint32_t *>(smem + align16((size_t)P.obuf_words * 8));
     float *pbuf = reinterpret_cast<float *>(smem + align16((size_t)P.obuf_words * 8) +
                                             align16((size_t)code_table_entries(P.s) * 4));
-    build_code_table(rt, P.s);
+    build_code_table(rt, P.s, P.code);
     const int j = (int)threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
@@ -554,7 +555,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         mex = mex > mpre ? mex : mpre;
         uint32_t Lp = 0;
         uint64_t pc = 0;
-        if (pendx >= 0) pc = omega_code((uint32_t)(pendx - mex), Lp);
+        if (pendx >= 0) pc = field_code(P.code, (uint32_t)(pendx - mex), Lp);
         const uint32_t bits = r + Lp;
 
         // ---- tile scan of bit counts ----

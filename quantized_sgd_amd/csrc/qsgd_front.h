@@ -37,6 +37,7 @@ struct QsgdParams {
     uint64_t *run_bits;    // [gridDim.x] total bits of each workgroup's run of tiles
     uint32_t obuf_words;   // words of a tile's bit string bound (+1 spare)
     uint32_t run, rem;     // workgroup b takes run_first(b) .. run_first(b + 1) - 1
+    uint32_t code;         // integer code of gaps and levels: 0 Elias omega, 1 Elias gamma
 };
 
 // Runs of consecutive tiles: the first `rem` workgroups take run + 1 tiles, the

@@ -31,32 +31,33 @@ def bucket_table(n, d, seg_len):
     return oracle.ragged_buckets(seg_len, d)
 
 
-def gpu_run(v: np.ndarray, s: int, d: int, seed: int, seg_len=None):
+def gpu_run(v: np.ndarray, s: int, d: int, seed: int, seg_len=None, code=oracle.OMEGA):
     vd = to_dev(v)
     if seg_len is None:
         lev, nrm = q.quantize(vd, s, d, seed)
-        out, bits, offs = q.encode(vd, s, d, seed)
+        out, bits, offs = q.encode(vd, s, d, seed, code=code)
         torch.cuda.synchronize()
         nbits = int(bits.item())
         words = out[: (nbits + 63) // 64]
-        vh = q.decode(out, offs, v.size, s, d)
+        vh = q.decode(out, offs, v.size, s, d, code=code)
     else:
         lay = q.RaggedLayout(seg_len, d)
         lev, nrm = q.quantize_ragged(vd, lay, s, seed)
-        out, bits, offs = q.encode_ragged(vd, lay, s, seed)
+        out, bits, offs = q.encode_ragged(vd, lay, s, seed, code=code)
         torch.cuda.synchronize()
         nbits = int(bits.item())
         words = out[: (nbits + 63) // 64]
-        vh = q.decode_ragged(out, offs, lay, s)
+        vh = q.decode_ragged(out, offs, lay, s, code=code)
     torch.cuda.synchronize()
     return dict(levels=lev.cpu().numpy(), norms=nrm.cpu().numpy(), words=u64(words),
                 offsets=u64(offs), bits=nbits, v_hat=vh.cpu().numpy(), out=out)
 
 
-def check_parity(v: np.ndarray, s: int, d: int, seed: int, seg_len=None, g=None):
-    """Full element-by-element parity of quantize, encode and decode."""
+def check_parity(v: np.ndarray, s: int, d: int, seed: int, seg_len=None, g=None, code=oracle.OMEGA):
+    """Full element-by-element parity of quantize, encode and decode (code: the
+    integer code of the record fields)."""
     if g is None:
-        g = gpu_run(v, s, d, seed, seg_len)
+        g = gpu_run(v, s, d, seed, seg_len, code)
     bst = bucket_table(v.size, d, seg_len)
     # norms
     on = oracle.bucket_norms(v, bst)
@@ -68,13 +69,13 @@ def check_parity(v: np.ndarray, s: int, d: int, seed: int, seg_len=None, g=None)
     olev, _ = oracle.quantize(v, bst, s, seed, norms=gn)
     assert np.array_equal(g["levels"], olev), np.flatnonzero(g["levels"] != olev)[:10]
     # stream given the GPU norms
-    words, offs, nbits = oracle.encode(olev, gn, bst, s)
+    words, offs, nbits = oracle.encode(olev, gn, bst, s, code)
     assert g["bits"] == nbits
     assert np.array_equal(g["offsets"], offs)
     assert np.array_equal(g["words"], words), np.flatnonzero(g["words"] != words)[:10]
     # decode
     want = oracle.dequantize(olev, gn, bst, s)
     assert np.array_equal(g["v_hat"].view(np.uint32), want.view(np.uint32))
-    rc, ovh = oracle.decode(words, offs, bst, s)
+    rc, ovh = oracle.decode(words, offs, bst, s, code)
     assert rc == oracle.OK and np.array_equal(ovh.view(np.uint32), want.view(np.uint32))
     return g, dict(norms_exact=int(np.sum(gn == on)), nb=len(on))

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(q.LIB_PATH)
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     for name in names:
         assert hasattr(lib, name), name
 
@@ -67,14 +67,26 @@ def test_decode_accumulate_argument_checks():
     assert lib.qsgd_decode_accumulate(addr, addr, 2, 100, 4, 16, 18, None) == 1    # acc not 16-byte aligned
 
 
+def test_code_choice_argument_checks():
+    # host-side rejections of the code-selecting calls (nothing is enqueued)
+    lib = q.lib()
+    assert lib.qsgd_encode_capacity_words_ex(1000, 2, 4, 512, 2) == 0          # unknown code
+    assert lib.qsgd_encode_capacity_words_ex(1000, 2, 4, 512, q.GAMMA) > 0
+    assert lib.qsgd_encode_ex(16, 1000, None, 3, 4, 512, 1, q.GAMMA, 16, 16, 16, None) == 1  # nb != ceil(n/d)
+    assert lib.qsgd_encode_ex(16, 1000, None, 2, 4, 512, 1, 7, 16, 16, 16, None) == 1        # unknown code
+    assert lib.qsgd_decode_ex(16, 16, 1000, None, 3, 4, 512, q.GAMMA, 16, None) == 1        # nb != ceil(n/d)
+    assert lib.qsgd_decode_ex(16, 16, 1000, None, 2, 4, 512, 9, 16, None) == 1              # unknown code
+
+
 def test_capacity_bounds_oracle_streams():
     # the capacity helper bounds the worst case; check it against oracle streams
     for n, d, s in [(4096, 4096, 64), (5000, 1, 1 << 24), (10000, 7, 3), (20000, 512, 16)]:
-        cap = q.encode_capacity_words(n, s, d)
-        v = np.full(n, 1.0, np.float32)
         bst = oracle.uniform_buckets(n, d)
-        _, _, _, _, nbits = oracle.compress(v, bst, s, 1)
-        assert cap * 64 > nbits
+        for code in (oracle.OMEGA, oracle.GAMMA):
+            cap = q.encode_capacity_words(n, s, d, code)
+            for v in (np.full(n, 1.0, np.float32), np.random.default_rng(n).standard_normal(n).astype(np.float32)):
+                _, _, _, _, nbits = oracle.compress(v, bst, s, 1, code=code)
+                assert cap * 64 > nbits
     assert q.encode_capacity_words(100, 4, 5000) == 0  # d beyond the tile: unsupported
     assert q.max_bucket() == 4096
 
