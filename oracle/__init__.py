@@ -64,6 +64,7 @@ def lib():
         L.or_ragged_buckets.argtypes = [_u64p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]
         L.or_ragged_buckets.restype = ctypes.c_uint64
         L.or_bucket_norms.argtypes = [_f32p, _u64p, ctypes.c_uint64, _f32p]
+        L.or_bucket_max_norms.argtypes = [_f32p, _u64p, ctypes.c_uint64, _f32p]
         L.or_quantize.argtypes = [_f32p, _u64p, ctypes.c_uint64, ctypes.c_uint32,
                                   ctypes.c_uint64, ctypes.c_void_p, _i32p, _f32p]
         L.or_quantize.restype = ctypes.c_int
@@ -151,6 +152,16 @@ def bucket_norms(v, bstart) -> np.ndarray:
     out = np.zeros(nb, dtype=np.float32)
     lib().or_bucket_norms(_p(v, _f32p), _p(bstart, _u64p), nb, _p(out, _f32p))
     return out
+
+
+def bucket_max_norms(v, bstart) -> np.ndarray:
+    """max|v_i| per bucket (the QSGDinf reading's scale)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    bstart = np.ascontiguousarray(bstart, dtype=np.uint64)
+    nb = len(bstart) - 1
+    out = np.zeros(max(nb, 1), dtype=np.float32)
+    lib().or_bucket_max_norms(_p(v, _f32p), _p(bstart, _u64p), nb, _p(out, _f32p))
+    return out[:nb]
 
 
 def quantize(v, bstart, s: int, seed: int, norms=None, u24=None):

@@ -165,6 +165,22 @@ void or_bucket_norms(const float *v, const uint64_t *bstart, uint64_t nb, float 
     for (uint64_t b = 0; b < nb; ++b) norms[b] = bucket_norm(v, bstart[b], bstart[b + 1]);
 }
 
+/* max_i |v_i| of each bucket: the scale of the reading of the heuristic
+ * variant that page "NUQSGD: Provably Communication-efficient Data-parallel SGD
+ * via Nonuniform Quantization" (abstract) names QSGDinf -- the infinity norm in
+ * place of ||v||_2. Exact (a value of the input). Quantizing with these norms
+ * given (or_quantize's given_norms) is that variant. */
+void or_bucket_max_norms(const float *v, const uint64_t *bstart, uint64_t nb, float *norms) {
+    for (uint64_t b = 0; b < nb; ++b) {
+        float m = 0.0f;
+        for (uint64_t i = bstart[b]; i < bstart[b + 1]; ++i) {
+            float a = fabsf(v[i]);
+            if (a > m) m = a;
+        }
+        norms[b] = m;
+    }
+}
+
 /* Q_s on one coordinate, in the page's order: l = floor(s|v|/||v||),
  * p = s|v|/||v|| - l, round up to l + 1 with probability p. The ratio
  * s|v|/||v|| is evaluated as RN32(|v| * RN64(s / ||v||)); the uniform is

@@ -76,6 +76,9 @@ uint64_t or_ragged_buckets(const uint64_t *seg_len, uint64_t nseg, uint64_t d,
 
 /* Bucket norms in fp64, index order. */
 void or_bucket_norms(const float *v, const uint64_t *bstart, uint64_t nb, float *norms);
+/* Bucket max-norms max|v_i| (the reading of the named variant QSGDinf; pass them
+ * as given_norms to or_quantize). */
+void or_bucket_max_norms(const float *v, const uint64_t *bstart, uint64_t nb, float *norms);
 
 /* Stochastic quantization. If given_norms is non-NULL those norms are used in
  * place of the computed ones (to condition on another implementation's norms).
