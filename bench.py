@@ -91,12 +91,13 @@ def cpu_baseline(w, max_coords: int, reps: int = 3):
                       f"quantize+encode+decode, median of {reps} runs, {t:.2f} s each"}
 
 
-def gamma_leg(q, torch, args, v, lay, n, s, d, seed, nb, cap_omega, stream, nbits_omega):
-    """The same workload with Elias-gamma record codes (qsgd_encode_ex /
-    qsgd_decode_ex): call times on the launch stream, bits per coordinate, and
-    the algorithmic-bytes HBM fractions, next to omega's."""
+def variant_leg(q, torch, args, v, lay, n, s, d, seed, nb, stream, nbits_omega, code, norm):
+    """The same workload with another record code (Elias gamma) or bucket scale
+    (max-norm, the QSGDinf reading), through qsgd_encode_ex / qsgd_decode_ex:
+    call times on the launch stream, bits per coordinate, and the
+    algorithmic-bytes HBM fractions, next to the default's."""
     dev = v.device
-    G = q.GAMMA
+    G = code
     ragged = lay is not None
     cap = lay.capacity_words(s, G) if ragged else q.encode_capacity_words(n, s, d, G)
     out = torch.empty(cap, dtype=torch.int64, device=dev)
@@ -106,9 +107,9 @@ def gamma_leg(q, torch, args, v, lay, n, s, d, seed, nb, cap_omega, stream, nbit
 
     def enc():
         if ragged:
-            q.encode_ragged(v, lay, s, seed, out=out, out_bits=bits, offsets=offs, code=G)
+            q.encode_ragged(v, lay, s, seed, out=out, out_bits=bits, offsets=offs, code=G, norm=norm)
         else:
-            q.encode(v, s, d, seed, out=out, out_bits=bits, offsets=offs, code=G)
+            q.encode(v, s, d, seed, out=out, out_bits=bits, offsets=offs, code=G, norm=norm)
 
     def dec():
         if ragged:
@@ -135,7 +136,7 @@ def gamma_leg(q, torch, args, v, lay, n, s, d, seed, nb, cap_omega, stream, nbit
     alg = 4.0 * n + nbits / 8.0 + 8.0 * (nb + 1)
     return {"encode_ms_avg": round(e_ms, 4), "decode_ms_avg": round(d_ms, 4),
             "round_trip_GBps_fp32": round(4.0 * n / ((e_ms + d_ms) * 1e-3) / 1e9, 2),
-            "bits_per_coord": round(nbits / n, 4), "bits_vs_omega": round(nbits / nbits_omega, 4),
+            "bits_per_coord": round(nbits / n, 4), "bits_vs_default": round(nbits / nbits_omega, 4),
             "encode_hbm_frac": round(alg / (e_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "decode_hbm_frac": round(alg / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
@@ -185,7 +186,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--cpu-sample", type=int, default=0, help="coordinates for the oracle (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-gamma", action="store_true", help="skip the Elias-gamma leg")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the Elias-gamma and max-norm legs")
     ap.add_argument("--acc-streams", type=int, default=4,
                     help="streams of the decode-accumulate measurement (configs 2, 3; 0: skip)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -298,8 +300,11 @@ def main():
                      "traffic": measured_traffic(dominant),
                      "algorithmic_bytes": round(enc_bytes if dominant == "encode" else dec_bytes)},
     }
-    if not args.no_gamma:
-        res["gamma"] = gamma_leg(q, torch, args, vs[0], lay, n, s, d, seed, nb, cap, stream, nbits)
+    if not args.no_variants:
+        res["gamma"] = variant_leg(q, torch, args, vs[0], lay, n, s, d, seed, nb, stream, nbits,
+                                   q.GAMMA, q.L2)
+        res["maxnorm"] = variant_leg(q, torch, args, vs[0], lay, n, s, d, seed, nb, stream, nbits,
+                                     q.OMEGA, q.MAXNORM)
     if args.acc_streams and args.config in (2, 3) and not ragged:
         res["decode_accumulate"] = decode_accumulate_leg(q, wl, torch, args, vs[0], n, s, d, seed, nb, stream)
     if not args.no_cpu_baseline:

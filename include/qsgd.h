@@ -71,6 +71,16 @@ typedef enum {
  * in binary (2 floor(log2 N) + 1 bits); the stream layout is otherwise the same. */
 typedef enum { QSGD_CODE_OMEGA = 0, QSGD_CODE_GAMMA = 1 } qsgd_code;
 
+/* Scale of a bucket. QSGD_NORM_L2 is the page's ||v||_2 (the default of every
+ * call without a norm argument). QSGD_NORM_MAX scales by max_i |v_i| instead:
+ * the pages name a practical heuristic variant "QSGDinf" (page "NUQSGD: Provably
+ * Communication-efficient Data-parallel SGD via Nonuniform Quantization",
+ * abstract) without defining it; this library reads the name as the infinity
+ * norm. The norm field of the stream then holds max|v_i| (exact), r_i =
+ * RN32(|v_i| * RN64(s / max|v|)) and everything else is unchanged, so decode
+ * needs no norm argument. The coordinates of largest magnitude get k = s. */
+typedef enum { QSGD_NORM_L2 = 0, QSGD_NORM_MAX = 1 } qsgd_norm;
+
 /* Human-readable name of a status code (static string). */
 const char *qsgd_status_string(qsgd_status status);
 
@@ -129,19 +139,23 @@ qsgd_status qsgd_encode(const float *v, uint64_t n, uint32_t s, uint32_t d, uint
 qsgd_status qsgd_decode(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
                         uint32_t s, uint32_t d, float *v_hat, hipStream_t stream);
 
-/* ---- choice of code (and of uniform or ragged buckets) in one call ----------
+/* ---- choice of code and norm (and of uniform or ragged buckets) in one call --
  * bucket_start is the DEVICE bucket table of a ragged batch, or NULL for
  * uniform buckets of d coordinates (then nb must be ceil(n/d)). Other arguments
- * as in qsgd_encode / qsgd_decode; a stream must be decoded with the code it
- * was encoded with. An unknown code is QSGD_ERR_INVALID_ARG. */
+ * as in qsgd_quantize / qsgd_encode / qsgd_decode; a stream must be decoded with
+ * the code it was encoded with. An unknown code or norm is QSGD_ERR_INVALID_ARG. */
 
 /* Capacity of `out` for qsgd_encode_ex (a bound for uniform and ragged layouts
  * alike); 0 for invalid arguments. */
 uint64_t qsgd_encode_capacity_words_ex(uint64_t n, uint64_t nb, uint32_t s, uint32_t d,
                                        qsgd_code code);
+qsgd_status qsgd_quantize_ex(const float *v, uint64_t n, const uint64_t *bucket_start, uint64_t nb,
+                             uint32_t s, uint32_t d, uint64_t seed, qsgd_norm norm, int32_t *levels,
+                             float *norms, hipStream_t stream);
 qsgd_status qsgd_encode_ex(const float *v, uint64_t n, const uint64_t *bucket_start, uint64_t nb,
-                           uint32_t s, uint32_t d, uint64_t seed, qsgd_code code, uint64_t *out,
-                           uint64_t *out_bits, uint64_t *bucket_bit_offsets, hipStream_t stream);
+                           uint32_t s, uint32_t d, uint64_t seed, qsgd_code code, qsgd_norm norm,
+                           uint64_t *out, uint64_t *out_bits, uint64_t *bucket_bit_offsets,
+                           hipStream_t stream);
 qsgd_status qsgd_decode_ex(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
                            const uint64_t *bucket_start, uint64_t nb, uint32_t s, uint32_t d,
                            qsgd_code code, float *v_hat, hipStream_t stream);

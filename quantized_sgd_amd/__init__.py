@@ -19,6 +19,7 @@ __all__ = [
     "QsgdError", "lib", "num_buckets", "encode_capacity_words", "quantize", "encode",
     "decode", "RaggedLayout", "quantize_ragged", "encode_ragged", "decode_ragged",
     "max_bucket", "max_streams", "decode_accumulate", "decode_accumulate_ragged", "OMEGA", "GAMMA",
+    "L2", "MAXNORM",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +32,7 @@ _vp = ctypes.c_void_p
 
 QSGD_OK, QSGD_ERR_INVALID_ARG, QSGD_ERR_LAUNCH, QSGD_ERR_UNSUPPORTED = 0, 1, 2, 3
 OMEGA, GAMMA = 0, 1  # integer code of the record fields (qsgd_code)
+L2, MAXNORM = 0, 1   # bucket scale (qsgd_norm): ||v||_2, or max|v_i| (QSGDinf)
 
 
 class QsgdError(RuntimeError):
@@ -70,7 +72,9 @@ def lib():
         L.qsgd_decode_ragged.argtypes = [_vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp, _vp]
         L.qsgd_encode_capacity_words_ex.argtypes = [_u64, _u64, _u32, _u32, ctypes.c_int]
         L.qsgd_encode_capacity_words_ex.restype = _u64
-        L.qsgd_encode_ex.argtypes = [_vp, _u64, _vp, _u64, _u32, _u32, _u64, ctypes.c_int, _vp, _vp, _vp, _vp]
+        L.qsgd_encode_ex.argtypes = [_vp, _u64, _vp, _u64, _u32, _u32, _u64, ctypes.c_int, ctypes.c_int,
+                                     _vp, _vp, _vp, _vp]
+        L.qsgd_quantize_ex.argtypes = [_vp, _u64, _vp, _u64, _u32, _u32, _u64, ctypes.c_int, _vp, _vp, _vp]
         L.qsgd_decode_ex.argtypes = [_vp, _vp, _u64, _vp, _u64, _u32, _u32, ctypes.c_int, _vp, _vp]
         L.qsgd_max_streams.argtypes = []
         L.qsgd_max_streams.restype = _u32
@@ -79,7 +83,7 @@ def lib():
         for name in ("qsgd_quantize", "qsgd_encode", "qsgd_decode", "qsgd_ragged_bucket_table",
                      "qsgd_quantize_ragged", "qsgd_encode_ragged", "qsgd_decode_ragged",
                      "qsgd_decode_accumulate", "qsgd_decode_accumulate_ragged", "qsgd_encode_ex",
-                     "qsgd_decode_ex"):
+                     "qsgd_decode_ex", "qsgd_quantize_ex"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -119,26 +123,34 @@ def encode_capacity_words(n: int, s: int, d: int, code: int = OMEGA) -> int:
     return int(lib().qsgd_encode_capacity_words_ex(n, num_buckets(n, d), s, d, code))
 
 
-def quantize(v: torch.Tensor, s: int, d: int, seed: int, levels=None, norms=None, stream=None):
-    """Q_s per bucket: returns (levels int32 = sgn * k, norms float32)."""
+def quantize(v: torch.Tensor, s: int, d: int, seed: int, levels=None, norms=None, stream=None,
+             norm: int = L2):
+    """Q_s per bucket: returns (levels int32 = sgn * k, norms float32). norm:
+    L2 (qsgd_quantize) or MAXNORM (qsgd_quantize_ex, the QSGDinf reading)."""
     n = v.numel()
     nb = num_buckets(n, d)
     if levels is None:
         levels = torch.empty(n, dtype=torch.int32, device=v.device)
     if norms is None:
         norms = torch.empty(max(nb, 1), dtype=torch.float32, device=v.device)
-    _check(lib().qsgd_quantize(_dev(v, torch.float32, "v"), n, s, d, seed,
-                               _dev(levels, torch.int32, "levels"),
-                               _dev(norms, torch.float32, "norms"), _stream(stream)),
-           "qsgd_quantize")
+    if norm == L2:
+        _check(lib().qsgd_quantize(_dev(v, torch.float32, "v"), n, s, d, seed,
+                                   _dev(levels, torch.int32, "levels"),
+                                   _dev(norms, torch.float32, "norms"), _stream(stream)),
+               "qsgd_quantize")
+    else:
+        _check(lib().qsgd_quantize_ex(_dev(v, torch.float32, "v"), n, None, nb, s, d, seed, norm,
+                                      _dev(levels, torch.int32, "levels"),
+                                      _dev(norms, torch.float32, "norms"), _stream(stream)),
+               "qsgd_quantize_ex")
     return levels, norms[:nb]
 
 
 def encode(v: torch.Tensor, s: int, d: int, seed: int, out=None, out_bits=None, offsets=None,
-           stream=None, code: int = OMEGA):
+           stream=None, code: int = OMEGA, norm: int = L2):
     """Returns (out words, out_bits [1], bucket bit offsets [nb + 1]) as device
     tensors (uint64 data in int64 tensors). The stream is out[: ceil(bits/64)].
-    code: OMEGA (qsgd_encode) or GAMMA (qsgd_encode_ex)."""
+    code OMEGA and norm L2 use qsgd_encode; other choices qsgd_encode_ex."""
     n = v.numel()
     nb = num_buckets(n, d)
     cap = encode_capacity_words(n, s, d, code)
@@ -152,13 +164,13 @@ def encode(v: torch.Tensor, s: int, d: int, seed: int, out=None, out_bits=None, 
         out_bits = torch.empty(1, dtype=torch.int64, device=v.device)
     if offsets is None:
         offsets = torch.empty(nb + 1, dtype=torch.int64, device=v.device)
-    if code == OMEGA:
+    if code == OMEGA and norm == L2:
         _check(lib().qsgd_encode(_dev(v, torch.float32, "v"), n, s, d, seed,
                                  _dev(out, torch.int64, "out"), _dev(out_bits, torch.int64, "out_bits"),
                                  _dev(offsets, torch.int64, "offsets"), _stream(stream)),
                "qsgd_encode")
     else:
-        _check(lib().qsgd_encode_ex(_dev(v, torch.float32, "v"), n, None, nb, s, d, seed, code,
+        _check(lib().qsgd_encode_ex(_dev(v, torch.float32, "v"), n, None, nb, s, d, seed, code, norm,
                                     _dev(out, torch.int64, "out"), _dev(out_bits, torch.int64, "out_bits"),
                                     _dev(offsets, torch.int64, "offsets"), _stream(stream)),
                "qsgd_encode_ex")
@@ -231,19 +243,26 @@ class RaggedLayout:
         return int(lib().qsgd_encode_capacity_words_ex(self.n, self.nb, s, self.d, code))
 
 
-def quantize_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, stream=None):
+def quantize_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, stream=None,
+                    norm: int = L2):
     levels = torch.empty(layout.n, dtype=torch.int32, device=v.device)
     norms = torch.empty(max(layout.nb, 1), dtype=torch.float32, device=v.device)
-    _check(lib().qsgd_quantize_ragged(_dev(v, torch.float32, "v"), layout.n,
-                                      _dev(layout.bucket_start, torch.int64, "bucket_start"),
-                                      layout.nb, s, layout.d, seed, _dev(levels, torch.int32, "levels"),
+    bs = _dev(layout.bucket_start, torch.int64, "bucket_start")
+    if norm == L2:
+        _check(lib().qsgd_quantize_ragged(_dev(v, torch.float32, "v"), layout.n, bs, layout.nb, s,
+                                          layout.d, seed, _dev(levels, torch.int32, "levels"),
+                                          _dev(norms, torch.float32, "norms"), _stream(stream)),
+               "qsgd_quantize_ragged")
+    else:
+        _check(lib().qsgd_quantize_ex(_dev(v, torch.float32, "v"), layout.n, bs, layout.nb, s, layout.d,
+                                      seed, norm, _dev(levels, torch.int32, "levels"),
                                       _dev(norms, torch.float32, "norms"), _stream(stream)),
-           "qsgd_quantize_ragged")
+               "qsgd_quantize_ex")
     return levels, norms[: layout.nb]
 
 
 def encode_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, out=None, out_bits=None,
-                  offsets=None, stream=None, code: int = OMEGA):
+                  offsets=None, stream=None, code: int = OMEGA, norm: int = L2):
     cap = layout.capacity_words(s, code)
     if cap == 0:
         raise QsgdError(QSGD_ERR_UNSUPPORTED, "qsgd_encode_capacity_words_ragged")
@@ -253,7 +272,7 @@ def encode_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, out=
         out_bits = torch.empty(1, dtype=torch.int64, device=v.device)
     if offsets is None:
         offsets = torch.empty(layout.nb + 1, dtype=torch.int64, device=v.device)
-    if code == OMEGA:
+    if code == OMEGA and norm == L2:
         _check(lib().qsgd_encode_ragged(_dev(v, torch.float32, "v"), layout.n,
                                         _dev(layout.bucket_start, torch.int64, "bucket_start"), layout.nb,
                                         s, layout.d, seed, _dev(out, torch.int64, "out"),
@@ -263,7 +282,7 @@ def encode_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, out=
     else:
         _check(lib().qsgd_encode_ex(_dev(v, torch.float32, "v"), layout.n,
                                     _dev(layout.bucket_start, torch.int64, "bucket_start"), layout.nb,
-                                    s, layout.d, seed, code, _dev(out, torch.int64, "out"),
+                                    s, layout.d, seed, code, norm, _dev(out, torch.int64, "out"),
                                     _dev(out_bits, torch.int64, "out_bits"),
                                     _dev(offsets, torch.int64, "offsets"), _stream(stream)),
                "qsgd_encode_ex")

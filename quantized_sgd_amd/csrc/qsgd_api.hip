@@ -139,9 +139,10 @@ uint32_t log2u(uint32_t d) { return 31u - (uint32_t)__builtin_clz(d); }
 
 qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb,
                           uint32_t s, uint32_t d, uint64_t seed, int32_t *levels, float *norms,
-                          hipStream_t stream) {
+                          hipStream_t stream, uint32_t norm = QSGD_NORM_L2) {
     qsgd_status st = check_common(v, s, d);
     if (st != QSGD_OK) return st;
+    if (norm > QSGD_NORM_MAX) return QSGD_ERR_INVALID_ARG;
     if (n == 0) return QSGD_OK;
     if (!v || !levels || !norms || !aligned16(levels)) return QSGD_ERR_INVALID_ARG;
     const bool ragged = bstart != nullptr;
@@ -151,6 +152,7 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
     P.v = v; P.n = n; P.nb = nb; P.bstart = bstart; P.seed = seed; P.s = s; P.d = d;
     P.K = p.K; P.ntiles = (uint32_t)p.ntiles; P.levels = levels; P.norms = norms;
     P.obuf_words = 0;
+    P.maxnorm = norm;
     if (use_aligned(bstart, s, d)) {
         hipLaunchKernelGGL(quantize_aligned_kernel, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P,
                            log2u(d));
@@ -166,10 +168,11 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
 
 qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb, uint32_t s,
                         uint32_t d, uint64_t seed, uint64_t *out, uint64_t *out_bits,
-                        uint64_t *offsets, hipStream_t stream, uint32_t code = QSGD_CODE_OMEGA) {
+                        uint64_t *offsets, hipStream_t stream, uint32_t code = QSGD_CODE_OMEGA,
+                        uint32_t norm = QSGD_NORM_L2) {
     qsgd_status st = check_common(v, s, d);
     if (st != QSGD_OK) return st;
-    if (code > QSGD_CODE_GAMMA) return QSGD_ERR_INVALID_ARG;
+    if (code > QSGD_CODE_GAMMA || norm > QSGD_NORM_MAX) return QSGD_ERR_INVALID_ARG;
     if (!out_bits || !offsets) return QSGD_ERR_INVALID_ARG;
     if (n == 0 || nb == 0) {
         hipLaunchKernelGGL(encode_empty_kernel, dim3(1), dim3(64), 0, stream, out_bits, offsets);
@@ -189,6 +192,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     P.run_bits = P.slots + p.slot_region_words + (p.ntiles + 1) / 2;
     P.obuf_words = p.obuf_words;
     P.code = code;
+    P.maxnorm = norm;
     // pass 1 grid: at most the resident workgroups (and kMaxRuns), each taking a
     // run of consecutive tiles
     auto runs_for = [&](uint32_t resident) {
@@ -365,13 +369,22 @@ uint64_t qsgd_encode_capacity_words_ex(uint64_t n, uint64_t nb, uint32_t s, uint
     return std::max(ca, cb);
 }
 
+qsgd_status qsgd_quantize_ex(const float *v, uint64_t n, const uint64_t *bucket_start, uint64_t nb,
+                             uint32_t s, uint32_t d, uint64_t seed, qsgd_norm norm, int32_t *levels,
+                             float *norms, hipStream_t stream) {
+    if (!bucket_start && nb != qsgd_num_buckets(n, d)) return QSGD_ERR_INVALID_ARG;
+    if (bucket_start && nb == 0 && n != 0) return QSGD_ERR_INVALID_ARG;
+    return quantize_impl(v, n, bucket_start, nb, s, d, seed, levels, norms, stream, (uint32_t)norm);
+}
+
 qsgd_status qsgd_encode_ex(const float *v, uint64_t n, const uint64_t *bucket_start, uint64_t nb,
-                           uint32_t s, uint32_t d, uint64_t seed, qsgd_code code, uint64_t *out,
-                           uint64_t *out_bits, uint64_t *bucket_bit_offsets, hipStream_t stream) {
+                           uint32_t s, uint32_t d, uint64_t seed, qsgd_code code, qsgd_norm norm,
+                           uint64_t *out, uint64_t *out_bits, uint64_t *bucket_bit_offsets,
+                           hipStream_t stream) {
     if (!bucket_start && nb != qsgd_num_buckets(n, d)) return QSGD_ERR_INVALID_ARG;
     if (bucket_start && nb == 0 && n != 0) return QSGD_ERR_INVALID_ARG;
     return encode_impl(v, n, bucket_start, nb, s, d, seed, out, out_bits, bucket_bit_offsets, stream,
-                       (uint32_t)code);
+                       (uint32_t)code, (uint32_t)norm);
 }
 
 qsgd_status qsgd_decode_ex(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,

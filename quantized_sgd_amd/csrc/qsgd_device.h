@@ -140,14 +140,18 @@ __device__ __forceinline__ T block_excl_scan(T x, Op op, T identity, T *scratch,
 // Segmented inclusive scan of (flag, value) over the block in thread order:
 // S_j = v_j if f_j else S_{j-1} + v_j. Returns S_{j-1} (the exclusive value; 0
 // for thread 0). Used for bucket sums of squares that span several threads.
+// MAXN: the same scan with max in place of + (for bucket max-norms; the values
+// are >= 0, so 0 is the identity).
+template <bool MAXN = false>
 __device__ __forceinline__ double block_seg_excl_sum(double v, int f, double *sv, int *sf) {
     const int lane = lane_id(), wave = wave_id();
+    auto op = [](double a, double b) { return MAXN ? (a > b ? a : b) : a + b; };
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const double yv = __shfl_up(v, off, 64);
         const int yf = __shfl_up(f, off, 64);
         if (lane >= off) {
-            if (!f) v = yv + v;
+            if (!f) v = op(yv, v);
             f |= yf;
         }
     }
@@ -155,9 +159,9 @@ __device__ __forceinline__ double block_seg_excl_sum(double v, int f, double *sv
     __syncthreads();
     double pv = 0.0;
     for (int w = 0; w < wave; ++w) {  // combine the earlier waves in order
-        if (sf[w]) pv = sv[w]; else pv = pv + sv[w];
+        if (sf[w]) pv = sv[w]; else pv = op(pv, sv[w]);
     }
-    const double incl = f ? v : pv + v;
+    const double incl = f ? v : op(pv, v);
     double ex = __shfl_up(incl, 1, 64);
     if (lane == 0) ex = pv;
     return ex;

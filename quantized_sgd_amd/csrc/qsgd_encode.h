@@ -125,7 +125,8 @@ __global__ __launch_bounds__(kWG) void quantize_kernel(QsgdParams P) {
     ThreadCoords c;
     load_coords(P, t, c);
     __syncthreads();
-    bucket_norms<RAGGED>(P, t, L.f, c);
+    if (P.maxnorm) bucket_norms<RAGGED, true>(P, t, L.f, c);
+    else bucket_norms<RAGGED, false>(P, t, L.f, c);
     ThreadLevels lv;
     quantize_coords(P, t, L.f, c, lv);
     const int j = (int)threadIdx.x;
@@ -206,7 +207,8 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
         ThreadCoords c;
         load_coords(P, t, c);
         __syncthreads();
-        bucket_norms<RAGGED>(P, t, L.f, c);
+        if (P.maxnorm) bucket_norms<RAGGED, true>(P, t, L.f, c);
+        else bucket_norms<RAGGED, false>(P, t, L.f, c);
         ThreadLevels lv;
         quantize_coords(P, t, L.f, c, lv);
 
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
 
 // Aligned fast path, front half. aligned_load: the thread's 16 coordinates
 // from g0 (0 past n). aligned_norm: the bucket norm RN32(sqrt(sum of squares))
-// of the thread's bucket. The sum: fp64 fma per thread in index order, an xor
+// of the thread's bucket (MAXN: its max-norm max|x_i|, exact in any order). The sum: fp64 fma per thread in index order, an xor
 // butterfly over the bucket's lanes (both operands of every addition are the
 // same pair on each lane, so all lanes get the same bits), and for G > 64 the
 // bucket's waves added in wave order through red[kWaves] (ends with a barrier
@@ -330,15 +332,17 @@ __device__ __forceinline__ void aligned_load(const QsgdParams &P, uint64_t g0, f
     }
 }
 
+template <bool MAXN = false>
 __device__ __forceinline__ float aligned_norm(const float (&x)[kCPT], uint32_t G, double *red) {
+    auto op = [](double a, double b) { return MAXN ? (a > b ? a : b) : a + b; };
     double acc = 0.0;
 #pragma unroll
     for (int q = 0; q < kCPT; ++q) {
         const double y = (double)x[q];
-        acc = fma(y, y, acc);
+        acc = MAXN ? op(acc, fabs(y)) : fma(y, y, acc);
     }
     const uint32_t gw = G < 64u ? G : 64u;
-    for (uint32_t o = 1; o < gw; o <<= 1) acc += __shfl_xor(acc, (int)o, 64);
+    for (uint32_t o = 1; o < gw; o <<= 1) acc = op(acc, __shfl_xor(acc, (int)o, 64));
     if (G > 64u) {
         const int wave = __builtin_amdgcn_readfirstlane(wave_id());
         if (lane_id() == 0) red[wave] = acc;
@@ -346,10 +350,10 @@ __device__ __forceinline__ float aligned_norm(const float (&x)[kCPT], uint32_t G
         const uint32_t nwb = G >> 6;
         const uint32_t w0 = (uint32_t)wave & ~(nwb - 1u);
         double tsum = red[w0];
-        for (uint32_t w = 1; w < nwb; ++w) tsum += red[w0 + w];
+        for (uint32_t w = 1; w < nwb; ++w) tsum = op(tsum, red[w0 + w]);
         acc = tsum;
     }
-    return (float)sqrt(acc);
+    return MAXN ? (float)acc : (float)sqrt(acc);
 }
 
 // Quantize, aligned fast path (the encode fast path's front half): one
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(kWG) void quantize_aligned_kernel(QsgdParams P, uin
     const uint64_t g0 = (uint64_t)tile * kTC + (uint64_t)(j * kCPT);
     float x[kCPT];
     aligned_load(P, g0, x);
-    const float norm = aligned_norm(x, G, sh_red);
+    const float norm = P.maxnorm ? aligned_norm<true>(x, G, sh_red) : aligned_norm<false>(x, G, sh_red);
     const double cb = norm == 0.0f ? 0.0 : (double)P.s / (double)norm;
     if ((j & (G - 1)) == 0 && g0 < P.n) P.norms[g0 >> log2d] = norm;
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
@@ -490,7 +494,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         } else {
             aligned_load(P, g0, x);
         }
-        const float norm = aligned_norm(x, G, sh_red);
+        const float norm = P.maxnorm ? aligned_norm<true>(x, G, sh_red) : aligned_norm<false>(x, G, sh_red);
         const double cb = norm == 0.0f ? 0.0 : (double)P.s / (double)norm;
         const bool bstart = first_of_bucket && g0 < P.n;
 

@@ -38,6 +38,7 @@ struct QsgdParams {
     uint32_t obuf_words;   // words of a tile's bit string bound (+1 spare)
     uint32_t run, rem;     // workgroup b takes run_first(b) .. run_first(b + 1) - 1
     uint32_t code;         // integer code of gaps and levels: 0 Elias omega, 1 Elias gamma
+    uint32_t maxnorm;      // bucket scale: 0 the L2 norm, 1 the max-norm max|v_i| (QSGDinf)
 };
 
 // Runs of consecutive tiles: the first `rem` workgroups take run + 1 tiles, the
@@ -153,8 +154,9 @@ __device__ __forceinline__ int first_bucket(const QsgdParams &P, const Tile &t, 
 // segmented scan in thread order. The order is fixed, so results are
 // reproducible; it differs from a plain left-to-right sum only in rounding.
 // Afterwards L.nrm[k] = RN32(sqrt(sum)) and L.cb[k] = RN64(s / norm) (0 for a
-// zero bucket). Ends with a barrier.
-template <bool RAGGED>
+// zero bucket). MAXN: the max-norm max|v_i| instead (exact, in any order).
+// Ends with a barrier.
+template <bool RAGGED, bool MAXN = false>
 __device__ __forceinline__ void bucket_norms(const QsgdParams &P, const Tile &t, FrontLds &L,
                                              ThreadCoords &c) {
     const int j = (int)threadIdx.x;
@@ -183,18 +185,20 @@ __device__ __forceinline__ void bucket_norms(const QsgdParams &P, const Tile &t,
                 cur_first = 0;
             }
             const double y = (double)c.x[q];
-            acc = acc + y * y;
+            if (MAXN) acc = acc > fabs(y) ? acc : fabs(y);
+            else acc = acc + y * y;
         }
     }
     const int ends_here = active && (nbnd == c.vx1);
     if (active && ends_here && cur_fresh) L.cb[k] = acc;
     // scan element: the last segment (flag: it starts a bucket)
-    const double ex = block_seg_excl_sum(active ? acc : 0.0, active ? cur_fresh : 0, L.segv, L.segf);
-    if (head_done) L.cb[c.kf] = ex + head;
-    else if (active && cur_first && !cur_fresh && ends_here) L.cb[k] = ex + acc;
+    const double ex = block_seg_excl_sum<MAXN>(active ? acc : 0.0, active ? cur_fresh : 0, L.segv, L.segf);
+    auto join = [](double a, double b) { return MAXN ? (a > b ? a : b) : a + b; };
+    if (head_done) L.cb[c.kf] = join(ex, head);
+    else if (active && cur_first && !cur_fresh && ends_here) L.cb[k] = join(ex, acc);
     __syncthreads();
     for (uint32_t b = threadIdx.x; b < t.K; b += kWG) {
-        const float nr = (float)sqrt(L.cb[b]);
+        const float nr = MAXN ? (float)L.cb[b] : (float)sqrt(L.cb[b]);
         L.nrm[b] = nr;
         L.cb[b] = nr == 0.0f ? 0.0 : (double)P.s / (double)nr;
     }

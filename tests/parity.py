@@ -31,19 +31,19 @@ def bucket_table(n, d, seg_len):
     return oracle.ragged_buckets(seg_len, d)
 
 
-def gpu_run(v: np.ndarray, s: int, d: int, seed: int, seg_len=None, code=oracle.OMEGA):
+def gpu_run(v: np.ndarray, s: int, d: int, seed: int, seg_len=None, code=oracle.OMEGA, norm=q.L2):
     vd = to_dev(v)
     if seg_len is None:
-        lev, nrm = q.quantize(vd, s, d, seed)
-        out, bits, offs = q.encode(vd, s, d, seed, code=code)
+        lev, nrm = q.quantize(vd, s, d, seed, norm=norm)
+        out, bits, offs = q.encode(vd, s, d, seed, code=code, norm=norm)
         torch.cuda.synchronize()
         nbits = int(bits.item())
         words = out[: (nbits + 63) // 64]
         vh = q.decode(out, offs, v.size, s, d, code=code)
     else:
         lay = q.RaggedLayout(seg_len, d)
-        lev, nrm = q.quantize_ragged(vd, lay, s, seed)
-        out, bits, offs = q.encode_ragged(vd, lay, s, seed, code=code)
+        lev, nrm = q.quantize_ragged(vd, lay, s, seed, norm=norm)
+        out, bits, offs = q.encode_ragged(vd, lay, s, seed, code=code, norm=norm)
         torch.cuda.synchronize()
         nbits = int(bits.item())
         words = out[: (nbits + 63) // 64]
@@ -53,16 +53,20 @@ def gpu_run(v: np.ndarray, s: int, d: int, seed: int, seg_len=None, code=oracle.
                 offsets=u64(offs), bits=nbits, v_hat=vh.cpu().numpy(), out=out)
 
 
-def check_parity(v: np.ndarray, s: int, d: int, seed: int, seg_len=None, g=None, code=oracle.OMEGA):
+def check_parity(v: np.ndarray, s: int, d: int, seed: int, seg_len=None, g=None, code=oracle.OMEGA,
+                 norm=q.L2):
     """Full element-by-element parity of quantize, encode and decode (code: the
-    integer code of the record fields)."""
+    integer code of the record fields; norm: the bucket scale, the max-norm
+    being exact and so compared bit for bit)."""
     if g is None:
-        g = gpu_run(v, s, d, seed, seg_len, code)
+        g = gpu_run(v, s, d, seed, seg_len, code, norm)
     bst = bucket_table(v.size, d, seg_len)
     # norms
-    on = oracle.bucket_norms(v, bst)
+    on = oracle.bucket_norms(v, bst) if norm == q.L2 else oracle.bucket_max_norms(v, bst)
     gn = g["norms"]
     assert gn.shape == on.shape
+    if norm != q.L2:
+        assert np.array_equal(gn.view(np.uint32), on.view(np.uint32))
     rel = np.abs(gn.astype(np.float64) - on) / np.maximum(np.abs(on.astype(np.float64)), 1e-45)
     assert np.all(rel <= 1e-6), float(rel.max())
     # levels given the GPU norms

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(q.LIB_PATH)
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for name in names:
         assert hasattr(lib, name), name
 
@@ -72,8 +72,11 @@ def test_code_choice_argument_checks():
     lib = q.lib()
     assert lib.qsgd_encode_capacity_words_ex(1000, 2, 4, 512, 2) == 0          # unknown code
     assert lib.qsgd_encode_capacity_words_ex(1000, 2, 4, 512, q.GAMMA) > 0
-    assert lib.qsgd_encode_ex(16, 1000, None, 3, 4, 512, 1, q.GAMMA, 16, 16, 16, None) == 1  # nb != ceil(n/d)
-    assert lib.qsgd_encode_ex(16, 1000, None, 2, 4, 512, 1, 7, 16, 16, 16, None) == 1        # unknown code
+    assert lib.qsgd_encode_ex(16, 1000, None, 3, 4, 512, 1, q.GAMMA, 0, 16, 16, 16, None) == 1  # nb != ceil(n/d)
+    assert lib.qsgd_encode_ex(16, 1000, None, 2, 4, 512, 1, 7, 0, 16, 16, 16, None) == 1        # unknown code
+    assert lib.qsgd_encode_ex(16, 1000, None, 2, 4, 512, 1, 0, 5, 16, 16, 16, None) == 1        # unknown norm
+    assert lib.qsgd_quantize_ex(16, 1000, None, 2, 4, 512, 1, 5, 16, 16, None) == 1             # unknown norm
+    assert lib.qsgd_quantize_ex(16, 1000, None, 3, 4, 512, 1, q.MAXNORM, 16, 16, None) == 1     # nb != ceil(n/d)
     assert lib.qsgd_decode_ex(16, 16, 1000, None, 3, 4, 512, q.GAMMA, 16, None) == 1        # nb != ceil(n/d)
     assert lib.qsgd_decode_ex(16, 16, 1000, None, 2, 4, 512, 9, 16, None) == 1              # unknown code
 
