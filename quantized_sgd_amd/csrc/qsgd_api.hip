@@ -204,8 +204,16 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     // pass 1: every tile into its slot
     if (use_aligned(bstart, s, d)) {
         const size_t lds = aligned_encode_lds_bytes(p.obuf_words, s);
-        const uint32_t blocks = runs_for(resident_blocks(encode_aligned_kernel, lds));
-        hipLaunchKernelGGL(encode_aligned_kernel, dim3(blocks), dim3(kWG), lds, stream, P, log2u(d));
+        // long thread halves are common when levels are large: mean level about
+        // 0.8 s / sqrt(d) under the L2 norm, 0.8 s / max|z| (about s / 4) under
+        // the max-norm; past about 2 a half's 8 records pass 64 bits
+        const bool levels = norm == QSGD_NORM_MAX ? s >= 8 : (uint64_t)s * s >= 6ull * d;
+        auto launch = [&](auto kernel) {
+            const uint32_t blocks = runs_for(resident_blocks(kernel, lds));
+            hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), lds, stream, P, log2u(d));
+        };
+        if (levels) launch(encode_aligned_kernel<true>);
+        else launch(encode_aligned_kernel<false>);
     } else {
         auto launch = [&](auto kernel) {
             const uint32_t blocks = runs_for(resident_blocks(kernel, p.lds_bytes));

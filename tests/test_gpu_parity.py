@@ -61,6 +61,19 @@ def test_long_records_per_thread(n, d, s, seed):
     check_parity(v, s, d, seed)
 
 
+@pytest.mark.parametrize("code", [0, 1])
+def test_long_halves_from_spikes(code):
+    # buckets of 1024 with s = 64: levels are small on average (the encoder keeps
+    # no level bytes for such launches), but 16 spikes of equal size per bucket
+    # get k = 16 and records of 13+ bits, so their thread halves pass 64 bits
+    rng = np.random.default_rng(44)
+    n, d = 64 * 1024 + 100, 1024
+    v = (1e-6 * rng.standard_normal(n)).astype(np.float32)
+    for b0 in range(0, n - 336, d):
+        v[b0 + 320:b0 + 336] = rng.choice([-1.0, 1.0], 16).astype(np.float32)
+    check_parity(v, 64, d, 44, code=code)
+
+
 def test_zero_buckets_and_spikes():
     n, d = 40000, 512
     v = np.zeros(n, np.float32)
