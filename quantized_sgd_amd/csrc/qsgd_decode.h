@@ -196,22 +196,41 @@ struct Bits {
     const uint32_t *src;
     uint32_t hlast;
 
-    // The 64 stream bits from bit p on, stream bit p in bit 0; at least the
-    // first 33 of them lie within the two dwords read (zeros above).
-    __device__ __forceinline__ uint64_t at(uint32_t p) const {
-        const uint32_t h = p >> 5;
-        uint64_t w;
+    // Stream bits [32h, 32h + 64), bit 32h in bit 0.
+    __device__ __forceinline__ uint64_t pair(uint32_t h) const {
         if (LDS) {
             const lds_cu32 *lds = (const lds_cu32 *)(uintptr_t)0;
-            w = ((uint64_t)lds[h + 1u] << 32) | (uint64_t)lds[h];
-        } else {
-            const uint32_t a = h <= hlast ? src[h ^ 1u] : 0u;
-            const uint32_t b = h + 1u <= hlast ? src[(h + 1u) ^ 1u] : 0u;
-            w = ((uint64_t)__builtin_bitreverse32(b) << 32) | (uint64_t)__builtin_bitreverse32(a);
+            return ((uint64_t)lds[h + 1u] << 32) | (uint64_t)lds[h];
         }
-        return w >> (p & 31u);
+        const uint32_t a = h <= hlast ? src[h ^ 1u] : 0u;
+        const uint32_t b = h + 1u <= hlast ? src[(h + 1u) ^ 1u] : 0u;
+        return ((uint64_t)__builtin_bitreverse32(b) << 32) | (uint64_t)__builtin_bitreverse32(a);
     }
+
+    // The 64 stream bits from bit p on, stream bit p in bit 0; at least the
+    // first 33 of them lie within the two dwords read (zeros above).
+    __device__ __forceinline__ uint64_t at(uint32_t p) const { return pair(p >> 5) >> (p & 31u); }
 };
+
+// Read-ahead window of a chain walk: stream bits [32h, 32h + 64). A walk reads
+// the window of its current position together with that position's table
+// entry; the next position is at most 12 bits on (one table step), so its 12
+// table bits lie in that window (p - 32h <= 43). The walk thus waits for one
+// LDS read per step instead of two dependent ones. After a general-path record
+// the window is read again at the new position.
+struct Win {
+    uint64_t w;
+    uint32_t h;
+};
+
+template <bool LDS>
+__device__ __forceinline__ Win win_at(const Bits<LDS> &r, uint32_t p) {
+    return Win{r.pair(p >> 5), p >> 5};
+}
+
+__device__ __forceinline__ uint32_t win_index(const Win &W, uint32_t p) {
+    return (uint32_t)(W.w >> (p - (W.h << 5))) & ((1u << kLutBits) - 1u);
+}
 
 // CODE: integer code of the record fields, 0 Elias omega, 1 Elias gamma.
 template <int CODE>
@@ -272,42 +291,58 @@ __device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const X &x, 
 // k <= s or gap <= bucket length: on the true chain those hold anyway, and a
 // speculative chain only has to be a deterministic function of its start. A
 // two-record entry is the same as two one-record steps, so every walker of a
-// chain visits the same positions.
+// chain visits the same positions. The entry is looked up in the window W (read
+// at a position at most 12 bits before p, or at p); W moves on to p's own
+// window for the next step.
 template <bool LDS, class X>
-__device__ __forceinline__ uint32_t lut_at(const Bits<LDS> &r, const X &x, uint32_t p) {
-    return x.lut[(uint32_t)r.at(p) & ((1u << kLutBits) - 1u)];
+__device__ __forceinline__ uint32_t lut_step(const Bits<LDS> &r, const X &x, uint32_t p, Win &W) {
+    const uint32_t e = x.lut[win_index(W, p)];
+    W = win_at(r, p);
+    return e;
+}
+
+// The general path of a chain step at p: past the record at p adding its gap to
+// sum, or one bit on if no record parses there; W follows p.
+template <bool LDS, class X>
+__device__ __forceinline__ void slow_step(const Bits<LDS> &r, const X &x, uint32_t &p, uint32_t &sum,
+                                          Win &W) {
+    uint32_t gap, neg, k;
+    const uint32_t q = record_slow(r, x, p, gap, neg, k);
+    sum += q ? gap : 0u;
+    p = q ? q : p + 1u;
+    W = win_at(r, p);
 }
 
 // One step of a chain: past the record at p adding its gap to sum, or one bit
 // on if no record parses there.
 template <bool LDS, class X>
 __device__ __forceinline__ void chain_step(const Bits<LDS> &r, const X &x, uint32_t &p,
-                                           uint32_t &sum) {
-    const uint32_t e = lut_at(r, x, p);
+                                           uint32_t &sum, Win &W) {
+    const uint32_t e = lut_step(r, x, p, W);
     if (e & 15u) {
         p += (e >> 4) & 15u;
         sum += ((e >> 8) & 15u) + 1u;
     } else {
-        uint32_t gap, neg, k;
-        const uint32_t q = record_slow(r, x, p, gap, neg, k);
-        sum += q ? gap : 0u;
-        p = q ? q : p + 1u;
+        slow_step(r, x, p, sum, W);
     }
 }
 
 // One record of the true chain at p: its end (0 if it does not parse), gap and
 // level byte sign << 7 | k (k <= 127 when the caller uses the byte).
+// W is the walk's read-ahead window (lut_step).
 template <bool LDS, class X>
 __device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const X &x, uint32_t p,
-                                              uint32_t &gap, uint32_t &neg, uint32_t &k) {
-    const uint32_t e = lut_at(r, x, p);
+                                              uint32_t &gap, uint32_t &neg, uint32_t &k, Win &W) {
+    const uint32_t e = lut_step(r, x, p, W);
     if (e & 15u) {
         gap = ((e >> 8) & 15u) + 1u;
         k = (e >> 12) & 127u;
         neg = (e >> 19) & 1u;
         return p + ((e >> 4) & 15u);
     }
-    return record_slow(r, x, p, gap, neg, k);
+    const uint32_t q = record_slow(r, x, p, gap, neg, k);
+    if (q) W = win_at(r, q);
+    return q;
 }
 
 __device__ __forceinline__ uint32_t bitlen32(uint32_t x) { return 32u - (uint32_t)__clz(x); }
@@ -322,6 +357,10 @@ constexpr uint32_t kCumSlots = 63;
 #define QSGD_GUESS_STEPS 6
 #endif
 constexpr int kGuessSteps = QSGD_GUESS_STEPS;
+// Buckets whose payload averages more bits per coordinate than this take no
+// guess steps: their long records miss the table on the true chain too, where
+// moving one bit on derails the chain.
+constexpr uint32_t kGuessBits = 4;
 
 // The first steps of a chain whose start is only a guess at a record boundary.
 // Such a start lands on bits that are not a record start as often as not, and
@@ -331,10 +370,10 @@ constexpr int kGuessSteps = QSGD_GUESS_STEPS;
 // the exact rule, and both continue alike from there.
 template <bool LDS, class X>
 __device__ __forceinline__ void guess_steps(const Bits<LDS> &r, const X &x, uint32_t &p,
-                                            uint32_t sn, uint32_t &sum) {
+                                            uint32_t sn, uint32_t &sum, Win &W) {
 #pragma unroll
     for (int i = 0; i < kGuessSteps; ++i) {
-        const uint32_t e = lut_at(r, x, p);
+        const uint32_t e = lut_step(r, x, p, W);
         const uint32_t len1 = (e >> 4) & 15u;
         const bool two = len1 < (e & 15u) && p + len1 < sn;
         const uint32_t adv = (e & 15u) == 0 ? 1u : two ? (e & 15u) : len1;
@@ -349,37 +388,38 @@ __device__ __forceinline__ void guess_steps(const Bits<LDS> &r, const X &x, uint
 // Phase A: follows a chain from `start` to its first position >= sn and returns
 // that position (the exit), with the gap sum of the records passed. MARK: sets
 // bit (p - start) of own0:own1 for each chain position p in [start, start + 128)
-// and stores in cum[i] the low byte of the gap sum before the i-th of them
-// (i < kCumSlots - 1; cum_top: the gap sum after the last noted position, so a
-// table entry is exact when cum_top < 256). Two-record table entries advance
+// and, with CUM, stores in cum[i] the low byte of the gap sum before the i-th of
+// them (i < kCumSlots - 1; cum_top: the gap sum after the last noted position, so
+// a table entry is exact when cum_top < 256). Two-record table entries advance
 // two records at once when the second starts before the current limit (the
 // end of the 64-bit mark word being filled, or sn).
-template <bool LDS, bool MARK, class X>
+template <bool LDS, bool MARK, bool CUM, class X>
 __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const X &x, uint32_t start,
                                                  uint32_t sn, uint32_t &ga, uint64_t &own0,
                                                  uint64_t &own1, uint8_t *cum, uint32_t &cum_top,
                                                  bool guess = false) {
     uint32_t p = start, sum = 0;
-    if (MARK && guess) guess_steps(r, x, p, sn, sum);
+    Win W = win_at(r, p);
+    if (MARK && guess) guess_steps(r, x, p, sn, sum, W);
     if (MARK) {
         uint32_t i = 0;
         // one step from p below lim: returns the step's chain positions
         // relative to p (bit 0, and bit len1 for a second record)
         auto step = [&](uint32_t lim) -> uint32_t {
-            const uint32_t e = lut_at(r, x, p);
-            cum[i] = (uint8_t)sum;
+            const uint32_t e = lut_step(r, x, p, W);
+            if (CUM) cum[i] = (uint8_t)sum;
             uint32_t m = 1u;
             if (e & 15u) {
                 const uint32_t len1 = (e >> 4) & 15u;
                 const uint32_t s1 = sum + ((e >> 8) & 15u) + 1u;
                 const bool two = len1 < (e & 15u) && p + len1 < lim;
-                cum[i + 1u] = (uint8_t)s1;
+                if (CUM) cum[i + 1u] = (uint8_t)s1;
                 m = ((uint32_t)two << len1) | 1u;
                 sum = two ? s1 + ((e >> 20) & 15u) + 1u : s1;
                 p += two ? (e & 15u) : len1;
                 i += two ? 2u : 1u;
             } else {
-                chain_step(r, x, p, sum);
+                slow_step(r, x, p, sum, W);
                 i += 1u;
             }
             i = i < kCumSlots - 2u ? i : kCumSlots - 2u;
@@ -398,14 +438,14 @@ __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const X &x,
         cum_top = sum;
     }
     while (p < sn) {
-        const uint32_t e = lut_at(r, x, p);
+        const uint32_t e = lut_step(r, x, p, W);
         if (e & 15u) {
             const uint32_t len1 = (e >> 4) & 15u;
             const bool two = len1 < (e & 15u) && p + len1 < sn;
             sum += ((e >> 8) & 15u) + 1u + (two ? ((e >> 20) & 15u) + 1u : 0u);
             p += two ? (e & 15u) : len1;
         } else {
-            chain_step(r, x, p, sum);
+            slow_step(r, x, p, sum, W);
         }
     }
     ga = sum;
@@ -448,8 +488,9 @@ __device__ __forceinline__ bool extend_chain(const Bits<LDS> &r, const X &x, uin
                                              uint32_t &y, uint32_t &gb) {
     uint32_t p = x0, sum = 0;
     bool found = false;
+    Win W = win_at(r, p);
     while (!meet_stop(p, sn, E, nxt0, nxt1, found)) {
-        const uint32_t e = lut_at(r, x, p);
+        const uint32_t e = lut_step(r, x, p, W);
         if (e & 15u) {
             const uint32_t p1 = p + ((e >> 4) & 15u);
             sum += ((e >> 8) & 15u) + 1u;
@@ -466,6 +507,7 @@ __device__ __forceinline__ bool extend_chain(const Bits<LDS> &r, const X &x, uin
             if (!q) break;
             p = q;
             sum += gap;
+            W = win_at(r, p);
         }
     }
     y = found ? p : E;
@@ -552,8 +594,10 @@ __device__ __forceinline__ void wave_sync() {
 // LDS_OUT: each record's level byte (sign << 7 | k) goes to the group's LDS
 // buffer `lvl` (index = coordinate - lbase, cleared here) and each bucket's
 // RN64(norm / s) to ebs[team]; otherwise every lane writes (ACC: adds) its own
-// output range with a QuadWriter.
-template <bool RAGGED, bool LDS_IN, bool LDS_OUT, bool ACC, int CODE>
+// output range with a QuadWriter. CUM: the lanes' gap-prefix tables live in
+// `lvl` (without them, the gap sum before a sync point is found by walking the
+// speculative chain again).
+template <bool RAGGED, bool LDS_IN, bool LDS_OUT, bool ACC, int CODE, bool CUM>
 __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64_t *offs,
                                              const uint32_t *lut,
                                              const Bits<LDS_IN> &r, uint64_t gbit, uint64_t b0,
@@ -570,6 +614,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
     uint64_t c0 = 0, len = 0;
     double e_b = 0.0;
     uint32_t nl = 0;
+    bool guess = false;
     if (tactive) {
         A = (uint32_t)(offs[b] - gbit);
         E = (uint32_t)(offs[b + 1] - gbit);
@@ -584,6 +629,9 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
                 nl = m < T ? m : T;
                 if (nl == 0) nl = 1;
             }
+            // guess steps pay where table misses are rare on the true chain:
+            // short records, at most kGuessBits payload bits per coordinate
+            guess = (uint64_t)Lp <= (uint64_t)kGuessBits * len;
         }
     }
     if (LDS_OUT && tactive && q == 0) ebs[team] = e_b;
@@ -601,38 +649,33 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
     bool found = false;
     uint8_t *cum = lvl + (uint32_t)lane * kCumSlots;
     uint32_t cum_top = 0;
-    if (act) cx = follow_chain<LDS_IN, true>(r, x, sq, sn, ga, own0, own1, cum, cum_top, q != 0);
+    if (act) cx = follow_chain<LDS_IN, true, CUM>(r, x, sq, sn, ga, own0, own1, cum, cum_top, guess && q != 0);
     if (act && last) found = true;
     // phase B against the next lane's window
     const uint64_t nxt0 = __shfl_down(own0, 1, (int)T);
     const uint64_t nxt1 = __shfl_down(own1, 1, (int)T);
     if (act && !last) found = extend_chain(r, x, cx, sn, E, nxt0, nxt1, ynext, gb);
 
-    // repair: restart, in order, every lane whose predecessor did not meet it.
-    // All lanes below the lowest broken lane of a team are exact and each round
-    // repairs that lane, so the loop ends after at most T rounds.
+    // repair: every lane whose predecessor's chain does not reach its start
+    // (did not meet it) restarts from the predecessor's exit, all such lanes in
+    // the same round. A restarted lane's start is consistent with its
+    // predecessor only while it equals the predecessor's exit; a predecessor
+    // that itself restarts in the same round and exits elsewhere breaks it
+    // again. In each round the lowest broken lane of a team restarts from an
+    // exact predecessor that no longer changes, so the lowest broken lane only
+    // moves up and the loop ends after at most T rounds; then every lane's start
+    // lies on its predecessor's chain, so all chains are exact from lane 0 on.
     bool repaired = false;
     uint32_t rstart = 0;
     while (true) {
         const bool pf = __shfl_up(found ? 1 : 0, 1, (int)T) != 0;
         const uint32_t px = __shfl_up(cx, 1, (int)T);
-        const bool broken = act && q >= 1 && !pf && !repaired;
-        const uint64_t bm = __ballot(broken);
-        if (bm == 0) break;
-        const uint64_t team_mask = (T == 64) ? ~0ull : (((1ull << T) - 1ull) << (team * T));
-        const uint64_t below = bm & team_mask & ((1ull << lane) - 1ull);
-        const bool fix = broken && below == 0;
-        // the predecessor of a restarted lane ends at its own exit
-        const bool succ_fix = __shfl_down(fix ? 1 : 0, 1, (int)T) != 0 && !last;
-        if (act && succ_fix) {
-            ynext = cx;
-            gb = 0;
-            found = true;
-        }
-        if (fix) {
+        const bool broken = act && q >= 1 && !pf;
+        if (__ballot(broken) == 0) break;
+        if (broken) {
             uint64_t d0 = 0, d1 = 0;
             uint32_t dtop = 0;
-            cx = follow_chain<LDS_IN, false>(r, x, px, sn, ga, d0, d1, nullptr, dtop);
+            cx = follow_chain<LDS_IN, false, false>(r, x, px, sn, ga, d0, d1, nullptr, dtop);
             if (last) {
                 found = true;
                 ynext = E;
@@ -642,6 +685,15 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
             }
             repaired = true;
             rstart = px;
+        }
+        // a restarted successor's records begin at its restart point: this
+        // lane's records end at its exit, which must be that point
+        const bool srep = __shfl_down(repaired ? 1 : 0, 1, (int)T) != 0 && !last;
+        const uint32_t srs = __shfl_down(rstart, 1, (int)T);
+        if (act && srep) {
+            found = cx == srs;
+            ynext = cx;
+            gb = 0;
         }
     }
 
@@ -656,11 +708,12 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
     // gaps of the records before the sync point: from the phase A table, else
     // by following the same speculative chain again
     uint32_t gpre = 0;
-    if (act && q >= 1 && !repaired && !cum_lookup(cum, cum_top, own0, own1, ystart - sq, gpre)) {
+    if (act && q >= 1 && !repaired && !(CUM && cum_lookup(cum, cum_top, own0, own1, ystart - sq, gpre))) {
         gpre = 0;
         uint32_t p = sq;
-        guess_steps(r, x, p, sn, gpre);
-        while (p < ystart) chain_step(r, x, p, gpre);
+        Win W = win_at(r, p);
+        if (guess) guess_steps(r, x, p, sn, gpre, W);
+        while (p < ystart) chain_step(r, x, p, gpre, W);
     }
     const uint32_t G = act ? ga + gb - gpre : 0u;
     // team-exclusive prefix sum of the index spans
@@ -683,8 +736,9 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
             uint32_t tix = (uint32_t)(c0 - lbase) + basej - 1u;
             const uint32_t tend = (uint32_t)(c0 - lbase) + (uint32_t)len;
             uint32_t p = ystart;
+            Win W = win_at(r, p);
             while (p < ynext) {
-                const uint32_t e = lut_at(r, x, p);
+                const uint32_t e = lut_step(r, x, p, W);
                 if (e & 15u) {
                     const uint32_t len1 = (e >> 4) & 15u;
                     tix += ((e >> 8) & 15u) + 1u;
@@ -701,6 +755,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
                     tix += gap;
                     lvl[tix < tend ? tix : kLevelSpare] = (uint8_t)((neg << 7) | k);
                     p = nq;
+                    W = win_at(r, p);
                 }
             }
         }
@@ -718,9 +773,10 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
         if (act) {
             uint32_t p = ystart;
             uint64_t jj = (uint64_t)basej - 1u;
+            Win W = win_at(r, p);
             while (p < ynext) {
                 uint32_t gap, neg, k;
-                const uint32_t nq = record_at(r, x, p, gap, neg, k);
+                const uint32_t nq = record_at(r, x, p, gap, neg, k, W);
                 if (!nq) break;
                 jj += gap;
                 if (jj >= hi) break;
@@ -779,6 +835,8 @@ constexpr size_t kStageBytes = (size_t)(kStageWords + kStagePad) * 8;
 constexpr size_t kLevelBytes = (size_t)kGroupCoords + 32;
 constexpr size_t kWaveLdsBytes = kStageBytes + kLevelBytes + 64 * 8;
 static_assert(kStageBytes % 16 == 0 && kLevelBytes % 16 == 0, "LDS carve-out alignment");
+// stream words of a group staged over the stage and the level buffer together
+constexpr int kBigStageWords = (int)((kStageBytes + kLevelBytes) / 8) - kStagePad;
 static_assert(kStageBytes >= 256 * sizeof(float), "the value table reuses the stage");
 // two workgroups per CU (160 KB of LDS)
 static_assert(2 * ((size_t)kDecWaves * kWaveLdsBytes + 16384) <= 160 * 1024, "decode LDS budget");
@@ -830,8 +888,12 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
             uint64_t w1 = E1 > A0 ? ((E1 + 63) >> 6) : w0;
             if (w1 > total_words) w1 = total_words;
             const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
+            // a group whose stream does not fit the stage is staged over the
+            // stage and the level buffer together (each lane then writes its
+            // outputs directly), or, larger still, read from global memory
             const bool in_lds = nw <= (uint64_t)kStageWords;
-            if (in_lds) {
+            const bool in_big = !in_lds && nw <= (uint64_t)kBigStageWords;
+            if (in_lds || in_big) {
                 // bit-reversed words: stream bit 64 i + t of the group in bit t of word i
                 for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64)
                     stage[i] = i < nw ? __builtin_bitreverse64(in[w0 + i]) : 0ull;
@@ -844,12 +906,15 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
             Bits<false> rg{reinterpret_cast<const uint32_t *>(in + w0),
                            (uint32_t)(2 * (total_words - w0)) - 1u};
             if (in_lds)
-                decode_group<RAGGED, true, LDS_OUT, ACC, CODE>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs, lbase,
-                                                         nclear16);
+                decode_group<RAGGED, true, LDS_OUT, ACC, CODE, true>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
+                                                               lbase, nclear16);
+            else if (in_big)
+                decode_group<RAGGED, true, false, ACC, CODE, false>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
+                                                              lbase, nclear16);
             else
-                decode_group<RAGGED, false, LDS_OUT, ACC, CODE>(D, offs, lut, rg, w0 * 64, b0, b1, lvl, ebs,
-                                                          lbase, nclear16);
-            if (LDS_OUT) {
+                decode_group<RAGGED, false, LDS_OUT, ACC, CODE, true>(D, offs, lut, rg, w0 * 64, b0, b1, lvl,
+                                                                ebs, lbase, nclear16);
+            if (LDS_OUT && !in_big) {
                 wave_sync();
                 // the staged stream is done with: its space holds the value table
                 store_group<RAGGED, ACC>(D, lvl, ebs, reinterpret_cast<float *>(stage), lbase, b0, b1);
