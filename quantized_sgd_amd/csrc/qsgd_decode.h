@@ -718,9 +718,13 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
     const uint32_t G = act ? ga + gb - gpre : 0u;
     // team-exclusive prefix sum of the index spans
     uint32_t incl = G;
-    for (uint32_t off = 1; off < T; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off, (int)T);
-        if (q >= off) incl += y;
+    if (T == 64u) {
+        incl = wave_incl_add_u32(G);
+    } else {
+        for (uint32_t off = 1; off < T; off <<= 1) {
+            const uint32_t y = __shfl_up(incl, off, (int)T);
+            if (q >= off) incl += y;
+        }
     }
     const uint32_t basej = incl - G;
 

@@ -8,6 +8,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 namespace qsgd {
@@ -114,6 +115,80 @@ __device__ __forceinline__ T wave_incl_scan(T x, Op op) {
         if (lane >= off) x = op(y, x);
     }
     return x;
+}
+
+// Wave64 inclusive scans of 32-bit values in registers with DPP lane moves
+// (CDNA data-parallel primitives): row_shr 1, 2, 4, 8 scan each row of 16
+// lanes, then row_bcast 15 and row_bcast 31 carry row totals into the later
+// rows. A lane whose source lies outside its row (or a row outside the row
+// mask) reads the identity. wave_shr1 moves each lane's value to the next lane
+// (lane 0 gets the identity), turning an inclusive scan into an exclusive one.
+// Same results as wave_incl_scan for max and +.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143, kDppWaveShr1 = 0x138;
+
+template <int CTRL, int ROWS>
+struct DppPair {
+    static constexpr int first = CTRL, second = ROWS;
+};
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_move(int identity, int x) {
+    return __builtin_amdgcn_update_dpp(identity, x, CTRL, ROWS, 0xf, false);
+}
+
+__device__ __forceinline__ int wave_incl_max_i32(int x) {
+    constexpr int id = INT_MIN;
+    auto mx = [](int a, int b) { return a > b ? a : b; };
+    x = mx(x, dpp_move<kDppRowShr1, 0xf>(id, x));
+    x = mx(x, dpp_move<kDppRowShr2, 0xf>(id, x));
+    x = mx(x, dpp_move<kDppRowShr4, 0xf>(id, x));
+    x = mx(x, dpp_move<kDppRowShr8, 0xf>(id, x));
+    x = mx(x, dpp_move<kDppRowBcast15, 0xa>(id, x));
+    x = mx(x, dpp_move<kDppRowBcast31, 0xc>(id, x));
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_add_u32(uint32_t v) {
+    int x = (int)v;
+    x += dpp_move<kDppRowShr1, 0xf>(0, x);
+    x += dpp_move<kDppRowShr2, 0xf>(0, x);
+    x += dpp_move<kDppRowShr4, 0xf>(0, x);
+    x += dpp_move<kDppRowShr8, 0xf>(0, x);
+    x += dpp_move<kDppRowBcast15, 0xa>(0, x);
+    x += dpp_move<kDppRowBcast31, 0xc>(0, x);
+    return (uint32_t)x;
+}
+
+__device__ __forceinline__ int wave_shr1_i32(int identity, int x) {
+    return dpp_move<kDppWaveShr1, 0xf>(identity, x);
+}
+
+// Total of a double over the wave (MAXN: the maximum of values >= 0), given to
+// every lane. The same DPP steps as above bring the total to lane 63, moving
+// the two 32-bit halves of each double (identity +0.0); a read of lane 63
+// broadcasts it. The combination order is fixed (rows by shifts, then rows
+// 0-1 and 2-3, then the halves), so every call rounds the same way.
+template <bool MAXN>
+__device__ __forceinline__ double wave_total_f64(double v) {
+    auto op = [](double a, double b) { return MAXN ? (a > b ? a : b) : a + b; };
+    auto mv = [](double x, auto ctrl_rows) -> double {
+        constexpr int CTRL = decltype(ctrl_rows)::first, ROWS = decltype(ctrl_rows)::second;
+        const uint64_t b = __double_as_longlong(x);
+        const int lo = dpp_move<CTRL, ROWS>(0, (int)(uint32_t)b);
+        const int hi = dpp_move<CTRL, ROWS>(0, (int)(uint32_t)(b >> 32));
+        return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+    };
+    v = op(v, mv(v, DppPair<kDppRowShr1, 0xf>{}));
+    v = op(v, mv(v, DppPair<kDppRowShr2, 0xf>{}));
+    v = op(v, mv(v, DppPair<kDppRowShr4, 0xf>{}));
+    v = op(v, mv(v, DppPair<kDppRowShr8, 0xf>{}));
+    v = op(v, mv(v, DppPair<kDppRowBcast15, 0xa>{}));
+    v = op(v, mv(v, DppPair<kDppRowBcast31, 0xc>{}));
+    const uint64_t b = __double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // Exclusive block scan; `scratch` holds kWaves entries and must not be reused by

@@ -243,15 +243,14 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
         const int marker = have ? prev : INT_MIN;
 
         // ---- exclusive max-scan of markers: origin of the pending first gap ----
-        int mi = wave_incl_scan(marker, [](int a, int b) { return a > b ? a : b; });
+        int mi = wave_incl_max_i32(marker);
         if (lane == 63) sh_mx[wave] = mi;
         __syncthreads();
         int mpre = INT_MIN;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
             if (w < wave) mpre = mpre > sh_mx[w] ? mpre : sh_mx[w];
-        int mex = __shfl_up(mi, 1, 64);
-        if (lane == 0) mex = INT_MIN;
+        int mex = wave_shr1_i32(INT_MIN, mi);
         mex = mex > mpre ? mex : mpre;
         uint32_t Lp = 0;
         uint64_t pc = 0;
@@ -259,7 +258,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
         const uint32_t bits = r + Lp;
 
         // ---- tile scan of bit counts ----
-        const uint32_t bi = wave_incl_scan(bits, [](uint32_t a, uint32_t b) { return a + b; });
+        const uint32_t bi = wave_incl_add_u32(bits);
         if (lane == 63) sh_bits[wave] = bi;
         __syncthreads();
         uint32_t bpre = 0, T = 0;
@@ -268,8 +267,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
             if (w < wave) bpre += sh_bits[w];
             T += sh_bits[w];
         }
-        uint32_t off = __shfl_up(bi, 1, 64);
-        if (lane == 0) off = 0;
+        uint32_t off = (uint32_t)wave_shr1_i32(0, (int)bi);
         off += bpre;
 
         const uint32_t W = (T + 63u) >> 6;
@@ -342,7 +340,9 @@ __device__ __forceinline__ float aligned_norm(const float (&x)[kCPT], uint32_t G
         acc = MAXN ? op(acc, fabs(y)) : fma(y, y, acc);
     }
     const uint32_t gw = G < 64u ? G : 64u;
-    for (uint32_t o = 1; o < gw; o <<= 1) acc = op(acc, __shfl_xor(acc, (int)o, 64));
+    if (gw == 64u) acc = wave_total_f64<MAXN>(acc);
+    else
+        for (uint32_t o = 1; o < gw; o <<= 1) acc = op(acc, __shfl_xor(acc, (int)o, 64));
     if (G > 64u) {
         const int wave = __builtin_amdgcn_readfirstlane(wave_id());
         if (lane_id() == 0) red[wave] = acc;
@@ -542,7 +542,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         const int marker = have ? prev : INT_MIN;
 
         // ---- exclusive max-scan of markers: origin of the pending first gap ----
-        const int mi = wave_incl_scan(marker, [](int a, int b) { return a > b ? a : b; });
+        const int mi = wave_incl_max_i32(marker);
         if (lane == 63) sh_mx[wave] = mi;
         __syncthreads();
         // the previous tile's words to its slot (each thread clears the words it
@@ -560,8 +560,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
             if (w < wave) mpre = mpre > sh_mx[w] ? mpre : sh_mx[w];
-        int mex = __shfl_up(mi, 1, 64);
-        if (lane == 0) mex = INT_MIN;
+        int mex = wave_shr1_i32(INT_MIN, mi);
         mex = mex > mpre ? mex : mpre;
         uint32_t Lp = 0;
         uint64_t pc = 0;
@@ -569,7 +568,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         const uint32_t bits = r + Lp;
 
         // ---- tile scan of bit counts ----
-        const uint32_t bi = wave_incl_scan(bits, [](uint32_t a, uint32_t b) { return a + b; });
+        const uint32_t bi = wave_incl_add_u32(bits);
         if (lane == 63) sh_bits[wave] = bi;
         __syncthreads();
         uint32_t bpre = 0, T = 0;
@@ -578,8 +577,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
             if (w < wave) bpre += sh_bits[w];
             T += sh_bits[w];
         }
-        uint32_t off = __shfl_up(bi, 1, 64);
-        if (lane == 0) off = 0;
+        uint32_t off = (uint32_t)wave_shr1_i32(0, (int)bi);
         off += bpre;
 
         // ---- OR the thread's pieces into the tile's words ----
