@@ -652,8 +652,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
     if (act) cx = follow_chain<LDS_IN, true, CUM>(r, x, sq, sn, ga, own0, own1, cum, cum_top, guess && q != 0);
     if (act && last) found = true;
     // phase B against the next lane's window
-    const uint64_t nxt0 = __shfl_down(own0, 1, (int)T);
-    const uint64_t nxt1 = __shfl_down(own1, 1, (int)T);
+    const uint64_t nxt0 = lane_next64(own0, T);
+    const uint64_t nxt1 = lane_next64(own1, T);
     if (act && !last) found = extend_chain(r, x, cx, sn, E, nxt0, nxt1, ynext, gb);
 
     // repair: every lane whose predecessor's chain does not reach its start
@@ -668,8 +668,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
     bool repaired = false;
     uint32_t rstart = 0;
     while (true) {
-        const bool pf = __shfl_up(found ? 1 : 0, 1, (int)T) != 0;
-        const uint32_t px = __shfl_up(cx, 1, (int)T);
+        const bool pf = lane_prev(found ? 1u : 0u, T) != 0u;
+        const uint32_t px = lane_prev(cx, T);
         const bool broken = act && q >= 1 && !pf;
         if (__ballot(broken) == 0) break;
         if (broken) {
@@ -688,8 +688,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
         }
         // a restarted successor's records begin at its restart point: this
         // lane's records end at its exit, which must be that point
-        const bool srep = __shfl_down(repaired ? 1 : 0, 1, (int)T) != 0 && !last;
-        const uint32_t srs = __shfl_down(rstart, 1, (int)T);
+        const bool srep = lane_next(repaired ? 1u : 0u, T) != 0u && !last;
+        const uint32_t srs = lane_next(rstart, T);
         if (act && srep) {
             found = cx == srs;
             ynext = cx;
@@ -698,7 +698,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
     }
 
     // exact start of each lane's records
-    const uint32_t py = __shfl_up(ynext, 1, (int)T);
+    const uint32_t py = lane_prev(ynext, T);
     uint32_t ystart = E;
     if (act) {
         if (q == 0) ystart = P0;

@@ -125,7 +125,7 @@ __device__ __forceinline__ T wave_incl_scan(T x, Op op) {
 // (lane 0 gets the identity), turning an inclusive scan into an exclusive one.
 // Same results as wave_incl_scan for max and +.
 constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
-constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143, kDppWaveShr1 = 0x138;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143, kDppWaveShr1 = 0x138, kDppWaveShl1 = 0x130;
 
 template <int CTRL, int ROWS>
 struct DppPair {
@@ -189,6 +189,23 @@ __device__ __forceinline__ double wave_total_f64(double v) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// The previous (next) lane's value within aligned groups of `width` lanes, a
+// lane at its group's edge getting its own value: __shfl_up (__shfl_down) by
+// one, with a DPP wave shift when the group is the whole wave.
+__device__ __forceinline__ uint32_t lane_prev(uint32_t x, uint32_t width) {
+    if (width == 64u) return (uint32_t)dpp_move<kDppWaveShr1, 0xf>((int)x, (int)x);
+    return __shfl_up(x, 1, (int)width);
+}
+
+__device__ __forceinline__ uint32_t lane_next(uint32_t x, uint32_t width) {
+    if (width == 64u) return (uint32_t)dpp_move<kDppWaveShl1, 0xf>((int)x, (int)x);
+    return __shfl_down(x, 1, (int)width);
+}
+
+__device__ __forceinline__ uint64_t lane_next64(uint64_t x, uint32_t width) {
+    return ((uint64_t)lane_next((uint32_t)(x >> 32), width) << 32) | lane_next((uint32_t)x, width);
 }
 
 // Exclusive block scan; `scratch` holds kWaves entries and must not be reused by
