@@ -106,24 +106,12 @@ __device__ __forceinline__ uint32_t omega_len(uint32_t N) {
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 
-template <typename T, typename Op>
-__device__ __forceinline__ T wave_incl_scan(T x, Op op) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const T y = __shfl_up(x, off, 64);
-        if (lane >= off) x = op(y, x);
-    }
-    return x;
-}
-
 // Wave64 inclusive scans of 32-bit values in registers with DPP lane moves
 // (CDNA data-parallel primitives): row_shr 1, 2, 4, 8 scan each row of 16
 // lanes, then row_bcast 15 and row_bcast 31 carry row totals into the later
 // rows. A lane whose source lies outside its row (or a row outside the row
 // mask) reads the identity. wave_shr1 moves each lane's value to the next lane
 // (lane 0 gets the identity), turning an inclusive scan into an exclusive one.
-// Same results as wave_incl_scan for max and +.
 constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
 constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143, kDppWaveShr1 = 0x138, kDppWaveShl1 = 0x130;
 
@@ -135,6 +123,24 @@ struct DppPair {
 template <int CTRL, int ROWS>
 __device__ __forceinline__ int dpp_move(int identity, int x) {
     return __builtin_amdgcn_update_dpp(identity, x, CTRL, ROWS, 0xf, false);
+}
+
+// A 64-bit value moved as two 32-bit halves (identity 0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_move64(uint64_t x) {
+    const int lo = dpp_move<CTRL, ROWS>(0, (int)(uint32_t)x);
+    const int hi = dpp_move<CTRL, ROWS>(0, (int)(uint32_t)(x >> 32));
+    return ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t wave_incl_add_u64(uint64_t x) {
+    x += dpp_move64<kDppRowShr1, 0xf>(x);
+    x += dpp_move64<kDppRowShr2, 0xf>(x);
+    x += dpp_move64<kDppRowShr4, 0xf>(x);
+    x += dpp_move64<kDppRowShr8, 0xf>(x);
+    x += dpp_move64<kDppRowBcast15, 0xa>(x);
+    x += dpp_move64<kDppRowBcast31, 0xc>(x);
+    return x;
 }
 
 __device__ __forceinline__ int wave_incl_max_i32(int x) {
@@ -173,11 +179,8 @@ template <bool MAXN>
 __device__ __forceinline__ double wave_total_f64(double v) {
     auto op = [](double a, double b) { return MAXN ? (a > b ? a : b) : a + b; };
     auto mv = [](double x, auto ctrl_rows) -> double {
-        constexpr int CTRL = decltype(ctrl_rows)::first, ROWS = decltype(ctrl_rows)::second;
-        const uint64_t b = __double_as_longlong(x);
-        const int lo = dpp_move<CTRL, ROWS>(0, (int)(uint32_t)b);
-        const int hi = dpp_move<CTRL, ROWS>(0, (int)(uint32_t)(b >> 32));
-        return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+        return __longlong_as_double((long long)dpp_move64<decltype(ctrl_rows)::first, decltype(ctrl_rows)::second>(
+            (uint64_t)__double_as_longlong(x)));
     };
     v = op(v, mv(v, DppPair<kDppRowShr1, 0xf>{}));
     v = op(v, mv(v, DppPair<kDppRowShr2, 0xf>{}));
@@ -208,25 +211,22 @@ __device__ __forceinline__ uint64_t lane_next64(uint64_t x, uint32_t width) {
     return ((uint64_t)lane_next((uint32_t)(x >> 32), width) << 32) | lane_next((uint32_t)x, width);
 }
 
-// Exclusive block scan; `scratch` holds kWaves entries and must not be reused by
-// another scan before the next __syncthreads(). Returns the block total too.
-template <typename T, typename Op>
-__device__ __forceinline__ T block_excl_scan(T x, Op op, T identity, T *scratch, T &total) {
-    const T incl = wave_incl_scan(x, op);
+// Exclusive block sum of 64-bit values in thread order (DPP wave scans, the
+// waves' totals through `scratch`, kWaves entries, not reused before the next
+// __syncthreads()); also returns the block total.
+__device__ __forceinline__ uint64_t block_excl_add_u64(uint64_t x, uint64_t *scratch, uint64_t &total) {
+    const uint64_t incl = wave_incl_add_u64(x);
     const int lane = lane_id(), wave = wave_id();
     if (lane == 63) scratch[wave] = incl;
     __syncthreads();
-    T prefix = identity;
-    T tot = identity;
+    uint64_t prefix = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-        if (w < wave) prefix = op(prefix, scratch[w]);
-        tot = op(tot, scratch[w]);
+        if (w < wave) prefix += scratch[w];
+        tot += scratch[w];
     }
-    T ex = __shfl_up(incl, 1, 64);
-    if (lane == 0) ex = identity;
     total = tot;
-    return op(prefix, ex);
+    return prefix + dpp_move64<kDppWaveShr1, 0xf>(incl);
 }
 
 // Segmented inclusive scan of (flag, value) over the block in thread order:

@@ -696,9 +696,8 @@ __global__ __launch_bounds__(kWG) void encode_finish_kernel(FinishParams F) {
     uint64_t acc = 0;
     for (uint32_t i = (uint32_t)j; i < r0; i += kWG) acc += F.run_bits[i];
     for (uint32_t t = run_first(r0, F.run, F.rem) + (uint32_t)j; t < t0; t += kWG) acc += F.tile_bits[t];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (lane == 0) sh_red[wave] = acc;
+    acc = wave_incl_add_u64(acc);
+    if (lane == 63) sh_red[wave] = acc;
     __syncthreads();
     uint64_t pre = 0;
 #pragma unroll
@@ -707,8 +706,7 @@ __global__ __launch_bounds__(kWG) void encode_finish_kernel(FinishParams F) {
     const uint32_t m = t1 - t0;
     const uint64_t mine = (uint32_t)j < m ? (uint64_t)F.tile_bits[t0 + j] : 0ull;
     uint64_t total = 0;
-    const uint64_t ex = block_excl_scan(mine, [](uint64_t a, uint64_t b) { return a + b; }, (uint64_t)0,
-                                        sh_scan, total);
+    const uint64_t ex = block_excl_add_u64(mine, sh_scan, total);
     if ((uint32_t)j < m) sh_base[j] = pre + ex;
     if (j == 0) sh_base[m] = pre + total;  // end of the share
     __syncthreads();
