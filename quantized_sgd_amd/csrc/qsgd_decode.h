@@ -813,18 +813,31 @@ __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t
         }
         wave_sync();
         const uint64_t qa = A >> 2, qb = (B + 3) >> 2;
-        for (uint64_t qd = qa + lane; qd < qb; qd += 64) {
-            const uint64_t a = qd << 2;
-            const uint32_t word = lw[(a - lbase) >> 2];
-            const float v0 = tbl[word & 0xffu], v1 = tbl[(word >> 8) & 0xffu];
-            const float v2 = tbl[(word >> 16) & 0xffu], v3 = tbl[word >> 24];
-            if (a >= A && a + 4 <= B) {
-                QuadWriter<ACC>::put4(D.v_hat + a, make_float4(v0, v1, v2, v3));
-            } else {
-                if (a >= A && a < B) QuadWriter<ACC>::put1(D.v_hat + a, v0);
-                if (a + 1 >= A && a + 1 < B) QuadWriter<ACC>::put1(D.v_hat + a + 1, v1);
-                if (a + 2 >= A && a + 2 < B) QuadWriter<ACC>::put1(D.v_hat + a + 2, v2);
-                if (a + 3 >= A && a + 3 < B) QuadWriter<ACC>::put1(D.v_hat + a + 3, v3);
+        if (((A | B) & 3u) == 0) {
+            // whole quads only: 32-bit quad indices from the bucket's first quad
+            const uint32_t nq = (uint32_t)(qb - qa);
+            const uint32_t *lq = lw + ((A - lbase) >> 2);
+            float4 *oq = reinterpret_cast<float4 *>(D.v_hat + A);
+            for (uint32_t i = lane; i < nq; i += 64) {
+                const uint32_t word = lq[i];
+                const float4 v = make_float4(tbl[word & 0xffu], tbl[(word >> 8) & 0xffu],
+                                             tbl[(word >> 16) & 0xffu], tbl[word >> 24]);
+                QuadWriter<ACC>::put4(reinterpret_cast<float *>(oq + i), v);
+            }
+        } else {
+            for (uint64_t qd = qa + lane; qd < qb; qd += 64) {
+                const uint64_t a = qd << 2;
+                const uint32_t word = lw[(a - lbase) >> 2];
+                const float v0 = tbl[word & 0xffu], v1 = tbl[(word >> 8) & 0xffu];
+                const float v2 = tbl[(word >> 16) & 0xffu], v3 = tbl[word >> 24];
+                if (a >= A && a + 4 <= B) {
+                    QuadWriter<ACC>::put4(D.v_hat + a, make_float4(v0, v1, v2, v3));
+                } else {
+                    if (a >= A && a < B) QuadWriter<ACC>::put1(D.v_hat + a, v0);
+                    if (a + 1 >= A && a + 1 < B) QuadWriter<ACC>::put1(D.v_hat + a + 1, v1);
+                    if (a + 2 >= A && a + 2 < B) QuadWriter<ACC>::put1(D.v_hat + a + 2, v2);
+                    if (a + 3 >= A && a + 3 < B) QuadWriter<ACC>::put1(D.v_hat + a + 3, v3);
+                }
             }
         }
         // the table is rebuilt for the next bucket
