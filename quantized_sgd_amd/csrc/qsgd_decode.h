@@ -1,4 +1,4 @@
-// Decoder: parses the Elias-omega stream and dequantizes.
+// Decoder: parses the Elias-omega (or Elias-gamma) stream and dequantizes.
 //
 // Page "QSGD (Quantized Stochastic Gradient Descent) with Elias Coding",
 // definition paragraph: the coding is lossless, so decode inverts it exactly;
@@ -21,18 +21,24 @@
 //            chain, so that position is the first true boundary of lane q+1's
 //            chain: lane q+1's records are exact from there.
 //   repair:  if lane q's chain does not meet lane q+1's within 128 bits, lane q+1
-//            restarts from lane q's true exit; pairs are repaired in order.
+//            restarts from lane q's exit; all such lanes restart together, and
+//            again while a restarted predecessor exits elsewhere.
 //   count:   each lane's index span is the sum of the gaps of its exact records
-//            (phase A + B sums minus those before its sync point, re-parsed);
-//            a team prefix sum gives absolute indices.
+//            (phase A + B sums minus those before its sync point, from the gap
+//            sums noted in phase A or parsed again); a team prefix sum gives
+//            absolute indices.
 //   write:   each lane parses its exact range again. For levels that fit a byte
 //            and groups of at most 4096 coordinates, it stores (sign, k) bytes
 //            in an LDS copy of the group, which the wave then dequantizes and
 //            writes with coalesced 16-byte stores; otherwise each lane writes
 //            its own index range directly.
-// Record parsing reads the 64 stream bits at any bit position from LDS (two
-// dwords) and looks the next 12 bits up in a table that decodes a whole record
-// (gap <= 16, k <= 16) at once; other records take the general omega loop.
+// Record parsing looks the next 12 stream bits up in a table that decodes one or
+// two whole records (gap <= 16, k <= 16) at once; other records take the
+// general omega (or gamma) loop. A walk keeps a 64-bit window of the stream,
+// read from LDS at its current position together with that position's table
+// entry, which holds the next step's table bits. Groups whose stream passes the
+// stage are staged over the stage and the level buffer together, or read from
+// global memory.
 #pragma once
 
 #include "qsgd_device.h"

@@ -31,9 +31,9 @@
 namespace qsgd {
 
 // Record code table for s <= kTabS: entry (code << 5) | length of
-// c(g) | sign | c(k) (c: the record fields' code; at most 23 bits) for g in [0, 16] (g = 0: no gap code) and k in
-// [0, s] (k = 0: no record, entry 0). Index ((k * 17 + g) << 1) | sign, which
-// needs no integer multiply (k * 17 = (k << 4) + k).
+// c(g) | sign | c(k) (c: the record fields' code; at most 23 bits) for g in
+// [0, 16] (g = 0: no gap code) and k in [0, s] (k = 0: no record, entry 0).
+// Index ((k * 17 + g) << 1) | sign.
 constexpr uint32_t kTabS = 64;
 constexpr uint32_t kTabG = 17;
 
