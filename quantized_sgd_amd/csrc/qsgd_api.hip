@@ -203,7 +203,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     };
     // pass 1: every tile into its slot
     if (use_aligned(bstart, s, d)) {
-        const size_t lds = aligned_encode_lds_bytes(p.obuf_words, s);
+        const size_t lds = aligned_encode_lds_bytes(p.obuf_words);
         // long thread halves are common when levels are large: mean level about
         // 0.8 s / sqrt(d) under the L2 norm, 0.8 s / max|z| (about s / 4) under
         // the max-norm; past about 2 a half's 8 records pass 64 bits

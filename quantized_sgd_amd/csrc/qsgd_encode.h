@@ -67,6 +67,70 @@ __device__ inline void build_code_table(uint32_t *rt, uint32_t s, uint32_t fcode
     }
 }
 
+// The same table for s = kTabS, computed at compile time for each code (the
+// entries of k <= s serve any s <= kTabS): the aligned encoder reads it from
+// constant memory through the vector L1 cache instead of building it in LDS.
+constexpr uint32_t ct_bitlen(uint32_t m) {
+    uint32_t b = 0;
+    while (m) {
+        ++b;
+        m >>= 1;
+    }
+    return b;
+}
+
+// Elias omega (CODE 0) or gamma (CODE 1) codeword of N >= 1, right-aligned.
+template <int CODE>
+constexpr uint64_t ct_field_code(uint32_t N, uint32_t &L) {
+    if (CODE) {
+        L = 2u * ct_bitlen(N) - 1u;
+        return N;
+    }
+    uint64_t code = 0;
+    L = 1;
+    uint32_t m = N;
+    while (m > 1u) {
+        const uint32_t b = ct_bitlen(m);
+        code |= (uint64_t)m << L;
+        L += b;
+        m = b - 1u;
+    }
+    return code;
+}
+
+struct alignas(16) CodeTable {
+    uint32_t e[kTabG * (kTabS + 1) * 2];
+};
+
+template <int CODE>
+constexpr CodeTable make_code_table() {
+    CodeTable t{};
+    for (uint32_t i = 0; i < kTabG * (kTabS + 1) * 2; ++i) {
+        const uint32_t neg = i & 1u;
+        const uint32_t g = (i >> 1) % kTabG;
+        const uint32_t k = (i >> 1) / kTabG;
+        uint32_t e = 0;
+        if (k) {
+            uint32_t Lk = 0;
+            const uint64_t kc = ct_field_code<CODE>(k, Lk);
+            uint64_t code = ((uint64_t)neg << Lk) | kc;
+            uint32_t len = Lk + 1;
+            if (g) {
+                uint32_t Lg = 0;
+                const uint64_t gc = ct_field_code<CODE>(g, Lg);
+                code |= gc << len;
+                len += Lg;
+            }
+            e = ((uint32_t)code << 5) | len;
+        }
+        t.e[i] = e;
+    }
+    return t;
+}
+
+__constant__ CodeTable kCodeTableOmega = make_code_table<0>();
+__constant__ CodeTable kCodeTableGamma = make_code_table<1>();
+
 // OR a left-aligned bit string (len <= 64 bits at the top of `word`) into the
 // LDS word window at bit position pos.
 __device__ __forceinline__ void or_bits(uint64_t *buf, uint32_t pos, uint64_t word, uint32_t len) {
@@ -411,9 +475,8 @@ __global__ __launch_bounds__(kWG) void quantize_aligned_kernel(QsgdParams P, uin
 //   - each thread ORs its bit string (norm or pending first gap, then its two
 //     record registers) into the tile's LDS words at its offset, and the words
 //     go to the tile's slot.
-__host__ __device__ constexpr size_t aligned_encode_lds_bytes(uint32_t obuf_words, uint32_t s) {
-    return align16((size_t)obuf_words * 8) + align16((size_t)code_table_entries(s) * 4) +
-           (size_t)kTC * 4;
+__host__ __device__ constexpr size_t aligned_encode_lds_bytes(uint32_t obuf_words) {
+    return align16((size_t)obuf_words * 8) + (size_t)kTC * 4;
 }
 
 // Starts copying the 4096 coordinates of a whole tile from v[g] into LDS
@@ -454,12 +517,11 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
     __shared__ uint32_t sh_bits[kWaves];
     __shared__ double sh_red[kWaves];
 
-    // dynamic LDS: [obuf][rt][pbuf] (aligned_encode_lds_bytes)
+    // dynamic LDS: [obuf][pbuf] (aligned_encode_lds_bytes); the record code
+    // table is read from constant memory
     uint64_t *obuf = reinterpret_cast<uint64_t *>(smem);
-    uint32_t *rt = reinterpret_cast<uint32_t *>(smem + align16((size_t)P.obuf_words * 8));
-    float *pbuf = reinterpret_cast<float *>(smem + align16((size_t)P.obuf_words * 8) +
-                                            align16((size_t)code_table_entries(P.s) * 4));
-    build_code_table(rt, P.s, P.code);
+    float *pbuf = reinterpret_cast<float *>(smem + align16((size_t)P.obuf_words * 8));
+    const uint32_t *rt = P.code ? kCodeTableGamma.e : kCodeTableOmega.e;
     const int j = (int)threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
