@@ -82,11 +82,11 @@ EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool align
     p.slot_region_words = (p.ntiles * p.obuf_words + 1) & ~(uint64_t)1;
     p.ws_words = p.slot_region_words + (p.ntiles + 1) / 2 + kMaxRuns;
     p.table = s <= kTabS;
-    p.lds_bytes = EncodeLayout(p.obuf_words, p.table ? code_table_entries(s) : 0u, p.K).total;
+    p.lds_bytes = EncodeLayout(p.obuf_words, p.K).total;
     return p;
 }
 
-size_t quantize_lds_bytes(const EncodePlan &p) { return EncodeLayout(0, 0, p.K).total; }
+size_t quantize_lds_bytes(const EncodePlan &p) { return EncodeLayout(0, p.K).total; }
 
 // Workgroups of a kernel that fit on the current device at once (cached per
 // kernel, LDS size and device; safe to call from several host threads).

@@ -43,33 +43,9 @@ __device__ __forceinline__ uint32_t code_index(uint32_t g, uint32_t k, uint32_t 
     return ((((k << 4) + k) + g) << 1) | neg;
 }
 
-__device__ inline void build_code_table(uint32_t *rt, uint32_t s, uint32_t fcode) {
-    const uint32_t n = code_table_entries(s);
-    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
-        const uint32_t neg = i & 1u;
-        const uint32_t g = (i >> 1) % kTabG;
-        const uint32_t k = (i >> 1) / kTabG;
-        uint32_t e = 0;
-        if (k) {
-            uint32_t Lk;
-            const uint64_t kc = field_code(fcode, k, Lk);
-            uint64_t code = ((uint64_t)neg << Lk) | kc;
-            uint32_t len = Lk + 1;
-            if (g) {
-                uint32_t Lg;
-                const uint64_t gc = field_code(fcode, g, Lg);
-                code |= gc << len;
-                len += Lg;
-            }
-            e = ((uint32_t)code << 5) | len;
-        }
-        rt[i] = e;
-    }
-}
-
-// The same table for s = kTabS, computed at compile time for each code (the
-// entries of k <= s serve any s <= kTabS): the aligned encoder reads it from
-// constant memory through the vector L1 cache instead of building it in LDS.
+// The table for s = kTabS, computed at compile time for each code (the entries
+// of k <= s serve any s <= kTabS); the encoders read it from constant memory
+// through the vector L1 cache.
 constexpr uint32_t ct_bitlen(uint32_t m) {
     uint32_t b = 0;
     while (m) {
@@ -99,13 +75,13 @@ constexpr uint64_t ct_field_code(uint32_t N, uint32_t &L) {
 }
 
 struct alignas(16) CodeTable {
-    uint32_t e[kTabG * (kTabS + 1) * 2];
+    uint32_t e[code_table_entries(kTabS)];
 };
 
 template <int CODE>
 constexpr CodeTable make_code_table() {
     CodeTable t{};
-    for (uint32_t i = 0; i < kTabG * (kTabS + 1) * 2; ++i) {
+    for (uint32_t i = 0; i < code_table_entries(kTabS); ++i) {
         const uint32_t neg = i & 1u;
         const uint32_t g = (i >> 1) % kTabG;
         const uint32_t k = (i >> 1) / kTabG;
@@ -144,18 +120,16 @@ __device__ __forceinline__ void or_bits(uint64_t *buf, uint32_t pos, uint64_t wo
 struct EncodeLds {
     FrontLds f;
     uint64_t *obuf;
-    uint32_t *rt;   // record code table (table path)
 };
 
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// Dynamic LDS layout shared by host and device: [obuf][rt][cb][segv][bs][nrm][segf].
+// Dynamic LDS layout shared by host and device: [obuf][cb][segv][bs][nrm][segf].
 struct EncodeLayout {
-    size_t obuf, rt, cb, segv, bs, nrm, segf, total;
-    __host__ __device__ EncodeLayout(uint32_t obuf_words, uint32_t rt_entries, uint32_t K) {
+    size_t obuf, cb, segv, bs, nrm, segf, total;
+    __host__ __device__ EncodeLayout(uint32_t obuf_words, uint32_t K) {
         size_t off = 0;
         obuf = off; off = align16(off + (size_t)obuf_words * 8);
-        rt = off;   off = align16(off + (size_t)rt_entries * 4);
         cb = off;   off = align16(off + (size_t)K * 8);
         segv = off; off = align16(off + kWaves * 8);
         bs = off;   off = align16(off + (size_t)(K + 1) * 4);
@@ -165,12 +139,10 @@ struct EncodeLayout {
     }
 };
 
-__device__ __forceinline__ EncodeLds carve_encode_lds(unsigned char *smem, const QsgdParams &P,
-                                                      uint32_t rt_entries) {
-    const EncodeLayout lay(P.obuf_words, rt_entries, P.K);
+__device__ __forceinline__ EncodeLds carve_encode_lds(unsigned char *smem, const QsgdParams &P) {
+    const EncodeLayout lay(P.obuf_words, P.K);
     EncodeLds L;
     L.obuf = reinterpret_cast<uint64_t *>(smem + lay.obuf);
-    L.rt = reinterpret_cast<uint32_t *>(smem + lay.rt);
     L.f.cb = reinterpret_cast<double *>(smem + lay.cb);
     L.f.segv = reinterpret_cast<double *>(smem + lay.segv);
     L.f.bs = reinterpret_cast<int32_t *>(smem + lay.bs);
@@ -182,7 +154,7 @@ __device__ __forceinline__ EncodeLds carve_encode_lds(unsigned char *smem, const
 template <bool RAGGED>
 __global__ __launch_bounds__(kWG) void quantize_kernel(QsgdParams P) {
     extern __shared__ __align__(16) unsigned char smem[];
-    EncodeLds L = carve_encode_lds(smem, P, 0);
+    EncodeLds L = carve_encode_lds(smem, P);
     const uint32_t tile = blockIdx.x;
     const Tile t = tile_geometry<RAGGED>(P, tile);
     fill_bucket_starts<RAGGED>(P, t, L.f);
@@ -254,9 +226,8 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
     __shared__ int sh_mx[kWaves];
     __shared__ uint32_t sh_bits[kWaves];
 
-    const uint32_t rt_entries = TABLE ? code_table_entries(P.s) : 0u;
-    EncodeLds L = carve_encode_lds(smem, P, rt_entries);
-    if (TABLE) build_code_table(L.rt, P.s, P.code);
+    EncodeLds L = carve_encode_lds(smem, P);
+    const uint32_t *rt = P.code ? kCodeTableGamma.e : kCodeTableOmega.e;
     const int j = (int)threadIdx.x;
     const int lane = lane_id();
     // the wave index as a scalar, so that branches on it are uniform to the compiler
@@ -294,7 +265,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
             const uint32_t k = lv.k[q];
             const uint32_t g = have ? (uint32_t)(x - prev) : 0u;
             uint64_t code;
-            const uint32_t len = record_entry<TABLE>(L.rt, g, k, (lv.neg >> q) & 1u, code, P.code);
+            const uint32_t len = record_entry<TABLE>(rt, g, k, (lv.neg >> q) & 1u, code, P.code);
             if (TABLE) ec[q] = ((uint32_t)code << 5) | len;
             else { ec[q] = len; ecx[TABLE ? 0 : q] = code; }
             r += len;
