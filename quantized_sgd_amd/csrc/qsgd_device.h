@@ -211,6 +211,32 @@ __device__ __forceinline__ uint64_t lane_next64(uint64_t x, uint32_t width) {
     return ((uint64_t)lane_next((uint32_t)(x >> 32), width) << 32) | lane_next((uint32_t)x, width);
 }
 
+// Total of a double over each half of the wave (lanes 0-31 and 32-63; MAXN:
+// the maximum of values >= 0), given to the lanes of that half: the row steps
+// of wave_total_f64, then row_bcast 15 into rows 1 and 3 only, so lanes 31 and
+// 63 hold the halves' totals.
+template <bool MAXN>
+__device__ __forceinline__ double half_wave_total_f64(double v) {
+    auto op = [](double a, double b) { return MAXN ? (a > b ? a : b) : a + b; };
+    auto mv = [](double x, auto ctrl_rows) -> double {
+        return __longlong_as_double((long long)dpp_move64<decltype(ctrl_rows)::first, decltype(ctrl_rows)::second>(
+            (uint64_t)__double_as_longlong(x)));
+    };
+    v = op(v, mv(v, DppPair<kDppRowShr1, 0xf>{}));
+    v = op(v, mv(v, DppPair<kDppRowShr2, 0xf>{}));
+    v = op(v, mv(v, DppPair<kDppRowShr4, 0xf>{}));
+    v = op(v, mv(v, DppPair<kDppRowShr8, 0xf>{}));
+    v = op(v, mv(v, DppPair<kDppRowBcast15, 0xa>{}));
+    const uint64_t b = __double_as_longlong(v);
+    const uint32_t src = lane_id() < 32 ? 31u : 63u;
+    const uint32_t lo0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 31);
+    const uint32_t hi0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 31);
+    const uint32_t lo1 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+    const uint32_t hi1 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+    const uint32_t lo = src == 31u ? lo0 : lo1, hi = src == 31u ? hi0 : hi1;
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // Exclusive block sum of 64-bit values in thread order (DPP wave scans, the
 // waves' totals through `scratch`, kWaves entries, not reused before the next
 // __syncthreads()); also returns the block total.

@@ -376,6 +376,7 @@ __device__ __forceinline__ float aligned_norm(const float (&x)[kCPT], uint32_t G
     }
     const uint32_t gw = G < 64u ? G : 64u;
     if (gw == 64u) acc = wave_total_f64<MAXN>(acc);
+    else if (gw == 32u) acc = half_wave_total_f64<MAXN>(acc);
     else
         for (uint32_t o = 1; o < gw; o <<= 1) acc = op(acc, __shfl_xor(acc, (int)o, 64));
     if (G > 64u) {
