@@ -83,6 +83,34 @@ def test_zero_buckets_and_spikes():
     check_parity(v, 16, d, 3)
 
 
+def test_chain_repairs_out_of_phase():
+    """Streams on which the decoder's speculative chains never meet the true one.
+    Under the max-norm with s = 1 a constant positive bucket has level 1 at every
+    coordinate (r = 1 exactly), so each record is the three bits 000 and the
+    payload is all zeros: a chain started 1 or 2 bits off a record boundary stays
+    off it to the end. With a segment length that is not a multiple of 3, lanes
+    start in all three phases, so most lanes are restarted, and a lane restarted
+    from a predecessor that is itself restarted must be restarted again. The
+    bucket lengths below (ragged, buckets of at most 4000) give 7 to 64 lanes of
+    129 to 188 bits, seven buckets out of phase."""
+    s, d = 1, 4000
+    seg = np.array([1000, 4096, 1001, 333, 3100, 650, 2500, 4000, 2731], dtype=np.int64)
+    v = np.full(int(seg.sum()), 0.5, dtype=np.float32)
+    v[4096 + 1000:4096 + 1000 + 1001] = 2.0   # a second constant
+    bst = oracle.ragged_buckets(seg, d)
+    _, _, _, offs, _ = oracle.compress(v, bst, s, 7, norms=oracle.bucket_max_norms(v, bst))
+    # the payload lengths give decoder segments that are not multiples of 3 bits
+    out_of_phase = 0
+    for b in range(len(bst) - 1):
+        lp = int(offs[b + 1] - offs[b]) - 32
+        assert lp == 3 * int(bst[b + 1] - bst[b])
+        nl = max(1, min(64, lp // 128))
+        out_of_phase += ((lp + nl - 1) // nl) % 3 != 0
+    assert out_of_phase >= 5
+    check_parity(v, s, d, 7, seg_len=seg, norm=q.MAXNORM)
+    check_parity(v, s, d, 8, seg_len=seg, norm=q.MAXNORM, code=oracle.GAMMA)
+
+
 def test_integer_valued_norms_are_exact():
     # small integers: every partial sum is exact in fp64, so GPU and oracle norms
     # must agree bit for bit whatever the summation order
