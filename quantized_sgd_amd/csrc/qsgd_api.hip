@@ -193,8 +193,8 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     P.obuf_words = p.obuf_words;
     P.code = code;
     P.maxnorm = norm;
-    // pass 1 grid: at most the resident workgroups (and kMaxRuns), each taking a
-    // run of consecutive tiles
+    // pass 1 grid: at most the given number of workgroups (and kMaxRuns), each
+    // taking a run of consecutive tiles
     auto runs_for = [&](uint32_t resident) {
         const uint64_t g = std::min<uint64_t>(std::min<uint64_t>(p.ntiles, resident), kMaxRuns);
         P.run = (uint32_t)(p.ntiles / g);
@@ -208,8 +208,12 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
         // 0.8 s / sqrt(d) under the L2 norm, 0.8 s / max|z| (about s / 4) under
         // the max-norm; past about 2 a half's 8 records pass 64 bits
         const bool levels = norm == QSGD_NORM_MAX ? s >= 8 : (uint64_t)s * s >= 6ull * d;
+        // twice the resident workgroups: the second half starts as workgroups of
+        // the first finish, which evens out the end of the pass (per encode, c3:
+        // 115.7 -> 109.2 us, c2: 54.9 -> 54.0, c4: 455 -> 442; on c3 1.5 times is
+        // slower than once, 2.5 and 4 times a little slower than twice)
         auto launch = [&](auto kernel) {
-            const uint32_t blocks = runs_for(resident_blocks(kernel, lds));
+            const uint32_t blocks = runs_for(2 * resident_blocks(kernel, lds));
             hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), lds, stream, P, log2u(d));
         };
         if (levels) launch(encode_aligned_kernel<true>);
@@ -278,6 +282,8 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
     const uint64_t groups = (nb + tpw - 1) / tpw;
     const uint64_t want = (groups + kDecWaves - 1) / kDecWaves;
     const size_t lds = decode_lds_bytes();
+    // the resident workgroups (twice as many: c3 119 -> 118.6 us, but c2 61.6 ->
+    // 64.9 us, where that gives every group a workgroup of its own)
     auto launch = [&](auto kernel) {
         const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, resident_blocks(kernel, lds, kDecWG));
         hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kDecWG), lds, stream, D);
