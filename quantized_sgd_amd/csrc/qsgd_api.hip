@@ -219,8 +219,9 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
         if (levels) launch(encode_aligned_kernel<true>);
         else launch(encode_aligned_kernel<false>);
     } else {
+        // twice the resident workgroups too (c5: 221 -> 211 us per encode)
         auto launch = [&](auto kernel) {
-            const uint32_t blocks = runs_for(resident_blocks(kernel, p.lds_bytes));
+            const uint32_t blocks = runs_for(2 * resident_blocks(kernel, p.lds_bytes));
             hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), p.lds_bytes, stream, P);
         };
         if (ragged) {
