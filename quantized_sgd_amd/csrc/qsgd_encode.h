@@ -247,13 +247,21 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
         ThreadLevels lv;
         quantize_coords(P, t, L.f, c, lv);
 
-        // ---- phase 1: record codes, bit count, last marker ----
+        // ---- phase 1: record codes, bit count, last marker; with the table, the
+        // norms of buckets starting here and the records are also packed
+        // right-aligned into two 64-bit registers (coordinates 0-7 and 8-15) ----
         uint32_t ec[kCPT];
         uint64_t ecx[TABLE ? 1 : kCPT];
+        uint64_t racc[2] = {0, 0};
+        uint32_t rlen[2] = {0, 0};
         uint32_t r = 0;
         int prev = 0;
         int have = 0;
         int pendx = -1;
+        // the tile-local bucket before the thread's first bucket start
+        int kb0 = c.kf;
+        if (c.vx0 < c.vx1 && ((lv.bst >> (c.vx0 - j * kCPT)) & 1u)) kb0 -= 1;
+        int kbp = kb0;
 #pragma unroll
         for (int q = 0; q < kCPT; ++q) {
             const int x = j * kCPT + q;
@@ -261,6 +269,11 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
                 r += 32u;
                 prev = x - 1;
                 have = 1;
+                if (TABLE) {
+                    ++kbp;
+                    racc[q >> 3] = (racc[q >> 3] << 32) | (uint64_t)__float_as_uint(L.f.nrm[kbp]);
+                    rlen[q >> 3] += 32u;
+                }
             }
             const uint32_t k = lv.k[q];
             const uint32_t g = have ? (uint32_t)(x - prev) : 0u;
@@ -268,6 +281,10 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
             const uint32_t len = record_entry<TABLE>(rt, g, k, (lv.neg >> q) & 1u, code, P.code);
             if (TABLE) ec[q] = ((uint32_t)code << 5) | len;
             else { ec[q] = len; ecx[TABLE ? 0 : q] = code; }
+            if (TABLE) {
+                racc[q >> 3] = (racc[q >> 3] << len) | code;
+                rlen[q >> 3] += len;
+            }
             r += len;
             if (k) {
                 if (!have) pendx = x;
@@ -313,8 +330,27 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
         uint32_t p = off;
         if (Lp) or_bits(L.obuf, p, pc << (64u - Lp), Lp);
         p += Lp;
-        int kb = c.kf;
-        if (c.vx0 < c.vx1 && ((lv.bst >> (c.vx0 - j * kCPT)) & 1u)) kb -= 1;
+        int kb = kb0;
+        if (TABLE && rlen[0] <= 64u && rlen[1] <= 64u) {
+            // the two packed registers; the bucket offsets from the record lengths
+            if (lv.bst) {
+                uint32_t pp = p;
+#pragma unroll
+                for (int q = 0; q < kCPT; ++q) {
+                    if ((lv.bst >> q) & 1u) {
+                        ++kb;
+                        P.offsets[t.b0 + kb] = pp;
+                        pp += 32u;
+                    }
+                    pp += ec[q] & 31u;
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (rlen[h]) or_bits(L.obuf, p, racc[h] << (64u - rlen[h]), rlen[h]);
+                p += rlen[h];
+            }
+        } else {
 #pragma unroll
         for (int q = 0; q < kCPT; ++q) {
             if ((lv.bst >> q) & 1u) {
@@ -329,6 +365,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(QsgdParams P) {
                 or_bits(L.obuf, p, code << (64u - len), len);
             }
             p += len;
+        }
         }
         __syncthreads();
 
