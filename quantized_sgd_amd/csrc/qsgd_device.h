@@ -255,7 +255,30 @@ __device__ __forceinline__ uint64_t block_excl_add_u64(uint64_t x, uint64_t *scr
     return prefix + dpp_move64<kDppWaveShr1, 0xf>(incl);
 }
 
-// Segmented inclusive scan of (flag, value) over the block in thread order:
+// Segmented inclusive scan over the wave in lane order with DPP lane moves (the
+// row shifts and broadcasts of the scans above; a lane that receives nothing
+// takes (0, 0), the identity): (v, f) becomes the combination of lanes
+// 0..lane, a set flag starting a new segment.
+template <bool MAXN>
+__device__ __forceinline__ void wave_seg_incl_f64(double &v, int &f) {
+    auto op = [](double a, double b) { return MAXN ? (a > b ? a : b) : a + b; };
+    auto step = [&](auto ctrl_rows) {
+        constexpr int C = decltype(ctrl_rows)::first, R = decltype(ctrl_rows)::second;
+        const double yv = __longlong_as_double((long long)dpp_move64<C, R>((uint64_t)__double_as_longlong(v)));
+        const int yf = dpp_move<C, R>(0, f);
+        if (!f) v = op(yv, v);
+        f |= yf;
+    };
+    step(DppPair<kDppRowShr1, 0xf>{});
+    step(DppPair<kDppRowShr2, 0xf>{});
+    step(DppPair<kDppRowShr4, 0xf>{});
+    step(DppPair<kDppRowShr8, 0xf>{});
+    step(DppPair<kDppRowBcast15, 0xa>{});
+    step(DppPair<kDppRowBcast31, 0xc>{});
+}
+
+// Segmented inclusive scan of (flag, value) over the block in thread order (the
+// waves by wave_seg_incl_f64, then in wave order through sv/sf):
 // S_j = v_j if f_j else S_{j-1} + v_j. Returns S_{j-1} (the exclusive value; 0
 // for thread 0). Used for bucket sums of squares that span several threads.
 // MAXN: the same scan with max in place of + (for bucket max-norms; the values
@@ -264,15 +287,7 @@ template <bool MAXN = false>
 __device__ __forceinline__ double block_seg_excl_sum(double v, int f, double *sv, int *sf) {
     const int lane = lane_id(), wave = wave_id();
     auto op = [](double a, double b) { return MAXN ? (a > b ? a : b) : a + b; };
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double yv = __shfl_up(v, off, 64);
-        const int yf = __shfl_up(f, off, 64);
-        if (lane >= off) {
-            if (!f) v = op(yv, v);
-            f |= yf;
-        }
-    }
+    wave_seg_incl_f64<MAXN>(v, f);
     if (lane == 63) { sv[wave] = v; sf[wave] = f; }
     __syncthreads();
     double pv = 0.0;
@@ -280,7 +295,9 @@ __device__ __forceinline__ double block_seg_excl_sum(double v, int f, double *sv
         if (sf[w]) pv = sv[w]; else pv = op(pv, sv[w]);
     }
     const double incl = f ? v : op(pv, v);
-    double ex = __shfl_up(incl, 1, 64);
+    // the previous lane's inclusive value; lane 0 takes the earlier waves'
+    double ex = __longlong_as_double(
+        (long long)dpp_move64<kDppWaveShr1, 0xf>((uint64_t)__double_as_longlong(incl)));
     if (lane == 0) ex = pv;
     return ex;
 }
