@@ -181,6 +181,56 @@ constexpr RecordLut make_record_lut() {
 __constant__ RecordLut kRecordLut = make_record_lut<0>();
 __constant__ RecordLut kRecordLutGamma = make_record_lut<1>();
 
+// Field table: the codeword of one field (omega or gamma, any value) that ends
+// within the kLutBits bits of a window, as (N << 4) | its length, else 0. Such
+// codewords hold N <= 63. The general path reads it from constant memory.
+template <int CODE>
+constexpr int lut_field_any(LutCursor &c) {
+    if (CODE) {
+        int z = 0;
+        while (true) {
+            const int b = lut_take(c, 1);
+            if (b < 0) return -1;
+            if (b == 1) break;
+            ++z;
+        }
+        int N = 1;
+        for (int i = 0; i < z; ++i) {
+            const int b = lut_take(c, 1);
+            if (b < 0) return -1;
+            N = (N << 1) | b;
+        }
+        return N;
+    }
+    int N = 1;
+    while (true) {
+        const int b = lut_take(c, 1);
+        if (b < 0) return -1;
+        if (b == 0) return N;
+        const int v = lut_take(c, N);
+        if (v < 0) return -1;
+        N = (1 << N) | v;
+    }
+}
+
+struct alignas(16) FieldLut {
+    uint16_t e[1u << kLutBits];
+};
+
+template <int CODE>
+constexpr FieldLut make_field_lut() {
+    FieldLut t{};
+    for (uint32_t i = 0; i < (1u << kLutBits); ++i) {
+        LutCursor c{reverse_bits(i, kLutBits), 0};
+        const int N = lut_field_any<CODE>(c);
+        t.e[i] = N > 0 ? (uint16_t)(((uint32_t)N << 4) | (uint32_t)c.pos) : (uint16_t)0;
+    }
+    return t;
+}
+
+__constant__ FieldLut kFieldLut = make_field_lut<0>();
+__constant__ FieldLut kFieldLutGamma = make_field_lut<1>();
+
 // ---- bit access -----------------------------------------------------------
 // Bit positions fit 32 bits (a group spans fewer than 2^31 bits: buckets of at
 // most 2^24 coordinates). LDS mode: a position is an LDS bit address; the
@@ -244,6 +294,7 @@ struct RecordCtx {
     static constexpr int code = CODE;
     const uint32_t *lut;
     uint32_t gbits, kbits, s;
+    const uint16_t *ft;  // field table of the code (kFieldLut / kFieldLutGamma)
 };
 
 // General omega decoding from bit p: returns N and advances p, or 0 if a group
@@ -282,6 +333,25 @@ __device__ __forceinline__ uint32_t gamma_at(const Bits<LDS> &r, uint32_t &p, ui
 template <bool LDS, class X>
 __device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const X &x, uint32_t p,
                                                 uint32_t &gap, uint32_t &neg, uint32_t &k) {
+    // both fields of at most kLutBits bits: one read of the stream (33 bits or
+    // more from p) and two of the field table. The bounds below are those of the
+    // general decoding: every group of a codeword is at most as long as the
+    // binary form of its value.
+    {
+        constexpr uint32_t m = (1u << kLutBits) - 1u;
+        const uint64_t w = r.at(p);
+        const uint32_t f1 = x.ft[(uint32_t)w & m];
+        const uint32_t l1 = f1 & 15u;
+        const uint32_t f2 = x.ft[(uint32_t)(w >> (l1 + 1u)) & m];
+        const uint32_t v1 = f1 >> 4, v2 = f2 >> 4;
+        if (f1 != 0u && f2 != 0u && 32u - (uint32_t)__clz(v1) <= x.gbits &&
+            32u - (uint32_t)__clz(v2) <= x.kbits && v2 <= x.s) {
+            gap = v1;
+            neg = (uint32_t)(w >> l1) & 1u;
+            k = v2;
+            return p + l1 + 1u + (f2 & 15u);
+        }
+    }
     uint32_t q = p;
     gap = X::code ? gamma_at(r, q, x.gbits) : omega_at(r, q, x.gbits);
     if (gap == 0) return 0;
@@ -641,7 +711,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
         }
     }
     if (LDS_OUT && tactive && q == 0) ebs[team] = e_b;
-    const RecordCtx<CODE> x{lut, tactive ? bitlen32((uint32_t)len) : 1u, bitlen32(D.s), D.s};
+    const RecordCtx<CODE> x{lut, tactive ? bitlen32((uint32_t)len) : 1u, bitlen32(D.s), D.s,
+                            CODE ? kFieldLutGamma.e : kFieldLut.e};
     const uint32_t P0 = A + 32u;
     const uint32_t seg = nl ? ((E - P0) + nl - 1u) / nl : 0u;
     const bool act = q < nl;
