@@ -83,7 +83,9 @@ struct DecodeParams {
 //   bits 12-19  level byte sign << 7 | k of the first record
 //   bits 20-23  gap - 1 of the second record
 //   bits 24-31  level byte of the second record
-// Computed at compile time.
+// With total length 0, the first field alone (any value) if it ends within the
+// 12 bits: bits 4-7 its length, bits 8-15 its value (else 0); the general path
+// decodes from it. Computed at compile time.
 struct alignas(16) RecordLut {
     uint32_t e[1 << kLutBits];
 };
@@ -158,32 +160,8 @@ constexpr uint32_t reverse_bits(uint32_t v, int n) {
     return r;
 }
 
-template <int CODE>
-constexpr RecordLut make_record_lut() {
-    RecordLut t{};
-    for (uint32_t i = 0; i < (1u << kLutBits); ++i) {
-        LutCursor c{reverse_bits(i, kLutBits), 0};  // the cursor reads the first bit from the top
-        uint32_t e = 0;
-        const int r1 = lut_record<CODE>(c);
-        if (r1 >= 0) {
-            const uint32_t l1 = (uint32_t)c.pos;
-            e = l1 | (l1 << 4) | ((uint32_t)r1 << 8);
-            LutCursor c2 = c;
-            const int r2 = lut_record<CODE>(c2);
-            if (r2 >= 0) e = (e & ~15u) | (uint32_t)c2.pos | ((uint32_t)r2 << 20);
-        }
-        t.e[i] = e;
-    }
-    return t;
-}
-
-// record tables of the omega (code 0) and gamma (code 1) streams
-__constant__ RecordLut kRecordLut = make_record_lut<0>();
-__constant__ RecordLut kRecordLutGamma = make_record_lut<1>();
-
-// Field table: the codeword of one field (omega or gamma, any value) that ends
-// within the kLutBits bits of a window, as (N << 4) | its length, else 0. Such
-// codewords hold N <= 63. The general path reads it from constant memory.
+// One field (omega or gamma, any value) at the cursor, or -1 if it does not
+// end within the window; a codeword of at most kLutBits bits holds N <= 63.
 template <int CODE>
 constexpr int lut_field_any(LutCursor &c) {
     if (CODE) {
@@ -213,23 +191,36 @@ constexpr int lut_field_any(LutCursor &c) {
     }
 }
 
-struct alignas(16) FieldLut {
-    uint16_t e[1u << kLutBits];
-};
-
+// Entry of window i: one or two records (total length in bits 0-3, see above);
+// where no record ends within the window, total length 0 and, if the first
+// field does, N << 8 | its length << 4 (0 if not).
 template <int CODE>
-constexpr FieldLut make_field_lut() {
-    FieldLut t{};
+constexpr RecordLut make_record_lut() {
+    RecordLut t{};
     for (uint32_t i = 0; i < (1u << kLutBits); ++i) {
-        LutCursor c{reverse_bits(i, kLutBits), 0};
-        const int N = lut_field_any<CODE>(c);
-        t.e[i] = N > 0 ? (uint16_t)(((uint32_t)N << 4) | (uint32_t)c.pos) : (uint16_t)0;
+        LutCursor c{reverse_bits(i, kLutBits), 0};  // the cursor reads the first bit from the top
+        uint32_t e = 0;
+        const int r1 = lut_record<CODE>(c);
+        if (r1 >= 0) {
+            const uint32_t l1 = (uint32_t)c.pos;
+            e = l1 | (l1 << 4) | ((uint32_t)r1 << 8);
+            LutCursor c2 = c;
+            const int r2 = lut_record<CODE>(c2);
+            if (r2 >= 0) e = (e & ~15u) | (uint32_t)c2.pos | ((uint32_t)r2 << 20);
+        } else {
+            LutCursor cf{reverse_bits(i, kLutBits), 0};
+            const int N = lut_field_any<CODE>(cf);
+            if (N > 0) e = ((uint32_t)N << 8) | ((uint32_t)cf.pos << 4);
+        }
+        t.e[i] = e;
     }
     return t;
 }
 
-__constant__ FieldLut kFieldLut = make_field_lut<0>();
-__constant__ FieldLut kFieldLutGamma = make_field_lut<1>();
+// record tables of the omega (code 0) and gamma (code 1) streams
+__constant__ RecordLut kRecordLut = make_record_lut<0>();
+__constant__ RecordLut kRecordLutGamma = make_record_lut<1>();
+
 
 // ---- bit access -----------------------------------------------------------
 // Bit positions fit 32 bits (a group spans fewer than 2^31 bits: buckets of at
@@ -294,7 +285,6 @@ struct RecordCtx {
     static constexpr int code = CODE;
     const uint32_t *lut;
     uint32_t gbits, kbits, s;
-    const uint16_t *ft;  // field table of the code (kFieldLut / kFieldLutGamma)
 };
 
 // General omega decoding from bit p: returns N and advances p, or 0 if a group
@@ -330,26 +320,44 @@ __device__ __forceinline__ uint32_t gamma_at(const Bits<LDS> &r, uint32_t &p, ui
 // One record c(gap) | sign | c(k) at bit p by general decoding of the code c.
 // Returns the position after it, or 0 if it does not parse (a record never
 // ends at 0): a group longer than the bound, or k > s.
+// The first field of the window a table entry was made from: its value N and
+// length, or false if it does not end within the window. A record entry's first
+// field is its gap (N <= 16); an entry without a record keeps the field itself.
+template <int CODE>
+__device__ __forceinline__ bool entry_field(uint32_t e, uint32_t &N, uint32_t &len) {
+    if (e & 15u) {
+        N = ((e >> 8) & 15u) + 1u;
+        const uint32_t b = 32u - (uint32_t)__clz(N);
+        len = CODE ? 2u * b - 1u : (N == 1u ? 1u : (N < 4u ? 3u : (N < 8u ? 6u : (N < 16u ? 7u : 11u))));
+        return true;
+    }
+    N = e >> 8;
+    len = (e >> 4) & 15u;
+    return len != 0u;
+}
+
+// e0: the table entry at p (one without a record).
 template <bool LDS, class X>
 __device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const X &x, uint32_t p,
-                                                uint32_t &gap, uint32_t &neg, uint32_t &k) {
-    // both fields of at most kLutBits bits: one read of the stream (33 bits or
-    // more from p) and two of the field table. The bounds below are those of the
+                                                uint32_t &gap, uint32_t &neg, uint32_t &k,
+                                                uint32_t e0) {
+    // both fields of at most kLutBits bits: the first from e0, the table entry at
+    // p, the second from the entry at its start (one read of the stream, 33 bits
+    // or more from p, and one of the table). The bounds below are those of the
     // general decoding: every group of a codeword is at most as long as the
     // binary form of its value.
     {
-        constexpr uint32_t m = (1u << kLutBits) - 1u;
-        const uint64_t w = r.at(p);
-        const uint32_t f1 = x.ft[(uint32_t)w & m];
-        const uint32_t l1 = f1 & 15u;
-        const uint32_t f2 = x.ft[(uint32_t)(w >> (l1 + 1u)) & m];
-        const uint32_t v1 = f1 >> 4, v2 = f2 >> 4;
-        if (f1 != 0u && f2 != 0u && 32u - (uint32_t)__clz(v1) <= x.gbits &&
-            32u - (uint32_t)__clz(v2) <= x.kbits && v2 <= x.s) {
-            gap = v1;
-            neg = (uint32_t)(w >> l1) & 1u;
-            k = v2;
-            return p + l1 + 1u + (f2 & 15u);
+        uint32_t v1, l1, v2, l2;
+        if (entry_field<X::code>(e0, v1, l1)) {
+            const uint64_t w = r.at(p);
+            const uint32_t e2 = x.lut[(uint32_t)(w >> (l1 + 1u)) & ((1u << kLutBits) - 1u)];
+            if (entry_field<X::code>(e2, v2, l2) && 32u - (uint32_t)__clz(v1) <= x.gbits &&
+                32u - (uint32_t)__clz(v2) <= x.kbits && v2 <= x.s) {
+                gap = v1;
+                neg = (uint32_t)(w >> l1) & 1u;
+                k = v2;
+                return p + l1 + 1u + l2;
+            }
         }
     }
     uint32_t q = p;
@@ -377,13 +385,14 @@ __device__ __forceinline__ uint32_t lut_step(const Bits<LDS> &r, const X &x, uin
     return e;
 }
 
-// The general path of a chain step at p: past the record at p adding its gap to
-// sum, or one bit on if no record parses there; W follows p.
+// The general path of a chain step at p (e: the table entry there): past the
+// record at p adding its gap to sum, or one bit on if no record parses there;
+// W follows p.
 template <bool LDS, class X>
 __device__ __forceinline__ void slow_step(const Bits<LDS> &r, const X &x, uint32_t &p, uint32_t &sum,
-                                          Win &W) {
+                                          Win &W, uint32_t e) {
     uint32_t gap, neg, k;
-    const uint32_t q = record_slow(r, x, p, gap, neg, k);
+    const uint32_t q = record_slow(r, x, p, gap, neg, k, e);
     sum += q ? gap : 0u;
     p = q ? q : p + 1u;
     W = win_at(r, p);
@@ -399,7 +408,7 @@ __device__ __forceinline__ void chain_step(const Bits<LDS> &r, const X &x, uint3
         p += (e >> 4) & 15u;
         sum += ((e >> 8) & 15u) + 1u;
     } else {
-        slow_step(r, x, p, sum, W);
+        slow_step(r, x, p, sum, W, e);
     }
 }
 
@@ -416,7 +425,7 @@ __device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const X &x, ui
         neg = (e >> 19) & 1u;
         return p + ((e >> 4) & 15u);
     }
-    const uint32_t q = record_slow(r, x, p, gap, neg, k);
+    const uint32_t q = record_slow(r, x, p, gap, neg, k, e);
     if (q) W = win_at(r, q);
     return q;
 }
@@ -495,7 +504,7 @@ __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const X &x,
                 p += two ? (e & 15u) : len1;
                 i += two ? 2u : 1u;
             } else {
-                slow_step(r, x, p, sum, W);
+                slow_step(r, x, p, sum, W, e);
                 i += 1u;
             }
             i = i < kCumSlots - 2u ? i : kCumSlots - 2u;
@@ -521,7 +530,7 @@ __device__ __forceinline__ uint32_t follow_chain(const Bits<LDS> &r, const X &x,
             sum += ((e >> 8) & 15u) + 1u + (two ? ((e >> 20) & 15u) + 1u : 0u);
             p += two ? (e & 15u) : len1;
         } else {
-            slow_step(r, x, p, sum, W);
+            slow_step(r, x, p, sum, W, e);
         }
     }
     ga = sum;
@@ -579,7 +588,7 @@ __device__ __forceinline__ bool extend_chain(const Bits<LDS> &r, const X &x, uin
             }
         } else {
             uint32_t gap, neg, k;
-            const uint32_t q = record_slow(r, x, p, gap, neg, k);
+            const uint32_t q = record_slow(r, x, p, gap, neg, k, e);
             if (!q) break;
             p = q;
             sum += gap;
@@ -711,8 +720,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
         }
     }
     if (LDS_OUT && tactive && q == 0) ebs[team] = e_b;
-    const RecordCtx<CODE> x{lut, tactive ? bitlen32((uint32_t)len) : 1u, bitlen32(D.s), D.s,
-                            CODE ? kFieldLutGamma.e : kFieldLut.e};
+    const RecordCtx<CODE> x{lut, tactive ? bitlen32((uint32_t)len) : 1u, bitlen32(D.s), D.s};
     const uint32_t P0 = A + 32u;
     const uint32_t seg = nl ? ((E - P0) + nl - 1u) / nl : 0u;
     const bool act = q < nl;
@@ -831,7 +839,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
                     p += two ? (e & 15u) : len1;
                 } else {
                     uint32_t gap, neg, k;
-                    const uint32_t nq = record_slow(r, x, p, gap, neg, k);
+                    const uint32_t nq = record_slow(r, x, p, gap, neg, k, e);
                     if (!nq) break;
                     tix += gap;
                     lvl[tix < tend ? tix : kLevelSpare] = (uint8_t)((neg << 7) | k);
