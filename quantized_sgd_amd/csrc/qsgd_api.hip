@@ -204,10 +204,10 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     // pass 1: every tile into its slot
     if (use_aligned(bstart, s, d)) {
         const size_t lds = aligned_encode_lds_bytes(p.obuf_words);
-        // long thread halves are common when levels are large: mean level about
-        // 0.8 s / sqrt(d) under the L2 norm, 0.8 s / max|z| (about s / 4) under
-        // the max-norm; past about 2 a half's 8 records pass 64 bits
-        const bool levels = norm == QSGD_NORM_MAX ? s >= 8 : (uint64_t)s * s >= 6ull * d;
+        // records packed per quarter of a thread when levels are large: mean level
+        // about 0.8 s / sqrt(d) under the L2 norm, 0.8 s / max|z| (about s / 4)
+        // under the max-norm; past about 2 a half's 8 records pass 64 bits
+        const bool quarters = norm == QSGD_NORM_MAX ? s >= 8 : (uint64_t)s * s >= 6ull * d;
         // twice the resident workgroups: the second half starts as workgroups of
         // the first finish, which evens out the end of the pass (per encode, c3:
         // 115.7 -> 109.2 us, c2: 54.9 -> 54.0, c4: 455 -> 442; on c3 1.5 times is
@@ -216,7 +216,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
             const uint32_t blocks = runs_for(2 * resident_blocks(kernel, lds));
             hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), lds, stream, P, log2u(d));
         };
-        if (levels) launch(encode_aligned_kernel<true>);
+        if (quarters) launch(encode_aligned_kernel<true>);
         else launch(encode_aligned_kernel<false>);
     } else {
         // twice the resident workgroups too (c5: 221 -> 211 us per encode)

@@ -516,10 +516,12 @@ __device__ __forceinline__ void store_tile_slot(const QsgdParams &P, uint64_t *o
     if (bstart) P.offsets[((uint64_t)tile << (12 - log2d)) + (threadIdx.x >> (log2d - 4))] = off;
 }
 
-// LEVELS: keep each thread's 16 levels as packed bytes for halves whose records
-// pass 64 bits (worth its registers when such halves are common: large levels);
-// otherwise such a half draws its levels again from v and Philox.
-template <bool LEVELS>
+// QUARTERS: records packed per quarter of the thread (4 coordinates) in four
+// 64-bit registers, for large levels, whose records would often pass 64 bits in
+// a half; otherwise per half (8 coordinates) in two. A part whose records pass
+// 64 bits draws its levels again from v and Philox and writes its records one
+// at a time.
+template <bool QUARTERS>
 __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint32_t log2d) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int sh_mx[kWaves];
@@ -575,9 +577,10 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
 
         // ---- levels and record codes; records packed right-aligned into two
         // 64-bit registers (coordinates 0-7 and 8-15) ----
-        uint32_t lvb[kCPT / 4] = {0, 0, 0, 0};
-        uint64_t racc[2] = {0, 0};
-        uint32_t rlen[2] = {0, 0};
+        constexpr int NA = QUARTERS ? 4 : 2;          // packing registers
+        constexpr int QS = QUARTERS ? 2 : 3;          // coordinate q goes to register q >> QS
+        uint64_t racc[NA] = {};
+        uint32_t rlen[NA] = {};
         int prev = x0 - 1;
         bool have = bstart;
         int pendx = -1;
@@ -599,17 +602,18 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
                 const uint32_t neg = __float_as_uint(x[q]) >> 31;
                 const uint32_t gg = have ? (uint32_t)(xi - prev) : 0u;
                 const uint32_t ent = rt[code_index(gg, k, neg)];
-                if (LEVELS) lvb[g] |= ((neg << 7) | k) << (8 * e);
                 const uint32_t len = ent & 31u;
-                racc[q >> 3] = (racc[q >> 3] << len) | (uint64_t)(ent >> 5);
-                rlen[q >> 3] += len;
+                racc[q >> QS] = (racc[q >> QS] << len) | (uint64_t)(ent >> 5);
+                rlen[q >> QS] += len;
                 const bool nz = k != 0u;
                 pendx = (nz && !have) ? xi : pendx;
                 prev = nz ? xi : prev;
                 have = have || nz;
             }
         }
-        const uint32_t r = (bstart ? 32u : 0u) + rlen[0] + rlen[1];
+        uint32_t r = bstart ? 32u : 0u;
+#pragma unroll
+        for (int h = 0; h < NA; ++h) r += rlen[h];
         const int marker = have ? prev : INT_MIN;
 
         // ---- exclusive max-scan of markers: origin of the pending first gap ----
@@ -660,36 +664,29 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
             or_bits(obuf, p, pc << (64u - Lp), Lp);
             p += Lp;
         }
-        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int h = 0; h < NA; ++h) {
             if (rlen[h] <= 64u) {
                 if (rlen[h]) or_bits(obuf, p, racc[h] << (64u - rlen[h]), rlen[h]);
                 p += rlen[h];
             } else {
-                // more than 64 bits in this half: its records one at a time,
+                // more than 64 bits in this part: its records one at a time,
                 // the gaps followed from the thread's first coordinate, the
-                // levels from the packed bytes or drawn again from v
+                // levels drawn again from v
+                constexpr int QW = kCPT / NA;
                 int pv = x0 - 1;
                 bool hv = bstart;
 #pragma unroll 1
-                for (int q = 0; q < 8 * h + 8; ++q) {
-                    uint32_t k, neg;
-                    if (LEVELS) {
-                        const uint32_t wv = lvb[0] * (q < 4) + lvb[1] * (q >= 4 && q < 8) +
-                                            lvb[2] * (q >= 8 && q < 12) + lvb[3] * (q >= 12);
-                        const uint32_t b8 = (wv >> (8 * (q & 3))) & 255u;
-                        k = b8 & 127u;
-                        neg = b8 >> 7;
-                    } else {
-                        const uint64_t gi = g0 + (uint64_t)q;
-                        uint32_t w[4];
-                        uint32_t k0 = key0, k1 = key1;
-                        asm volatile("" : "+s"(k0), "+s"(k1));
-                        philox4x32_10((uint32_t)(gi >> 2), (uint32_t)(gi >> 34), k0, k1, w);
-                        const float xv = gi < P.n ? P.v[gi] : 0.0f;
-                        k = qlevel(xv, cb, w[q & 3]);
-                        neg = __float_as_uint(xv) >> 31;
-                    }
-                    if (q >= 8 * h) {
+                for (int q = 0; q < QW * h + QW; ++q) {
+                    const uint64_t gi = g0 + (uint64_t)q;
+                    uint32_t w[4];
+                    uint32_t k0 = key0, k1 = key1;
+                    asm volatile("" : "+s"(k0), "+s"(k1));
+                    philox4x32_10((uint32_t)(gi >> 2), (uint32_t)(gi >> 34), k0, k1, w);
+                    const float xv = gi < P.n ? P.v[gi] : 0.0f;
+                    const uint32_t k = qlevel(xv, cb, w[q & 3]);
+                    const uint32_t neg = __float_as_uint(xv) >> 31;
+                    if (q >= QW * h) {
                         const uint32_t gg = hv ? (uint32_t)(x0 + q - pv) : 0u;
                         const uint32_t ent = rt[code_index(gg, k, neg)];
                         const uint32_t len = ent & 31u;
