@@ -761,22 +761,33 @@ __global__ __launch_bounds__(kWG) void encode_finish_kernel(FinishParams F) {
     // stream offset of t0: the totals of the pass-1 runs before t0's run, then
     // the lengths of the tiles of that run before t0
     const uint32_t r0 = run_of(t0, F.run, F.rem);
+    const uint32_t m = t1 - t0;  // this share's tiles (chunk <= kFinishTiles <= kWG)
+    const uint64_t mine = (uint32_t)j < m ? (uint64_t)F.tile_bits[t0 + j] : 0ull;
     uint64_t acc = 0;
     for (uint32_t i = (uint32_t)j; i < r0; i += kWG) acc += F.run_bits[i];
     for (uint32_t t = run_first(r0, F.run, F.rem) + (uint32_t)j; t < t0; t += kWG) acc += F.tile_bits[t];
     acc = wave_incl_add_u64(acc);
     if (lane == 63) sh_red[wave] = acc;
-    __syncthreads();
-    uint64_t pre = 0;
+    if (m <= 64u) {
+        // the share's tiles are wave 0's lanes: their offsets need no second
+        // block-wide step
+        const uint64_t incl = wave_incl_add_u64(mine);
+        __syncthreads();
+        uint64_t pre = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) pre += sh_red[w];
-    // offsets of this share's tiles (chunk <= kFinishTiles <= kWG)
-    const uint32_t m = t1 - t0;
-    const uint64_t mine = (uint32_t)j < m ? (uint64_t)F.tile_bits[t0 + j] : 0ull;
-    uint64_t total = 0;
-    const uint64_t ex = block_excl_add_u64(mine, sh_scan, total);
-    if ((uint32_t)j < m) sh_base[j] = pre + ex;
-    if (j == 0) sh_base[m] = pre + total;  // end of the share
+        for (int w = 0; w < kWaves; ++w) pre += sh_red[w];
+        if ((uint32_t)j < m) sh_base[j] = pre + incl - mine;
+        if ((uint32_t)j + 1u == m) sh_base[m] = pre + incl;  // end of the share
+    } else {
+        __syncthreads();
+        uint64_t pre = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) pre += sh_red[w];
+        uint64_t total = 0;
+        const uint64_t ex = block_excl_add_u64(mine, sh_scan, total);
+        if ((uint32_t)j < m) sh_base[j] = pre + ex;
+        if (j == 0) sh_base[m] = pre + total;  // end of the share
+    }
     __syncthreads();
 
     // every stream word whose first bit lies in this share's tiles, four per
