@@ -182,12 +182,16 @@ void or_bucket_max_norms(const float *v, const uint64_t *bstart, uint64_t nb, fl
 }
 
 /* Q_s on one coordinate, in the page's order: l = floor(s|v|/||v||),
- * p = s|v|/||v|| - l, round up to l + 1 with probability p. The ratio
- * s|v|/||v|| is evaluated as RN32(|v| * RN64(s / ||v||)); the uniform is
- * u = u24 * 2^-24 and the coordinate rounds up iff u < p. Returns k. */
-static uint32_t level_of(float v, double c_b, uint32_t u24) {
+ * p = s|v|/||v|| - l, round up to l + 1 with probability p. The ratio is the
+ * binary32 value nearest to the exact quotient s|v|/||v|| (ties to even): s|v| is
+ * exact in fp64 (at most 24 + 24 significant bits), the fp64 quotient is
+ * correctly rounded, and rounding that to fp32 gives the correctly rounded
+ * fp32 quotient, because an fp32 rounding boundary is either hit exactly (then
+ * the fp64 quotient is exact too) or lies more than 2^-49 relative away. The
+ * uniform is u = u24 * 2^-24 and the coordinate rounds up iff u < p. Returns k. */
+static uint32_t level_of(float v, float norm, uint32_t s, uint32_t u24) {
     float a = fabsf(v);
-    float r = (float)((double)a * c_b);
+    float r = (float)(((double)s * (double)a) / (double)norm);
     float l = floorf(r);
     float p = r - l; /* exact: l <= r < l + 1 */
     float u = (float)u24 * 0x1p-24f;
@@ -211,10 +215,9 @@ static int quantize_impl(const float *v, const uint64_t *bstart, uint64_t nb, ui
             for (uint64_t i = lo; i < hi; ++i) levels[i] = 0;
             continue;
         }
-        double c_b = (double)s / (double)norm;
         for (uint64_t i = lo; i < hi; ++i) {
             uint32_t w24 = u24 ? u24[i] : (or_random_word(seed, i) >> 8);
-            uint32_t k = level_of(v[i], c_b, w24);
+            uint32_t k = level_of(v[i], norm, s, w24);
             if (k > s) return OR_ERR_ARG; /* only with a norm below max |v_i| */
             levels[i] = signbit(v[i]) ? -(int32_t)k : (int32_t)k;
         }
@@ -234,10 +237,12 @@ int or_quantize_u24(const float *v, const uint64_t *bstart, uint64_t nb, uint32_
     return quantize_impl(v, bstart, nb, s, 0, u24, given_norms, levels, norms_out);
 }
 
-/* Q_s(v)_i = ||v|| * sgn(v_i) * k_i / s, evaluated as RN32(k * RN64(||v|| / s)). */
+/* Q_s(v)_i = ||v|| * sgn(v_i) * k_i / s: the magnitude is the binary32 value
+ * nearest to the exact ||v|| k / s (ties to even). norm * k is exact in fp64 (at
+ * most 24 + 24 significant bits); the fp64 quotient and its rounding to fp32
+ * give the correctly rounded result, as for the ratio in level_of. */
 static float dequant_magnitude(float norm, uint32_t s, uint32_t k) {
-    double e_b = (double)norm / (double)s;
-    return (float)((double)k * e_b);
+    return (float)(((double)norm * (double)k) / (double)s);
 }
 
 void or_dequantize(const int32_t *levels, const float *norms, const uint64_t *bstart,

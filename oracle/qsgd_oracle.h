@@ -21,7 +21,8 @@
  * The pages give real-valued mathematics only. Every step they leave open is
  * fixed as follows (each a reading, see the comments at the definitions):
  *  - norm:     RN32(sqrt(sum (double)v_i^2)), summed in index order in fp64.
- *  - ratio:    r_i = RN32(|v_i| * c_b) with c_b = RN64(s / norm_b), in fp64.
+ *  - ratio:    r_i = RN32(s |v_i| / norm_b), the fp32 value nearest to the exact
+ *              quotient (ties to even).
  *  - rounding: l = floor(r), p = r - l, u = (w >> 8) * 2^-24 with w the
  *              Philox4x32-10 word (i & 3) of counter (i >> 2, key = seed),
  *              k = l + [u < p].
@@ -30,8 +31,8 @@
  *              bucket-local 1-based distance to the previous non-zero; buckets
  *              are concatenated with no padding; stream bit t is bit 63 - (t mod 64)
  *              of 64-bit word t / 64; bucket b starts at offsets[b].
- *  - dequantization: m = RN32(k * e_b) with e_b = RN64(norm_b / s); value +-m,
- *              +0.0f where k = 0.
+ *  - dequantization: m = RN32(norm_b k / s), the fp32 value nearest to the
+ *              exact quotient (ties to even); value +-m, +0.0f where k = 0.
  */
 #ifndef QSGD_ORACLE_H
 #define QSGD_ORACLE_H

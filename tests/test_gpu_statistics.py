@@ -49,9 +49,10 @@ def test_rounding_mean_and_bits_over_seeds():
         lev = lev.cpu().numpy()
         if norms is None:
             norms = nrm.cpu().numpy()
-            # the reading of the scaling: r = RN32(|v| RN64(s / norm)), l = floor(r), p = r - l
-            c = np.float64(s) / norms.astype(np.float64)
-            r = (np.abs(v).astype(np.float64) * np.repeat(c, d)[:n]).astype(np.float32)
+            # the reading of the scaling: r = RN32(s |v| / norm), l = floor(r), p = r - l
+            # (s |v| is exact in fp64 and the fp64 quotient rounds to the right fp32)
+            nrm_of = np.repeat(norms.astype(np.float64), d)[:n]
+            r = ((np.float64(s) * np.abs(v).astype(np.float64)) / nrm_of).astype(np.float32)
             l = np.floor(r).astype(np.int64)
             p = (r - np.float32(l)).astype(np.float64)
             pup = np.ceil(p * 2.0**24) / 2.0**24

@@ -7,9 +7,9 @@ fp32 addition per stream, streams in order.
 
 The pins use buckets of one coordinate with s = 1, where the method is exact:
 the norm of a one-coordinate bucket is |v_i| (the fp64 square of an fp32 value
-is exact and so is its square root), r = RN32(|v_i| * RN64(1 / |v_i|)) = 1, so
+is exact and so is its square root), r = RN32(1 * |v_i| / |v_i|) = 1, so
 l = 1, p = 0 and k = 1 whatever the random draw, and decoding returns
-RN32(1 * RN64(|v_i| / 1)) = |v_i| with the sign: v_hat = v exactly, except
+RN32(|v_i| * 1 / 1) = |v_i| with the sign: v_hat = v exactly, except
 that zeros come back as +0.0. The accumulate must then be numpy's float32
 left fold of the inputs.
 """
