@@ -153,6 +153,7 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
     P.K = p.K; P.ntiles = (uint32_t)p.ntiles; P.levels = levels; P.norms = norms;
     P.obuf_words = 0;
     P.maxnorm = norm;
+    P.sigma = odd_part(s);
     if (use_aligned(bstart, s, d)) {
         hipLaunchKernelGGL(quantize_aligned_kernel, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P,
                            log2u(d));
@@ -193,6 +194,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     P.obuf_words = p.obuf_words;
     P.code = code;
     P.maxnorm = norm;
+    P.sigma = odd_part(s);
     // pass 1 grid: at most the given number of workgroups (and kMaxRuns), each
     // taking a run of consecutive tiles
     auto runs_for = [&](uint32_t resident) {
@@ -265,6 +267,8 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
     D.nstreams = nstreams;
     D.bstart = bstart; D.v_hat = v_hat;
     D.n = n; D.nb = nb; D.s = s; D.d = d;
+    D.s_pow2 = (s & (s - 1)) == 0 ? 1u : 0u;
+    D.inv_s = 1.0 / (double)s;
     // LDS-staged output: whole groups of buckets of at most kGroupCoords
     // coordinates, levels fit int8. Team size: a power of two, about one lane per
     // 64 coordinates of a bucket, teams * buckets per group <= 64.

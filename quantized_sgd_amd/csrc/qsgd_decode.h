@@ -2,7 +2,8 @@
 //
 // Page "QSGD (Quantized Stochastic Gradient Descent) with Elias Coding",
 // definition paragraph: the coding is lossless, so decode inverts it exactly;
-// Q_s(v)_i = ||v|| sgn(v_i) k_i / s, evaluated as RN32(k * RN64(norm / s)).
+// Q_s(v)_i = ||v|| sgn(v_i) k_i / s, the binary32 value nearest to the exact
+// quotient (dequant_value).
 //
 // Work split. A wave64 owns a group of consecutive buckets and a team of T lanes
 // (T = 1..64, chosen from the bucket size) decodes each bucket. The wave first
@@ -71,6 +72,8 @@ struct DecodeParams {
     uint32_t team;           // lanes per bucket (power of two, 1..64)
     uint32_t tpw;            // buckets per wave group (tpw * team <= 64)
     uint32_t lds_out;        // 1: levels staged in LDS (s <= 127, tpw * d <= kGroupCoords)
+    uint32_t s_pow2;         // s is a power of two (norm / s exact)
+    double inv_s;            // 1 / s (exact when s_pow2)
 };
 
 // ---- record table -------------------------------------------------------
@@ -678,7 +681,7 @@ __device__ __forceinline__ void wave_sync() {
 // offsets `offs`; `r` reads the group's stream, bit 0 being stream bit `gbit`.
 // LDS_OUT: each record's level byte (sign << 7 | k) goes to the group's LDS
 // buffer `lvl` (index = coordinate - lbase, cleared here) and each bucket's
-// RN64(norm / s) to ebs[team]; otherwise every lane writes (ACC: adds) its own
+// norm to ebs[team]; otherwise every lane writes (ACC: adds) its own
 // output range with a QuadWriter. CUM: the lanes' gap-prefix tables live in
 // `lvl` (without them, the gap sum before a sync point is found by walking the
 // speculative chain again).
@@ -707,7 +710,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
         len = bucket_first<RAGGED>(D, b + 1) - c0;
         if (E >= A + 32u && len > 0) {
             const float norm = __uint_as_float(__builtin_bitreverse32((uint32_t)r.at(A)));
-            e_b = (double)norm / (double)D.s;
+            e_b = (double)norm;
             const uint32_t Lp = E - (A + 32u);
             if (Lp > 0) {
                 const uint32_t m = Lp / (uint32_t)kSyncWin;
@@ -869,7 +872,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
                 if (!nq) break;
                 jj += gap;
                 if (jj >= hi) break;
-                const float m = (float)((double)k * e_b);
+                const float m = dequant_value(e_b, k, D.s, D.s_pow2 != 0u, D.inv_s);
                 w.put(c0 + jj, neg ? -m : m);
                 p = nq;
             }
@@ -878,8 +881,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
     }
 }
 
-// Writes the group's buckets from the LDS level bytes: RN32(k * RN64(norm / s))
-// with the byte's sign (+0.0f for k = 0), 16-byte stores for whole aligned
+// Writes the group's buckets from the LDS level bytes: RN32(norm k / s)
+// (dequant_value) with the byte's sign (+0.0f for k = 0), 16-byte stores for whole aligned
 // quads of a bucket, single floats for quads that a bucket boundary cuts (ACC:
 // added to the output). The value of each of the 256 level bytes is tabulated
 // per bucket in `tbl` first.
@@ -893,7 +896,7 @@ __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t
         const double e = ebs[b - b0];
 #pragma unroll
         for (uint32_t t = lane; t < 256u; t += 64u) {
-            const float m = (float)((double)(t & 127u) * e);
+            const float m = dequant_value(e, t & 127u, D.s, D.s_pow2 != 0u, D.inv_s);
             tbl[t] = __uint_as_float(__float_as_uint(m) | ((t & 128u) << 24));
         }
         wave_sync();

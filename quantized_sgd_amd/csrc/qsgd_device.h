@@ -48,17 +48,81 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
     o[0] = x0; o[1] = x1; o[2] = x2; o[3] = x3;
 }
 
-// Level k of one coordinate: r = RN32(|v| * c) with c = RN64(s / norm) of its
-// bucket, l = floor(r), p = r - l (exact), uniform u = (w >> 8) 2^-24, k = l + [u < p].
-// Each operation is one IEEE op (the library is built with -ffp-contract=off).
-__device__ __forceinline__ uint32_t qlevel(float v, double c, uint32_t w) {
-    const float a = fabsf(v);
-    const float r = (float)((double)a * c);
-    // r >= 0: truncation is the floor, and fract gives r - floor(r) exactly
-    const uint32_t l = (uint32_t)r;
-    const float p = __builtin_amdgcn_fractf(r);
+// The ratio r = RN32(s |v| / norm) of the page's l and p, the binary32 value
+// nearest to the exact quotient (ties to even). Fast form: r = RN32(|v| * c)
+// with c = RD64(s / norm), the fp64 quotient rounded toward zero, per bucket.
+// Exactness of the fast form. The fp64 value |v| c lies within 2^-51 (relative)
+// of the exact quotient q and never above it when q is an fp64 number. With
+// |v| = alpha 2^ea, norm = nu 2^en (alpha, nu < 2^24) and s <= 2^24, q differs
+// from any number M = mu 2^em with mu < 2^25 (an fp32 rounding boundary) by
+// more than 2^-49 relative unless q = M exactly, since s |v| - M norm is a
+// non-zero multiple of 2^min(ea, em + en) then. So RN32 agrees unless q is
+// exactly a boundary:
+//  - q = 2^-150 (half the least subnormal, which rounds to 0): |v| c <= q
+//    then, so the fast form gives 0 as well;
+//  - other boundaries of the subnormal range: both neighbours are positive and
+//    below 2^-126, where the decision u < p is the same for both;
+//  - a midpoint of the normal range (25-bit odd mu): the odd parts of s, |v| and
+//    norm then satisfy sigma alpha' = mu nu' with alpha' < 2^24 < mu, so the odd
+//    part of norm's significand is below the odd part sigma of s. A bucket where
+//    that can happen (never for s a power of two) takes the exact form: the
+//    fp64 quotient of the exact product s |v| and norm, rounded to fp32.
+__device__ __forceinline__ double ratio_scale(float norm, uint32_t s) {
+    if (norm == 0.0f) return 0.0;
+    const double q = (double)s / (double)norm;                 // RN64
+    const double rem = __builtin_fma(q, (double)norm, -(double)s);  // exact: q norm - s
+    return rem > 0.0 ? __longlong_as_double(__double_as_longlong(q) - 1) : q;
+}
+
+// True when the ratio of some coordinate of a bucket with this norm can be an
+// exact fp32 midpoint: the odd part of norm's integer significand is below
+// sigma, the odd part of s (norm > 0).
+__device__ __forceinline__ bool ratio_may_tie(float norm, uint32_t sigma) {
+    if (norm == 0.0f) return false;
+    const uint32_t b = __float_as_uint(norm);
+    uint32_t m = b & 0x7fffffu;
+    if (b >> 23) m |= 0x800000u;
+    return (m >> __builtin_ctz(m)) < sigma;
+}
+
+// The fast form of the signed ratio: sign of v, magnitude RN32(|v| c).
+__device__ __forceinline__ float ratio_fast(float v, double c) { return (float)((double)v * c); }
+
+// The exact form: the fp64 quotient of s v (exact) and norm, rounded to fp32.
+__device__ __forceinline__ float ratio_exact(float v, float norm, uint32_t s) {
+    return norm == 0.0f ? 0.0f * v : (float)(((double)s * (double)v) / (double)norm);
+}
+
+// Level k from the signed ratio r of a coordinate: l = floor(|r|),
+// p = |r| - l (exact), uniform u = (w >> 8) 2^-24, k = l + [u < p]. Each
+// operation is one IEEE op (the library is built with -ffp-contract=off).
+__device__ __forceinline__ uint32_t level_of_ratio(float r, uint32_t w) {
+    const float a = fabsf(r);
+    // a >= 0: truncation is the floor, and fract gives a - floor(a) exactly
+    const uint32_t l = (uint32_t)a;
+    const float p = __builtin_amdgcn_fractf(a);
     const float u = (float)(w >> 8) * 0x1p-24f;
     return l + (u < p ? 1u : 0u);
+}
+
+// Level of one coordinate of a bucket (c = ratio_scale, exact = ratio_may_tie).
+__device__ __forceinline__ uint32_t qlevel(float v, double c, bool exact, float norm, uint32_t s,
+                                           uint32_t w) {
+    return level_of_ratio(exact ? ratio_exact(v, norm, s) : ratio_fast(v, c), w);
+}
+
+// Odd part of s.
+__host__ __device__ __forceinline__ uint32_t odd_part(uint32_t s) {
+    while (s && !(s & 1u)) s >>= 1;
+    return s;
+}
+
+// Dequantized magnitude RN32(norm k / s), the binary32 value nearest to the exact
+// quotient: norm k is exact in fp64, so the fp64 quotient rounded to fp32 is it.
+// For s a power of two (pow2) the quotient norm / s is exact and a product serves.
+__device__ __forceinline__ float dequant_value(double norm, uint32_t k, uint32_t s, bool pow2,
+                                               double inv_s) {
+    return pow2 ? (float)((double)k * (norm * inv_s)) : (float)(((double)k * norm) / (double)s);
 }
 
 // Elias omega codeword of N >= 1 (Elias 1975), right-aligned: a final 0 bit, and

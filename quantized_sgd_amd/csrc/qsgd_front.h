@@ -39,6 +39,7 @@ struct QsgdParams {
     uint32_t run, rem;     // workgroup b takes run_first(b) .. run_first(b + 1) - 1
     uint32_t code;         // integer code of gaps and levels: 0 Elias omega, 1 Elias gamma
     uint32_t maxnorm;      // bucket scale: 0 the L2 norm, 1 the max-norm max|v_i| (QSGDinf)
+    uint32_t sigma;        // odd part of s (ratio_may_tie)
 };
 
 // Runs of consecutive tiles: the first `rem` workgroups take run + 1 tiles, the
@@ -56,7 +57,8 @@ __host__ __device__ __forceinline__ uint32_t run_of(uint32_t t, uint32_t run, ui
 // LDS carved out of the dynamic shared memory block for the front half.
 struct FrontLds {
     int32_t *bs;      // [K + 1] bucket starts relative to A
-    double *cb;       // [K] sum of squares, then RN64(s / norm)
+    double *cb;       // [K] sum of squares, then ratio_scale(norm, s), or -1 where
+                      // the bucket takes the exact ratio (ratio_may_tie)
     float *nrm;       // [K] norms
     double *segv;     // [kWaves] scan scratch
     int *segf;        // [kWaves]
@@ -153,8 +155,9 @@ __device__ __forceinline__ int first_bucket(const QsgdParams &P, const Tile &t, 
 // order per bucket segment; buckets that span threads are combined with a
 // segmented scan in thread order. The order is fixed, so results are
 // reproducible; it differs from a plain left-to-right sum only in rounding.
-// Afterwards L.nrm[k] = RN32(sqrt(sum)) and L.cb[k] = RN64(s / norm) (0 for a
-// zero bucket). MAXN: the max-norm max|v_i| instead (exact, in any order).
+// Afterwards L.nrm[k] = RN32(sqrt(sum)) and L.cb[k] = RD64(s / norm) (0 for a
+// zero bucket; -1 for a bucket whose ratios are computed exactly, see
+// ratio_may_tie). MAXN: the max-norm max|v_i| instead (exact, in any order).
 // Ends with a barrier.
 template <bool RAGGED, bool MAXN = false>
 __device__ __forceinline__ void bucket_norms(const QsgdParams &P, const Tile &t, FrontLds &L,
@@ -200,7 +203,7 @@ __device__ __forceinline__ void bucket_norms(const QsgdParams &P, const Tile &t,
     for (uint32_t b = threadIdx.x; b < t.K; b += kWG) {
         const float nr = MAXN ? (float)L.cb[b] : (float)sqrt(L.cb[b]);
         L.nrm[b] = nr;
-        L.cb[b] = nr == 0.0f ? 0.0 : (double)P.s / (double)nr;
+        L.cb[b] = ratio_may_tie(nr, P.sigma) ? -1.0 : ratio_scale(nr, P.s);
     }
     __syncthreads();
 }
@@ -241,7 +244,8 @@ __device__ __forceinline__ void quantize_coords(const QsgdParams &P, const Tile 
                     cb = L.cb[k];
                     o.bst |= 1u << q;
                 }
-                kk = qlevel(c.x[q], cb, w[e]);
+                kk = level_of_ratio(cb < 0.0 ? ratio_exact(c.x[q], L.nrm[k], P.s) : ratio_fast(c.x[q], cb),
+                                    w[e]);
                 if (__float_as_uint(c.x[q]) >> 31) o.neg |= 1u << q;
             }
             o.k[q] = kk;

@@ -14,39 +14,13 @@ midpoints ("ties"), which a quotient evaluated through an inexact fp64
 reciprocal or scale factor can round the wrong way.
 """
 import math
-import random
 from fractions import Fraction
 
 import numpy as np
 import pytest
 
 import oracle
-
-U24 = 1 << 24
-
-
-def rn32(q: Fraction) -> float:
-    """The binary32 value nearest to q (ties to even), by integer arithmetic."""
-    if q == 0:
-        return 0.0
-    neg = q < 0
-    q = abs(q)
-    e = q.numerator.bit_length() - q.denominator.bit_length()
-    if Fraction(2) ** e > q:
-        e -= 1
-    quantum = max(e, -126) - 23        # exponent of the spacing at q (subnormals: 2^-149)
-    scaled = q / Fraction(2) ** quantum
-    n = scaled.numerator // scaled.denominator
-    rem = scaled - n
-    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
-        n += 1
-    val = float(Fraction(n) * Fraction(2) ** quantum)
-    assert float(np.float32(val)) == val  # representable
-    return -val if neg else val
-
-
-def f32(x) -> float:
-    return float(np.float32(x))
+from tests.ties import U24, dequant_ties, f32, ratio_ties, rn32
 
 
 def test_rn32_agrees_with_numpy_on_doubles():
@@ -82,43 +56,6 @@ def probe_u24s(a: float, norm: float, s: int):
     p = r - math.floor(r)
     P = math.ceil(p * U24)
     return sorted({0, max(P - 1, 0), min(P, U24 - 1), U24 - 1})
-
-
-def ratio_ties(s: int, count: int, seed: int):
-    """(a, norm) with s a / norm exactly an fp32 midpoint (a 25-bit odd
-    significand). With s = sigma 2^es, a = alpha 2^ea and norm = nu 2^en (odd
-    sigma, alpha, nu), that needs sigma alpha = mu nu with mu odd in
-    (2^24, 2^25), hence nu < sigma: take alpha = nu beta, mu = sigma beta."""
-    sigma = s >> ((s & -s).bit_length() - 1)
-    rnd = random.Random(seed)
-    out = []
-    nus = [nu for nu in range(1, sigma, 2)]
-    assert nus, "a power-of-two s has no ratio ties in the normal range"
-    while len(out) < count:
-        nu = rnd.choice(nus)
-        lo = (1 << 24) // sigma + 1
-        hi = min((1 << 25) // sigma, ((1 << 24) - 1) // nu)
-        if lo > hi:
-            continue
-        beta = rnd.randrange(lo, hi + 1) | 1
-        if beta > hi or nu * beta >= 1 << 24:
-            continue
-        alpha = nu * beta
-        j = rnd.randrange(-3, max(1, s.bit_length() - 1))   # r in [2^j, 2^(j+1))
-        es = (s & -s).bit_length() - 1
-        ea = j - 24 - es
-        norm_exp = rnd.randrange(-3, 4)
-        a = math.ldexp(alpha, ea + norm_exp)
-        norm = math.ldexp(nu, norm_exp)
-        if not (0 < a <= norm) or f32(a) != a or f32(norm) != norm:
-            continue
-        q = Fraction(s) * Fraction(a) / Fraction(norm)
-        m = q / Fraction(2) ** (math.floor(math.log2(q)) - 24)
-        assert m.denominator == 1 and m.numerator % 2 == 1  # an exact midpoint
-        if q > s:
-            continue
-        out.append((a, norm))
-    return out
 
 
 @pytest.mark.parametrize("s", [3, 100, 1000])
@@ -182,36 +119,6 @@ def test_dequantize_known_tie():
     assert rn32(Fraction(71116920 * 85, 100)) == 60449384.0
     assert float(oracle_magnitudes(71116920.0, 100, [85])[0]) == 60449384.0
     assert float(oracle_magnitudes(71116920.0, 100, [-85])[0]) == -60449384.0
-
-
-def dequant_ties(s: int, count: int, seed: int):
-    """(norm, k) with norm k / s exactly an fp32 midpoint: nu kappa = mu sigma
-    (odd parts) with mu odd in (2^24, 2^25), hence kappa > sigma."""
-    es = (s & -s).bit_length() - 1
-    sigma = s >> es
-    rnd = random.Random(seed)
-    kappas = [kp for kp in range(sigma + 2, s + 1, 2)]
-    assert kappas, "no dequantization ties for this s"
-    out = []
-    while len(out) < count:
-        kappa = rnd.choice(kappas)
-        g = math.gcd(kappa, sigma)
-        # nu = sigma / g * t, mu = kappa / g * t with t odd
-        lo = ((1 << 24) * g) // kappa + 1
-        hi = min(((1 << 25) * g) // kappa, ((1 << 24) - 1) * g // sigma)
-        if lo > hi:
-            continue
-        t = rnd.randrange(lo, hi + 1) | 1
-        nu, mu = sigma // g * t, kappa // g * t
-        if not ((1 << 24) < mu < (1 << 25)) or nu >= 1 << 24 or t % 2 == 0:
-            continue
-        kmax = s // kappa
-        k = kappa << rnd.randrange(0, kmax.bit_length())
-        if k > s:
-            continue
-        norm = math.ldexp(nu, rnd.randrange(-20, 20))
-        out.append((norm, k))
-    return out
 
 
 @pytest.mark.parametrize("s", [100, 1000, 12])
