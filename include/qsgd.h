@@ -15,7 +15,8 @@
  * this library implements, bit for bit):
  *   norm_b   = RN32(sqrt(sum_{i in b} (double)v_i^2)) with an fp64 sum in a fixed
  *              (deterministic) order.
- *   r_i      = RN32(|v_i| * RN64(s / norm_b));  l = floor(r);  p = r - l.
+ *   r_i      = RN32(s |v_i| / norm_b), the binary32 value nearest to the exact
+ *              quotient (ties to even);  l = floor(r);  p = r - l.
  *   uniform  = (w >> 8) * 2^-24 where w is word (i & 3) of Philox4x32-10
  *              (Salmon et al., SC'11) with key (lo32(seed), hi32(seed)) and
  *              counter (lo32(i >> 2), hi32(i >> 2), 0, 0); i is the flat index
@@ -26,8 +27,8 @@
  *              bucket start (bucket-local indices). Buckets are concatenated with
  *              no padding. Stream bit t is bit 63 - (t mod 64) of 64-bit word
  *              t / 64; unused bits of the last word are 0.
- *   decode   = v_hat_i = +-RN32(k * RN64(norm_b / s)) for coded coordinates
- *              (minus for sign bit 1), +0.0f elsewhere.
+ *   decode   = v_hat_i = +-RN32(norm_b k / s), the binary32 value nearest to the
+ *              exact quotient (minus for sign bit 1), +0.0f elsewhere.
  *   An all-zero bucket has norm 0 and no records.
  *
  * Conventions for every entry point:
@@ -77,7 +78,7 @@ typedef enum { QSGD_CODE_OMEGA = 0, QSGD_CODE_GAMMA = 1 } qsgd_code;
  * Communication-efficient Data-parallel SGD via Nonuniform Quantization",
  * abstract) without defining it; this library reads the name as the infinity
  * norm. The norm field of the stream then holds max|v_i| (exact), r_i =
- * RN32(|v_i| * RN64(s / max|v|)) and everything else is unchanged, so decode
+ * RN32(s |v_i| / max|v|) and everything else is unchanged, so decode
  * needs no norm argument. The coordinates of largest magnitude get k = s. */
 typedef enum { QSGD_NORM_L2 = 0, QSGD_NORM_MAX = 1 } qsgd_norm;
 
