@@ -63,7 +63,8 @@ typedef enum {
     QSGD_OK = 0,
     QSGD_ERR_INVALID_ARG = 1,
     QSGD_ERR_LAUNCH = 2,
-    QSGD_ERR_UNSUPPORTED = 3
+    QSGD_ERR_UNSUPPORTED = 3,
+    QSGD_ERR_SCRATCH = 4      /* qsgd_encode_noalloc: the workspace exceeds the fixed scratch */
 } qsgd_status;
 
 /* Integer code of the record fields (gaps and levels). The page names "Elias
@@ -233,6 +234,36 @@ qsgd_status qsgd_decode_accumulate_ragged(const uint64_t *const *in,
                                           const uint64_t *const *bucket_bit_offsets, uint32_t k,
                                           uint64_t n, const uint64_t *bucket_start, uint64_t nb,
                                           uint32_t s, uint32_t d, float *acc, hipStream_t stream);
+
+/* ---- encode without allocation ----------------------------------------------
+ * For callers that cannot allocate device memory during the call (code under
+ * HIP graph capture, tight loops, harnesses that forbid allocation): the same
+ * computation as qsgd_encode, with the encoder's workspace (one bit-string slot
+ * per tile of at most 4096 coordinates, the tiles' lengths and the pass-1 run
+ * totals) in a fixed scratch array of 64 MiB inside the library instead of the
+ * tail of `out`. Every device the library runs on holds its own copy of that
+ * array until the process ends; its address is looked up on the first call on
+ * a device. The call allocates nothing (no hipMalloc, no library allocation).
+ * Nothing in the scratch needs clearing between calls: each call writes every
+ * workspace word it reads. Calls that overlap in time on one device share the
+ * scratch and race: serialize them (for instance on one stream).
+ *
+ * qsgd_encode_noalloc_capacity_words: the words `out` must hold, the stream
+ * bound of qsgd_encode_capacity_words without the workspace; 0 when the
+ * workspace of (n, s, d) exceeds the scratch or the arguments are invalid.
+ * About 8 KB of scratch per tile at s = 64 (under 2 KB at s = 1): up to about
+ * 34 M coordinates at s = 64, d = 4096, 39 M at s = 16, d = 512, and 149 M at
+ * s = 1, d = 512.
+ *
+ * qsgd_encode_noalloc: arguments as qsgd_encode, with `out` holding
+ * qsgd_encode_noalloc_capacity_words(n, s, d) words. Returns QSGD_ERR_SCRATCH,
+ * enqueueing nothing, when the workspace exceeds the scratch; its results are
+ * bit-identical to qsgd_encode's.
+ */
+uint64_t qsgd_encode_noalloc_capacity_words(uint64_t n, uint32_t s, uint32_t d);
+qsgd_status qsgd_encode_noalloc(const float *v, uint64_t n, uint32_t s, uint32_t d, uint64_t seed,
+                                uint64_t *out, uint64_t *out_bits, uint64_t *bucket_bit_offsets,
+                                hipStream_t stream);
 
 #ifdef __cplusplus
 }

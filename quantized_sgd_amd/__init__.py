@@ -19,7 +19,7 @@ __all__ = [
     "QsgdError", "lib", "num_buckets", "encode_capacity_words", "quantize", "encode",
     "decode", "RaggedLayout", "quantize_ragged", "encode_ragged", "decode_ragged",
     "max_bucket", "max_streams", "decode_accumulate", "decode_accumulate_ragged", "OMEGA", "GAMMA",
-    "L2", "MAXNORM",
+    "L2", "MAXNORM", "encode_noalloc", "encode_noalloc_capacity_words",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,7 +30,7 @@ _u64 = ctypes.c_uint64
 _u32 = ctypes.c_uint32
 _vp = ctypes.c_void_p
 
-QSGD_OK, QSGD_ERR_INVALID_ARG, QSGD_ERR_LAUNCH, QSGD_ERR_UNSUPPORTED = 0, 1, 2, 3
+QSGD_OK, QSGD_ERR_INVALID_ARG, QSGD_ERR_LAUNCH, QSGD_ERR_UNSUPPORTED, QSGD_ERR_SCRATCH = 0, 1, 2, 3, 4
 OMEGA, GAMMA = 0, 1  # integer code of the record fields (qsgd_code)
 L2, MAXNORM = 0, 1   # bucket scale (qsgd_norm): ||v||_2, or max|v_i| (QSGDinf)
 
@@ -80,7 +80,10 @@ def lib():
         L.qsgd_max_streams.restype = _u32
         L.qsgd_decode_accumulate.argtypes = [_vp, _vp, _u32, _u64, _u32, _u32, _vp, _vp]
         L.qsgd_decode_accumulate_ragged.argtypes = [_vp, _vp, _u32, _u64, _vp, _u64, _u32, _u32, _vp, _vp]
-        for name in ("qsgd_quantize", "qsgd_encode", "qsgd_decode", "qsgd_ragged_bucket_table",
+        L.qsgd_encode_noalloc_capacity_words.argtypes = [_u64, _u32, _u32]
+        L.qsgd_encode_noalloc_capacity_words.restype = _u64
+        L.qsgd_encode_noalloc.argtypes = [_vp, _u64, _u32, _u32, _u64, _vp, _vp, _vp, _vp]
+        for name in ("qsgd_encode_noalloc", "qsgd_quantize", "qsgd_encode", "qsgd_decode", "qsgd_ragged_bucket_table",
                      "qsgd_quantize_ragged", "qsgd_encode_ragged", "qsgd_decode_ragged",
                      "qsgd_decode_accumulate", "qsgd_decode_accumulate_ragged", "qsgd_encode_ex",
                      "qsgd_decode_ex", "qsgd_quantize_ex"):
@@ -317,3 +320,29 @@ def decode_accumulate_ragged(words_list, offsets_list, layout: RaggedLayout, s: 
                                                _stream(stream)),
            "qsgd_decode_accumulate_ragged")
     return acc
+
+
+def encode_noalloc_capacity_words(n: int, s: int, d: int) -> int:
+    """Words `out` must hold for encode_noalloc (0: the workspace of (n, s, d)
+    exceeds the library's fixed scratch)."""
+    return int(lib().qsgd_encode_noalloc_capacity_words(n, s, d))
+
+
+def encode_noalloc(v: torch.Tensor, s: int, d: int, seed: int, out: torch.Tensor, out_bits: torch.Tensor,
+                   offsets: torch.Tensor, stream=None):
+    """qsgd_encode_noalloc: encode with the workspace in the library's fixed
+    scratch; every buffer is the caller's (out: encode_noalloc_capacity_words
+    words, out_bits: 1, offsets: num_buckets + 1)."""
+    n = v.numel()
+    cap = encode_noalloc_capacity_words(n, s, d)
+    if cap and out.numel() < cap:
+        raise ValueError(f"out holds {out.numel()} words, needs {cap}")
+    if out_bits.numel() < 1:
+        raise ValueError("out_bits needs 1 word")
+    if offsets.numel() < num_buckets(n, d) + 1:
+        raise ValueError(f"offsets holds {offsets.numel()} words, needs {num_buckets(n, d) + 1}")
+    _check(lib().qsgd_encode_noalloc(_dev(v, torch.float32, "v"), n, s, d, seed,
+                                     _dev(out, torch.int64, "out"), _dev(out_bits, torch.int64, "out_bits"),
+                                     _dev(offsets, torch.int64, "offsets"), _stream(stream)),
+           "qsgd_encode_noalloc")
+    return out, out_bits, offsets

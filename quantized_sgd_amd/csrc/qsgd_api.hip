@@ -167,10 +167,12 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
     return launch_status();
 }
 
+// ws: the encoder's workspace (EncodePlan::ws_words words), or nullptr for the
+// tail of `out` after the stream bound.
 qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb, uint32_t s,
                         uint32_t d, uint64_t seed, uint64_t *out, uint64_t *out_bits,
                         uint64_t *offsets, hipStream_t stream, uint32_t code = QSGD_CODE_OMEGA,
-                        uint32_t norm = QSGD_NORM_L2) {
+                        uint32_t norm = QSGD_NORM_L2, uint64_t *ws = nullptr) {
     qsgd_status st = check_common(v, s, d);
     if (st != QSGD_OK) return st;
     if (code > QSGD_CODE_GAMMA || norm > QSGD_NORM_MAX) return QSGD_ERR_INVALID_ARG;
@@ -188,7 +190,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     P.v = v; P.n = n; P.nb = nb; P.bstart = bstart; P.seed = seed; P.s = s; P.d = d;
     P.K = p.K; P.ntiles = (uint32_t)p.ntiles;
     P.offsets = offsets;
-    P.slots = out + p.stream_words;
+    P.slots = ws ? ws : out + p.stream_words;
     P.tile_bits = reinterpret_cast<uint32_t *>(P.slots + p.slot_region_words);
     P.run_bits = P.slots + p.slot_region_words + (p.ntiles + 1) / 2;
     P.obuf_words = p.obuf_words;
@@ -323,6 +325,38 @@ uint64_t ragged_count(const uint64_t *seg_len, uint32_t nseg, uint32_t d, uint64
     return nb;
 }
 
+// ---- fixed scratch of the no-allocation encode ----------------------------
+// Each device that runs the library holds its own copy of this array for the
+// life of the process. In host code `scratch` is only a stand-in for the symbol:
+// the device address of a device's copy comes from hipGetSymbolAddress, looked
+// up once per device (with that device current) on the first call there.
+constexpr uint64_t kScratchBytes = 64ull << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
+
+uint64_t *scratch_on_current_device() {
+    static std::mutex mu;
+    static uint64_t *addr[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> g(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev] = static_cast<uint64_t *>(p);
+    }
+    return addr[dev];
+}
+
+// The plan of a no-allocation encode: valid (K > 0) only when its workspace
+// fits the scratch.
+EncodePlan noalloc_plan(uint64_t n, uint32_t s, uint32_t d) {
+    const uint64_t nb = d ? (n + d - 1) / d : 0;
+    EncodePlan p = make_plan(n, nb, s, d, d % 16 == 0);
+    if (p.K && p.ws_words * 8 > kScratchBytes) p.K = 0;
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -333,6 +367,7 @@ const char *qsgd_status_string(qsgd_status status) {
         case QSGD_ERR_INVALID_ARG: return "QSGD_ERR_INVALID_ARG";
         case QSGD_ERR_LAUNCH: return "QSGD_ERR_LAUNCH";
         case QSGD_ERR_UNSUPPORTED: return "QSGD_ERR_UNSUPPORTED";
+        case QSGD_ERR_SCRATCH: return "QSGD_ERR_SCRATCH";
     }
     return "QSGD_UNKNOWN_STATUS";
 }
@@ -455,6 +490,27 @@ qsgd_status qsgd_decode_ragged(const uint64_t *in, const uint64_t *bucket_bit_of
                                float *v_hat, hipStream_t stream) {
     if (!bucket_start && nb) return QSGD_ERR_INVALID_ARG;
     return decode_impl(&in, &bucket_bit_offsets, 1, false, n, bucket_start, nb, s, d, v_hat, stream);
+}
+
+uint64_t qsgd_encode_noalloc_capacity_words(uint64_t n, uint32_t s, uint32_t d) {
+    if (d == 0 || s == 0 || s > (1u << 24)) return 0;
+    if (n == 0) return 1;
+    const EncodePlan p = noalloc_plan(n, s, d);
+    return p.K ? p.stream_words : 0;
+}
+
+qsgd_status qsgd_encode_noalloc(const float *v, uint64_t n, uint32_t s, uint32_t d, uint64_t seed,
+                                uint64_t *out, uint64_t *out_bits, uint64_t *bucket_bit_offsets,
+                                hipStream_t stream) {
+    qsgd_status st = check_common(v, s, d);
+    if (st != QSGD_OK) return st;
+    if (n == 0) return encode_impl(v, n, nullptr, 0, s, d, seed, out, out_bits, bucket_bit_offsets, stream);
+    const EncodePlan p = noalloc_plan(n, s, d);
+    if (p.K == 0) return QSGD_ERR_SCRATCH;
+    uint64_t *ws = scratch_on_current_device();
+    if (!ws) return QSGD_ERR_LAUNCH;
+    return encode_impl(v, n, nullptr, qsgd_num_buckets(n, d), s, d, seed, out, out_bits, bucket_bit_offsets,
+                       stream, QSGD_CODE_OMEGA, QSGD_NORM_L2, ws);
 }
 
 qsgd_status qsgd_decode_accumulate_ragged(const uint64_t *const *in,
