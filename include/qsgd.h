@@ -89,8 +89,10 @@ const char *qsgd_status_string(qsgd_status status);
 /* ceil(n / d): the number of buckets of a single vector (0 if d == 0). */
 uint64_t qsgd_num_buckets(uint64_t n, uint32_t d);
 
-/* Largest bucket length that qsgd_quantize / qsgd_encode accept (4096 in this
- * build); larger d returns QSGD_ERR_UNSUPPORTED. Decode accepts d <= 2^24. */
+/* Largest bucket length of a ragged batch (4081 in this build: a tile of 4096
+ * coordinates holds whole buckets starting anywhere); longer ragged buckets
+ * return QSGD_ERR_UNSUPPORTED. Uniform buckets may have any length up to the
+ * whole vector (d >= n is the single bucket of n coordinates). */
 uint32_t qsgd_max_bucket(void);
 
 /* Number of uint64 words the `out` buffer of qsgd_encode must hold for (n, s, d):

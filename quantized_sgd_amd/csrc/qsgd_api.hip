@@ -12,6 +12,7 @@
 
 #include "qsgd_decode.h"
 #include "qsgd_encode.h"
+#include "qsgd_span.h"
 
 using namespace qsgd;
 
@@ -58,14 +59,35 @@ struct EncodePlan {
     uint64_t slot_region_words = 0;
     bool table = false;         // record codes from the LDS table (s <= kTabS)
     size_t lds_bytes = 0;
+    bool span = false;          // buckets longer than a tile (qsgd_span.h): aligned 4096-windows
+    uint64_t span_off = 0;      // workspace words before the span path's arrays
 };
 
+// Words of the span path's arrays in the workspace (after slots, tile lengths
+// and run totals): partial sums, norms, and the per-run pending state.
+uint64_t span_words(uint64_t ntiles, uint64_t nb) {
+    return 3 * ntiles + (nb + 1) / 2 + kSpanMaxRuns + kSpanMaxRuns / 2 + kSpanMaxRuns +
+           kSpanMaxRuns / 2 + kSpanMaxRuns;
+}
+
+// The span path's arrays carved out of the workspace at ws + span_off.
+SpanParams carve_span(uint64_t *ws, uint64_t span_off, uint64_t ntiles, uint64_t nb) {
+    SpanParams sp{};
+    uint64_t *q = ws + span_off;
+    sp.partial = reinterpret_cast<double *>(q); q += 3 * ntiles;
+    sp.norms = reinterpret_cast<float *>(q); q += (nb + 1) / 2;
+    sp.run_pend = q; q += kSpanMaxRuns;
+    sp.run_pend_tile = reinterpret_cast<uint32_t *>(q); q += kSpanMaxRuns / 2;
+    sp.run_mark = q; q += kSpanMaxRuns;
+    sp.lp = reinterpret_cast<uint32_t *>(q); q += kSpanMaxRuns / 2;
+    sp.pc = q;
+    return sp;
+}
+
 EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool aligned_starts,
-                     uint32_t code = QSGD_CODE_OMEGA) {
+                     uint32_t code = QSGD_CODE_OMEGA, bool ragged = false) {
     EncodePlan p;
     p.K = buckets_per_tile(d, aligned_starts);
-    if (p.K == 0) return p;
-    p.ntiles = (nb + p.K - 1) / p.K;
     const uint64_t Ls = host_code_len(code, s);
     // stream bound: 32 nb + n (2.5 + Ls) bits (both codes spend at most 1.5 g
     // bits on a gap g, so a bucket's gap codes take at most 1.5 times its
@@ -73,6 +95,24 @@ EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool align
     const uint64_t twice_bits = 64 * nb + n * (5 + 2 * Ls);
     p.stream_words = (twice_bits + 127) / 128 + 1;
     p.stream_words = (p.stream_words + 31) & ~(uint64_t)31;
+    p.table = s <= kTabS;
+    if (p.K == 0) {
+        // buckets longer than a tile: uniform buckets only, over aligned windows
+        // of 4096 coordinates (at most three buckets meet one); a window's first
+        // gap may reach back over earlier windows, 64 bits more at most
+        if (ragged || d <= 2048) return p;
+        p.span = true;
+        p.K = 1;
+        p.ntiles = (n + kTC - 1) / kTC;
+        const uint64_t tile_twice_bits = 64ull * kSpanK + (uint64_t)kTC * (5 + 2 * Ls) + 128;
+        p.obuf_words = (uint32_t)((tile_twice_bits + 127) / 128 + 1);
+        p.slot_region_words = (p.ntiles * p.obuf_words + 1) & ~(uint64_t)1;
+        p.span_off = p.slot_region_words + (p.ntiles + 1) / 2 + kMaxRuns;
+        p.ws_words = p.span_off + span_words(p.ntiles, nb);
+        p.lds_bytes = align16((size_t)(p.obuf_words + 1) * 8);
+        return p;
+    }
+    p.ntiles = (nb + p.K - 1) / p.K;
     // a tile's bit string: the same bound for its K buckets and at most 4096
     // coordinates, plus one spare word (a two-word read at the string's end)
     const uint64_t tile_twice_bits = 64ull * p.K + (uint64_t)kTC * (5 + 2 * Ls);
@@ -81,7 +121,6 @@ EncodePlan make_plan(uint64_t n, uint64_t nb, uint32_t s, uint32_t d, bool align
     // aligned when out is)
     p.slot_region_words = (p.ntiles * p.obuf_words + 1) & ~(uint64_t)1;
     p.ws_words = p.slot_region_words + (p.ntiles + 1) / 2 + kMaxRuns;
-    p.table = s <= kTabS;
     p.lds_bytes = EncodeLayout(p.obuf_words, p.K).total;
     return p;
 }
@@ -137,6 +176,10 @@ bool use_aligned(const uint64_t *bstart, uint32_t s, uint32_t d) {
 
 uint32_t log2u(uint32_t d) { return 31u - (uint32_t)__builtin_clz(d); }
 
+// Uniform buckets longer than the vector are the single bucket of n
+// coordinates: planned (and launched) as d = n.
+uint32_t eff_d(uint64_t n, uint32_t d) { return (n > 0 && d > n) ? (uint32_t)n : d; }
+
 qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb,
                           uint32_t s, uint32_t d, uint64_t seed, int32_t *levels, float *norms,
                           hipStream_t stream, uint32_t norm = QSGD_NORM_L2) {
@@ -146,14 +189,32 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
     if (n == 0) return QSGD_OK;
     if (!v || !levels || !norms || !aligned16(levels)) return QSGD_ERR_INVALID_ARG;
     const bool ragged = bstart != nullptr;
-    EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0));
+    if (!ragged) d = eff_d(n, d);
+    EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0), QSGD_CODE_OMEGA, ragged);
     if (p.K == 0) return QSGD_ERR_UNSUPPORTED;
+    if (p.ntiles >= (1ull << 32) || nb >= (1ull << 31)) return QSGD_ERR_UNSUPPORTED;
     QsgdParams P{};
     P.v = v; P.n = n; P.nb = nb; P.bstart = bstart; P.seed = seed; P.s = s; P.d = d;
     P.K = p.K; P.ntiles = (uint32_t)p.ntiles; P.levels = levels; P.norms = norms;
     P.obuf_words = 0;
     P.maxnorm = norm;
     P.sigma = odd_part(s);
+    if (p.span) {
+        // the windows' partial sums live in the levels buffer (24 bytes per
+        // window of 16 KB) until the last kernel overwrites it with the levels
+        P.sp.partial = reinterpret_cast<double *>(levels);
+        P.sp.norms = norms;
+        P.norms = nullptr;
+        if (norm == QSGD_NORM_MAX) {
+            hipLaunchKernelGGL(span_norm_partial_kernel<true>, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P);
+            hipLaunchKernelGGL(span_norm_fold_kernel<true>, dim3((uint32_t)nb), dim3(kWG), 0, stream, P);
+        } else {
+            hipLaunchKernelGGL(span_norm_partial_kernel<false>, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P);
+            hipLaunchKernelGGL(span_norm_fold_kernel<false>, dim3((uint32_t)nb), dim3(kWG), 0, stream, P);
+        }
+        hipLaunchKernelGGL(span_quantize_kernel, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P);
+        return launch_status();
+    }
     if (use_aligned(bstart, s, d)) {
         hipLaunchKernelGGL(quantize_aligned_kernel, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P,
                            log2u(d));
@@ -183,9 +244,10 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     }
     if (!v || !out || !aligned16(out)) return QSGD_ERR_INVALID_ARG;
     const bool ragged = bstart != nullptr;
-    EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0), code);
+    if (!ragged) d = eff_d(n, d);
+    EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0), code, ragged);
     if (p.K == 0) return QSGD_ERR_UNSUPPORTED;
-    if (p.lds_bytes > kMaxLds || p.ntiles >= (1ull << 32)) return QSGD_ERR_UNSUPPORTED;
+    if (p.lds_bytes > kMaxLds || p.ntiles >= (1ull << 32) || nb >= (1ull << 31)) return QSGD_ERR_UNSUPPORTED;
     QsgdParams P{};
     P.v = v; P.n = n; P.nb = nb; P.bstart = bstart; P.seed = seed; P.s = s; P.d = d;
     P.K = p.K; P.ntiles = (uint32_t)p.ntiles;
@@ -205,6 +267,41 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
         P.rem = (uint32_t)(p.ntiles - (uint64_t)P.run * g);
         return (uint32_t)g;
     };
+    if (p.span) {
+        // buckets longer than a tile: norms first, then pass 1 over the windows,
+        // the runs' pending gap codes, and pass 2 (qsgd_span.h)
+        P.sp = carve_span(P.slots, p.span_off, p.ntiles, nb);
+        if (norm == QSGD_NORM_MAX) {
+            hipLaunchKernelGGL(span_norm_partial_kernel<true>, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P);
+            hipLaunchKernelGGL(span_norm_fold_kernel<true>, dim3((uint32_t)nb), dim3(kWG), 0, stream, P);
+        } else {
+            hipLaunchKernelGGL(span_norm_partial_kernel<false>, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P);
+            hipLaunchKernelGGL(span_norm_fold_kernel<false>, dim3((uint32_t)nb), dim3(kWG), 0, stream, P);
+        }
+        auto launch = [&](auto kernel) {
+            const uint64_t g = std::min<uint64_t>(std::min<uint64_t>(p.ntiles,
+                                                                     2 * resident_blocks(kernel, p.lds_bytes)),
+                                                  kSpanMaxRuns);
+            P.run = (uint32_t)(p.ntiles / g);
+            P.rem = (uint32_t)(p.ntiles - (uint64_t)P.run * g);
+            hipLaunchKernelGGL(kernel, dim3((uint32_t)g), dim3(kWG), p.lds_bytes, stream, P);
+            return (uint32_t)g;
+        };
+        const uint32_t runs = p.table ? launch(span_encode_kernel<true>) : launch(span_encode_kernel<false>);
+        hipLaunchKernelGGL(span_pending_kernel, dim3(1), dim3(kWG), 0, stream, P, runs);
+        SpanFinishParams S{};
+        S.F.out = out; S.F.slots = P.slots; S.F.tile_bits = P.tile_bits; S.F.offsets = offsets;
+        S.F.run_bits = P.run_bits; S.F.run = P.run; S.F.rem = P.rem;
+        S.F.out_bits = out_bits; S.F.nb = nb; S.F.ntiles = (uint32_t)p.ntiles; S.F.slot_words = p.obuf_words;
+        S.F.K = 0;
+        S.F.chunk = kFinishChunk;
+        S.sp = P.sp;
+        S.n = n;
+        S.d = d;
+        const uint32_t fgrid = (uint32_t)((p.ntiles + S.F.chunk - 1) / S.F.chunk);
+        hipLaunchKernelGGL(span_finish_kernel, dim3(fgrid), dim3(kWG), 0, stream, S);
+        return launch_status();
+    }
     // pass 1: every tile into its slot
     if (use_aligned(bstart, s, d)) {
         const size_t lds = aligned_encode_lds_bytes(p.obuf_words);
@@ -260,6 +357,7 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
     for (uint32_t k = 0; k < nstreams; ++k)
         if (!in[k] || !offsets[k]) return QSGD_ERR_INVALID_ARG;
     if (!v_hat || !aligned16(v_hat)) return QSGD_ERR_INVALID_ARG;
+    if (!bstart) d = eff_d(n, d);
     if (d > (1u << 24)) return QSGD_ERR_UNSUPPORTED;
     DecodeParams D{};
     for (uint32_t k = 0; k < nstreams; ++k) {
@@ -352,6 +450,7 @@ uint64_t *scratch_on_current_device() {
 // fits the scratch.
 EncodePlan noalloc_plan(uint64_t n, uint32_t s, uint32_t d) {
     const uint64_t nb = d ? (n + d - 1) / d : 0;
+    d = eff_d(n, d);
     EncodePlan p = make_plan(n, nb, s, d, d % 16 == 0);
     if (p.K && p.ws_words * 8 > kScratchBytes) p.K = 0;
     return p;
@@ -374,12 +473,13 @@ const char *qsgd_status_string(qsgd_status status) {
 
 uint64_t qsgd_num_buckets(uint64_t n, uint32_t d) { return d ? (n + d - 1) / d : 0; }
 
-uint32_t qsgd_max_bucket(void) { return (uint32_t)kTC; }
+uint32_t qsgd_max_bucket(void) { return (uint32_t)(kTC - 15); }
 
 uint64_t qsgd_encode_capacity_words(uint64_t n, uint32_t s, uint32_t d) {
     if (d == 0 || s == 0) return 0;
     const uint64_t nb = qsgd_num_buckets(n, d);
     if (nb == 0) return 1;
+    d = eff_d(n, d);
     EncodePlan p = make_plan(n, nb, s, d, d % 16 == 0);
     if (p.K == 0) return 0;
     return p.stream_words + p.ws_words;
@@ -388,7 +488,7 @@ uint64_t qsgd_encode_capacity_words(uint64_t n, uint32_t s, uint32_t d) {
 uint64_t qsgd_encode_capacity_words_ragged(uint64_t n, uint64_t nb, uint32_t s, uint32_t d) {
     if (d == 0 || s == 0) return 0;
     if (nb == 0) return 1;
-    EncodePlan p = make_plan(n, nb, s, d, false);
+    EncodePlan p = make_plan(n, nb, s, d, false, QSGD_CODE_OMEGA, true);
     if (p.K == 0) return 0;
     return p.stream_words + p.ws_words;
 }
@@ -418,6 +518,7 @@ uint64_t qsgd_encode_capacity_words_ex(uint64_t n, uint64_t nb, uint32_t s, uint
     if (nb == 0) return 1;
     // the larger of the two tilings (bucket starts on multiples of 16 or not;
     // buckets of more than 4081 coordinates only tile with aligned starts)
+    if (nb == 1) d = eff_d(n, d);
     EncodePlan a = make_plan(n, nb, s, d, true, code), b = make_plan(n, nb, s, d, false, code);
     const uint64_t ca = a.K ? a.stream_words + a.ws_words : 0, cb = b.K ? b.stream_words + b.ws_words : 0;
     return std::max(ca, cb);

@@ -15,6 +15,17 @@
 
 namespace qsgd {
 
+// Workspace of the path for buckets longer than a tile (qsgd_span.h).
+struct SpanParams {
+    double *partial;          // [ntiles][3] per-window partial sums (or maxima) of bucket pieces
+    float *norms;             // [nb] bucket norms
+    uint64_t *run_pend;       // [runs] index of the run's pending record, or ~0
+    uint32_t *run_pend_tile;  // [runs] its window
+    uint64_t *run_mark;       // [runs] index + 2 of the run's last marker, or 0
+    uint32_t *lp;             // [runs] length of the pending record's gap code (0: none)
+    uint64_t *pc;             // [runs] that code, right-aligned
+};
+
 struct QsgdParams {
     const float *v;
     uint64_t n;
@@ -40,6 +51,7 @@ struct QsgdParams {
     uint32_t code;         // integer code of gaps and levels: 0 Elias omega, 1 Elias gamma
     uint32_t maxnorm;      // bucket scale: 0 the L2 norm, 1 the max-norm max|v_i| (QSGDinf)
     uint32_t sigma;        // odd part of s (ratio_may_tie)
+    SpanParams sp;         // buckets longer than a tile only
 };
 
 // Runs of consecutive tiles: the first `rem` workgroups take run + 1 tiles, the

@@ -83,15 +83,22 @@ def test_code_choice_argument_checks():
 
 def test_capacity_bounds_oracle_streams():
     # the capacity helper bounds the worst case; check it against oracle streams
-    for n, d, s in [(4096, 4096, 64), (5000, 1, 1 << 24), (10000, 7, 3), (20000, 512, 16)]:
+    for n, d, s in [(4096, 4096, 64), (5000, 1, 1 << 24), (10000, 7, 3), (20000, 512, 16),
+                    # buckets longer than a tile (the span path), and d around its threshold
+                    (100, 5000, 4), (20000, 5000, 3), (9000, 9000, 64), (13000, 4081, 8),
+                    (13000, 4082, 8), (13000, 4095, 8), (13000, 4096, 8), (40000, 40000, 1)]:
         bst = oracle.uniform_buckets(n, d)
         for code in (oracle.OMEGA, oracle.GAMMA):
             cap = q.encode_capacity_words(n, s, d, code)
             for v in (np.full(n, 1.0, np.float32), np.random.default_rng(n).standard_normal(n).astype(np.float32)):
                 _, _, _, _, nbits = oracle.compress(v, bst, s, 1, code=code)
                 assert cap * 64 > nbits
-    assert q.encode_capacity_words(100, 4, 5000) == 0  # d beyond the tile: unsupported
-    assert q.max_bucket() == 4096
+    # uniform buckets of any length are served; ragged batches up to 4081
+    assert q.encode_capacity_words(100, 4, 5000) > 0
+    assert q.max_bucket() == 4081
+    lib = q.lib()
+    assert lib.qsgd_encode_capacity_words_ragged(100000, 20, 4, 5000) == 0
+    assert lib.qsgd_encode_capacity_words_ragged(100000, 30, 4, 4081) > 0
 
 
 def test_status_strings():
