@@ -34,7 +34,10 @@
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers, allocated and owned by the caller,
  *     except the arguments documented as HOST arrays. The library allocates no
- *     device memory and keeps no device state between calls.
+ *     device memory during a call and keeps no device state between calls; its
+ *     one fixed scratch array (64 MiB per device, held from the library's first
+ *     use on a device until the process ends) serves qsgd_encode_noalloc and the
+ *     decode of uniform buckets longer than 16384 coordinates only.
  *   - Calls only enqueue work on `stream` (0 = the null stream) and return
  *     without synchronizing; results are valid once the stream reaches them.
  *   - Argument errors are detected on the host before anything is enqueued and
@@ -64,7 +67,7 @@ typedef enum {
     QSGD_ERR_INVALID_ARG = 1,
     QSGD_ERR_LAUNCH = 2,
     QSGD_ERR_UNSUPPORTED = 3,
-    QSGD_ERR_SCRATCH = 4      /* qsgd_encode_noalloc: the workspace exceeds the fixed scratch */
+    QSGD_ERR_SCRATCH = 4      /* the call's records exceed the library's fixed scratch */
 } qsgd_status;
 
 /* Integer code of the record fields (gaps and levels). The page names "Elias
@@ -137,8 +140,15 @@ qsgd_status qsgd_encode(const float *v, uint64_t n, uint32_t s, uint32_t d, uint
  *   bucket_bit_offsets  [ceil(n/d) + 1] the offsets written by qsgd_encode.
  *   v_hat               [n] fp32 output, 16-byte aligned; every element is written
  *                       exactly once.
- * n, s, d must be those of the encode call; d <= 2^24 (larger d returns
- * QSGD_ERR_UNSUPPORTED).
+ * n, s, d must be those of the encode call. Uniform buckets of any length are
+ * decoded; those longer than 16384 coordinates are cut into chunks of 16384
+ * stream bits, one wave each, and need the library's fixed scratch (see
+ * qsgd_encode_noalloc): such calls must not overlap in time on one device with
+ * each other or with qsgd_encode_noalloc, and return QSGD_ERR_SCRATCH when
+ * their chunk records exceed it (about 2 M chunks). A bucket's stream must be
+ * shorter than 2^31 bits (checked against the bound of qsgd_encode_capacity_words;
+ * QSGD_ERR_UNSUPPORTED otherwise). Buckets of a ragged table are decoded up to
+ * 2^24 coordinates.
  */
 qsgd_status qsgd_decode(const uint64_t *in, const uint64_t *bucket_bit_offsets, uint64_t n,
                         uint32_t s, uint32_t d, float *v_hat, hipStream_t stream);
@@ -248,7 +258,8 @@ qsgd_status qsgd_decode_accumulate_ragged(const uint64_t *const *in,
  * a device. The call allocates nothing (no hipMalloc, no library allocation).
  * Nothing in the scratch needs clearing between calls: each call writes every
  * workspace word it reads. Calls that overlap in time on one device share the
- * scratch and race: serialize them (for instance on one stream).
+ * scratch and race: serialize them (for instance on one stream). Decodes of
+ * uniform buckets longer than 16384 coordinates use the same array.
  *
  * qsgd_encode_noalloc_capacity_words: the words `out` must hold, the stream
  * bound of qsgd_encode_capacity_words without the workspace; 0 when the

@@ -20,6 +20,7 @@ namespace {
 
 constexpr uint32_t kMaxRuns = 4096;    // pass-1 workgroups at most (run totals in the workspace)
 constexpr uint32_t kFinishChunk = 8;   // tiles per pass-2 workgroup
+constexpr uint32_t kChunkD = 16384;    // uniform buckets longer than this decode in chunks
 
 uint32_t host_omega_len(uint64_t N) {  // Elias omega codeword length
     uint32_t L = 1;
@@ -179,6 +180,32 @@ uint32_t log2u(uint32_t d) { return 31u - (uint32_t)__builtin_clz(d); }
 // Uniform buckets longer than the vector are the single bucket of n
 // coordinates: planned (and launched) as d = n.
 uint32_t eff_d(uint64_t n, uint32_t d) { return (n > 0 && d > n) ? (uint32_t)n : d; }
+
+// ---- the library's fixed scratch ------------------------------------------
+// Used by qsgd_encode_noalloc (the encoder's workspace) and by decodes of
+// buckets longer than kChunkD coordinates (their chunk records).
+// Each device that runs the library holds its own copy of this array for the
+// life of the process. In host code `scratch` is only a stand-in for the symbol:
+// the device address of a device's copy comes from hipGetSymbolAddress, looked
+// up once per device (with that device current) on the first call there.
+constexpr uint64_t kScratchBytes = 64ull << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
+
+uint64_t *scratch_on_current_device() {
+    static std::mutex mu;
+    static uint64_t *addr[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> g(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev] = static_cast<uint64_t *>(p);
+    }
+    return addr[dev];
+}
+
 
 qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb,
                           uint32_t s, uint32_t d, uint64_t seed, int32_t *levels, float *norms,
@@ -344,6 +371,61 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     return launch_status();
 }
 
+// Uniform buckets longer than kChunkD coordinates: the chunked decode
+// (qsgd_decode.h, "buckets longer than a chunk"), stream by stream, with the
+// chunk records in the fixed scratch.
+qsgd_status decode_chunked(const uint64_t *const *in, const uint64_t *const *offsets, uint32_t nstreams,
+                           bool acc, uint64_t n, uint64_t nb, uint32_t s, uint32_t d, float *v_hat,
+                           hipStream_t stream, uint32_t code) {
+    // chunk slots per bucket from the bound 32 + d (2.5 + |c(s)|) on its stream
+    const uint64_t Ls = host_code_len(code, s);
+    const uint64_t maxbits = ((uint64_t)d * (5 + 2 * Ls) + 1) / 2;
+    if (maxbits + 32 >= (1ull << 31)) return QSGD_ERR_UNSUPPORTED;
+    const uint64_t nch = (maxbits + kChunkBits - 1) / kChunkBits;
+    const uint64_t slots = nb * nch;
+    const uint64_t bytes = slots * (sizeof(ChunkRec) + 8) + nb * 8 + 256;
+    if (bytes > kScratchBytes || slots / kDecWaves + 1 >= (1ull << 31)) return QSGD_ERR_SCRATCH;
+    uint64_t *ws = scratch_on_current_device();
+    if (!ws) return QSGD_ERR_LAUNCH;
+    ChunkParams C{};
+    C.D.nstreams = 1;
+    C.D.v_hat = v_hat;
+    C.D.n = n; C.D.nb = nb; C.D.s = s; C.D.d = d;
+    C.D.s_pow2 = (s & (s - 1)) == 0 ? 1u : 0u;
+    C.D.inv_s = 1.0 / (double)s;
+    C.D.team = 64;
+    C.D.tpw = 1;
+    C.D.lds_out = 0;
+    C.rec = reinterpret_cast<ChunkRec *>(ws);
+    C.vstart = reinterpret_cast<uint32_t *>(C.rec + slots);
+    C.vbase = C.vstart + slots;
+    C.bstate = C.vbase + slots;
+    C.nch = (uint32_t)nch;
+    const size_t lds = decode_lds_bytes();
+    const uint32_t grid = (uint32_t)((slots + kDecWaves - 1) / kDecWaves);
+    const uint32_t fgrid = (uint32_t)((nb + kDecWaves - 1) / kDecWaves);
+    for (uint32_t k = 0; k < nstreams; ++k) {
+        C.in = in[k];
+        C.offs = offsets[k];
+        if (code == QSGD_CODE_GAMMA) hipLaunchKernelGGL(chunk_parse_kernel<1>, dim3(grid), dim3(kDecWG), lds, stream, C);
+        else hipLaunchKernelGGL(chunk_parse_kernel<0>, dim3(grid), dim3(kDecWG), lds, stream, C);
+        hipLaunchKernelGGL(chunk_scan_kernel, dim3((uint32_t)nb), dim3(kWG), 0, stream, C);
+        auto write = [&](auto wk, auto fk) {
+            hipLaunchKernelGGL(wk, dim3(grid), dim3(kDecWG), lds, stream, C);
+            hipLaunchKernelGGL(fk, dim3(fgrid), dim3(kDecWG), lds, stream, C);
+        };
+        if (acc) {
+            if (code == QSGD_CODE_GAMMA) write(chunk_write_kernel<true, 1>, chunk_fallback_kernel<true, 1>);
+            else write(chunk_write_kernel<true, 0>, chunk_fallback_kernel<true, 0>);
+        } else {
+            if (code == QSGD_CODE_GAMMA) write(chunk_write_kernel<false, 1>, chunk_fallback_kernel<false, 1>);
+            else write(chunk_write_kernel<false, 0>, chunk_fallback_kernel<false, 0>);
+        }
+        if (hipGetLastError() != hipSuccess) return QSGD_ERR_LAUNCH;
+    }
+    return QSGD_OK;
+}
+
 // Decodes one stream into v_hat, or (acc) adds the decodes of the nstreams
 // streams in[k] / offsets[k] to v_hat in stream order.
 qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offsets, uint32_t nstreams,
@@ -358,6 +440,7 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
         if (!in[k] || !offsets[k]) return QSGD_ERR_INVALID_ARG;
     if (!v_hat || !aligned16(v_hat)) return QSGD_ERR_INVALID_ARG;
     if (!bstart) d = eff_d(n, d);
+    if (!bstart && d > kChunkD) return decode_chunked(in, offsets, nstreams, acc, n, nb, s, d, v_hat, stream, code);
     if (d > (1u << 24)) return QSGD_ERR_UNSUPPORTED;
     DecodeParams D{};
     for (uint32_t k = 0; k < nstreams; ++k) {
@@ -421,29 +504,6 @@ uint64_t ragged_count(const uint64_t *seg_len, uint32_t nseg, uint32_t d, uint64
     }
     if (table) table[nb] = base;
     return nb;
-}
-
-// ---- fixed scratch of the no-allocation encode ----------------------------
-// Each device that runs the library holds its own copy of this array for the
-// life of the process. In host code `scratch` is only a stand-in for the symbol:
-// the device address of a device's copy comes from hipGetSymbolAddress, looked
-// up once per device (with that device current) on the first call there.
-constexpr uint64_t kScratchBytes = 64ull << 20;
-constexpr int kMaxDevices = 64;
-static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
-
-uint64_t *scratch_on_current_device() {
-    static std::mutex mu;
-    static uint64_t *addr[kMaxDevices] = {};
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-    std::lock_guard<std::mutex> g(mu);
-    if (!addr[dev]) {
-        void *p = nullptr;
-        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
-        addr[dev] = static_cast<uint64_t *>(p);
-    }
-    return addr[dev];
 }
 
 // The plan of a no-allocation encode: valid (K > 0) only when its workspace

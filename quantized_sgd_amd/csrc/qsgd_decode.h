@@ -685,25 +685,61 @@ __device__ __forceinline__ void wave_sync() {
 // output range with a QuadWriter. CUM: the lanes' gap-prefix tables live in
 // `lvl` (without them, the gap sum before a sync point is found by walking the
 // speculative chain again).
-template <bool RAGGED, bool LDS_IN, bool LDS_OUT, bool ACC, int CODE, bool CUM>
+// A piece of one bucket decoded outside the bucket tables (buckets longer
+// than a chunk): its payload [P0, E) in the reader's positions, the first
+// output coordinate c0 and the output length len (MODE 2), the bucket's length
+// blen (the bound of its gaps), its norm, whether guessed starts take guess
+// steps, and whether lane 0's start is itself a guess (MODE 1, chunks after the
+// first).
+struct GroupView {
+    uint32_t P0, E;
+    uint64_t c0, len, blen;
+    double norm;
+    bool guess, lane0_guess;
+};
+
+// MODE 1 result: the gap sum from P0 along the chunk's chain to its exit X
+// (the first chain position at or past E).
+struct ChunkOut {
+    uint32_t T, X;
+};
+
+// MODE 0: the buckets [b0, b1) of a wave group. MODE 1: parse a chunk of a long
+// bucket with one team (no output; lane 0 may start on a guess). MODE 2: decode
+// a piece [P0, E) of a long bucket that starts on an exact record boundary,
+// with one team, into [c0, c0 + len) (lane writers).
+template <bool RAGGED, bool LDS_IN, bool LDS_OUT, bool ACC, int CODE, bool CUM, int MODE = 0>
 __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64_t *offs,
                                              const uint32_t *lut,
                                              const Bits<LDS_IN> &r, uint64_t gbit, uint64_t b0,
                                              uint64_t b1, uint8_t *lvl, double *ebs, uint64_t lbase,
-                                             uint32_t nclear16) {
+                                             uint32_t nclear16, const GroupView *gv = nullptr,
+                                             ChunkOut *co = nullptr) {
     const int lane = lane_id();
     const uint32_t T = D.team;
     const uint32_t q = (uint32_t)lane % T;
     const uint32_t team = (uint32_t)lane / T;
 
     const uint64_t b = b0 + team;
-    const bool tactive = team < D.tpw && b < b1;
+    const bool tactive = MODE ? team == 0 : (team < D.tpw && b < b1);
     uint32_t A = 0, E = 0;
     uint64_t c0 = 0, len = 0;
     double e_b = 0.0;
     uint32_t nl = 0;
     bool guess = false;
-    if (tactive) {
+    if (MODE && tactive) {
+        A = gv->P0 - 32u;
+        E = gv->E;
+        c0 = gv->c0;
+        len = gv->len;
+        e_b = gv->norm;
+        if (E > gv->P0) {
+            const uint32_t m = (E - gv->P0) / (uint32_t)kSyncWin;
+            nl = m < T ? m : T;
+            if (nl == 0) nl = 1;
+        }
+        guess = gv->guess;
+    } else if (tactive) {
         A = (uint32_t)(offs[b] - gbit);
         E = (uint32_t)(offs[b + 1] - gbit);
         c0 = bucket_first<RAGGED>(D, b);
@@ -723,7 +759,7 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
         }
     }
     if (LDS_OUT && tactive && q == 0) ebs[team] = e_b;
-    const RecordCtx<CODE> x{lut, tactive ? bitlen32((uint32_t)len) : 1u, bitlen32(D.s), D.s};
+    const RecordCtx<CODE> x{lut, tactive ? bitlen32((uint32_t)(MODE ? gv->blen : len)) : 1u, bitlen32(D.s), D.s};
     const uint32_t P0 = A + 32u;
     const uint32_t seg = nl ? ((E - P0) + nl - 1u) / nl : 0u;
     const bool act = q < nl;
@@ -737,7 +773,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
     bool found = false;
     uint8_t *cum = lvl + (uint32_t)lane * kCumSlots;
     uint32_t cum_top = 0;
-    if (act) cx = follow_chain<LDS_IN, true, CUM>(r, x, sq, sn, ga, own0, own1, cum, cum_top, guess && q != 0);
+    const bool lguess = guess && (q != 0 || (MODE == 1 && gv->lane0_guess));
+    if (act) cx = follow_chain<LDS_IN, true, CUM>(r, x, sq, sn, ga, own0, own1, cum, cum_top, lguess);
     if (act && last) found = true;
     // phase B against the next lane's window
     const uint64_t nxt0 = lane_next64(own0, T);
@@ -815,6 +852,14 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
         }
     }
     const uint32_t basej = incl - G;
+
+    if (MODE == 1) {
+        // the team's total and the last lane's exit
+        const uint32_t src = (uint32_t)__builtin_amdgcn_readfirstlane((int)(nl ? nl - 1u : 0u));
+        co->T = nl ? (uint32_t)__builtin_amdgcn_readlane((int)incl, (int)src) : 0u;
+        co->X = nl ? (uint32_t)__builtin_amdgcn_readlane((int)cx, (int)src) : P0;
+        return;
+    }
 
     if (LDS_OUT) {
         // the gap-prefix tables are done with: clear the group's level bytes
@@ -1030,4 +1075,269 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     }
 }
 
+
+// ---- buckets longer than a chunk ---------------------------------------------
+// A bucket whose payload is too long for one team is cut into chunks of
+// kChunkBits bits, one wave each:
+//   chunk_parse_kernel: the team parses its chunk as a bucket whose lane 0
+//     starts on a guess (chunk 0: the exact payload start), giving the gap sum T
+//     along that chain to its exit X; lane 0 then follows the true chain on from
+//     X and the next chunk's lane-0 chain from that chunk's start, always
+//     stepping the one behind, until they meet at y (within kChunkMerge bits):
+//     y is an exact record boundary of the next chunk, with gx the gaps from X
+//     to y and g0 those of the next chunk's chain before y;
+//   chunk_scan_kernel: per bucket, chunk c holds the records from y_{c-1} to
+//     y_c, whose gaps sum to T_c - g0_{c-1} + gx_c; a scan gives each chunk its
+//     first coordinate;
+//   chunk_write_kernel: each chunk decoded from its exact start y_{c-1} to y_c
+//     by the same team parse (lane writers);
+//   chunk_fallback_kernel: a bucket where two chains do not meet within the
+//     window (or whose stream is malformed) is decoded whole by one team.
+// Their records live in the library's fixed scratch.
+constexpr uint32_t kChunkBits = 64u * 256u;   // 256 bits per lane
+constexpr uint32_t kChunkMerge = 8192u;       // bits of the next chunk the merge search may use
+constexpr uint32_t kChunkFail = 0xffffffffu;
+
+struct ChunkRec {       // per chunk slot, written by chunk_parse_kernel
+    uint32_t y;         // merge point relative to the bucket's first stream bit (kChunkFail: none)
+    uint32_t g0, T, gx;
+};
+
+struct ChunkParams {
+    DecodeParams D;
+    const uint64_t *in;       // the stream
+    const uint64_t *offs;     // its bucket offsets
+    ChunkRec *rec;            // [nb * nch]
+    uint32_t *vstart;         // [nb * nch] exact start of chunk c's records (relative to the bucket)
+    uint32_t *vbase;          // [nb * nch] bucket index of chunk c's first coordinate
+    uint32_t *bstate;         // [nb * 2]: chunks in use, failed flag
+    uint32_t nch;             // chunk slots per bucket
+};
+
+// The payload bit range and chunk count of bucket b.
+__device__ __forceinline__ void chunk_bucket(const ChunkParams &C, uint64_t b, uint64_t &A, uint64_t &E,
+                                             uint64_t &nbits, uint32_t &nact) {
+    A = C.offs[b];
+    E = C.offs[b + 1];
+    nbits = E >= A + 32 ? E - A - 32 : 0;
+    nact = (uint32_t)((nbits + kChunkBits - 1) / kChunkBits);
+}
+
+// Lanes and segment length of a team parse of [P0, E) (as decode_group sets them).
+__device__ __forceinline__ uint32_t chunk_lane0_end(uint32_t P0, uint32_t E) {
+    if (E <= P0) return E;
+    uint32_t nl = (E - P0) / (uint32_t)kSyncWin;
+    nl = nl < 64u ? nl : 64u;
+    if (nl == 0) nl = 1;
+    const uint32_t seg = ((E - P0) + nl - 1u) / nl;
+    return nl == 1u ? E : P0 + seg;
+}
+
+// Stages stream words [w0, w0 + nw) of `in` (zeros at and past total words)
+// bit-reversed into the wave's LDS region, with kStagePad zero words after.
+__device__ __forceinline__ void chunk_stage(uint64_t *stage, const uint64_t *in, uint64_t w0, uint64_t nw,
+                                            uint64_t total_words) {
+    for (uint64_t i = (uint64_t)lane_id(); i < nw + kStagePad; i += 64)
+        stage[i] = (i < nw && w0 + i < total_words) ? __builtin_bitreverse64(in[w0 + i]) : 0ull;
+    wave_sync();
+}
+
+constexpr uint64_t kChunkStageWords = (uint64_t)kBigStageWords;
+static_assert((kChunkBits + kChunkMerge + 256) / 64 + 2 <= kChunkStageWords, "chunk stage");
+
+template <int CODE>
+__global__ __launch_bounds__(kDecWG) void chunk_parse_kernel(ChunkParams C) {
+    extern __shared__ __align__(16) uint64_t dsmem[];
+    uint32_t *lut = reinterpret_cast<uint32_t *>(reinterpret_cast<unsigned char *>(dsmem) +
+                                                 (size_t)kDecWaves * kWaveLdsBytes);
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(CODE ? kRecordLutGamma.e : kRecordLut.e);
+        uint4 *dst = reinterpret_cast<uint4 *>(lut);
+        for (uint32_t i = threadIdx.x; i < sizeof(RecordLut) / 16; i += kDecWG) dst[i] = src[i];
+    }
+    __syncthreads();
+    const int wv = wave_id();
+    uint64_t *stage = reinterpret_cast<uint64_t *>(reinterpret_cast<unsigned char *>(dsmem) +
+                                                   (size_t)wv * kWaveLdsBytes);
+    const uint64_t slot = (uint64_t)blockIdx.x * kDecWaves + (uint64_t)wv;
+    const uint64_t b = slot / C.nch;
+    const uint32_t c = (uint32_t)(slot % C.nch);
+    if (b >= C.D.nb) return;
+    uint64_t A, E, nbits;
+    uint32_t nact;
+    chunk_bucket(C, b, A, E, nbits, nact);
+    if (c >= nact || E - A >= (1ull << 31)) return;
+    const uint64_t c0 = b * C.D.d;
+    const uint64_t blen = (c0 + C.D.d < C.D.n ? c0 + C.D.d : C.D.n) - c0;
+    const bool guess = nbits <= (uint64_t)kGuessBits * blen;
+    const uint64_t total_words = (C.offs[C.D.nb] + 63) >> 6;
+    // stage from the word holding the chunk's first bit through the merge window
+    const uint64_t cs = A + 32 + (uint64_t)c * kChunkBits;
+    const uint64_t ce = cs + kChunkBits < E ? cs + kChunkBits : E;
+    const uint64_t w0 = cs >> 6;
+    const uint64_t wl = (ce + kChunkMerge + 256 + 63) >> 6;
+    chunk_stage(stage, C.in, w0, wl - w0, total_words);
+    Bits<true> rl{nullptr, 0u};
+    const uint64_t lgbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
+    const uint32_t P0r = (uint32_t)(cs - lgbit), Er = (uint32_t)(ce - lgbit);
+    GroupView gv{P0r, Er, 0, 0, blen, 0.0, guess, c > 0};
+    ChunkOut co{0, P0r};
+    decode_group<false, true, false, false, CODE, false, 1>(C.D, nullptr, lut, rl, lgbit, 0, 0, nullptr,
+                                                            nullptr, 0, 0, &gv, &co);
+    ChunkRec rec{kChunkFail, 0, co.T, 0};
+    if (lane_id() == 0) {
+        const RecordCtx<CODE> x{lut, bitlen32((uint32_t)blen), bitlen32(C.D.s), C.D.s};
+        const uint32_t Eb = (uint32_t)(E - lgbit);
+        if (ce == E) {
+            // the last chunk: its chain must end exactly at the bucket's end
+            if (co.X == Eb) rec.y = (uint32_t)(E - A);
+        } else {
+            // the next chunk's lane 0 starts at ce with the same guess steps
+            uint32_t pa = co.X, pb = Er, ga = 0, gb = 0;
+            Win Wa = win_at(rl, pa), Wb = win_at(rl, pb);
+            const uint64_t ce2 = ce + kChunkBits < E ? ce + kChunkBits : E;
+            if (guess) guess_steps(rl, x, pb, chunk_lane0_end(Er, (uint32_t)(ce2 - lgbit)), gb, Wb);
+            const uint32_t lim = Er + kChunkMerge;
+            while (pa != pb && pa <= lim && pb <= lim && pa <= Eb && pb <= Eb) {
+                if (pa < pb) chain_step(rl, x, pa, ga, Wa);
+                else chain_step(rl, x, pb, gb, Wb);
+            }
+            if (pa == pb && pa <= lim && pa <= Eb) {
+                rec.y = (uint32_t)(pa + lgbit - A);
+                rec.g0 = gb;
+                rec.gx = ga;
+            }
+        }
+        C.rec[slot] = rec;
+    }
+}
+
+// One workgroup per bucket: each chunk's first coordinate, or the bucket marked
+// failed.
+__global__ __launch_bounds__(kWG) void chunk_scan_kernel(ChunkParams C) {
+    __shared__ uint64_t tot[kWG];
+    __shared__ uint32_t bad;
+    const uint64_t b = blockIdx.x;
+    const uint32_t j = threadIdx.x;
+    uint64_t A, E, nbits;
+    uint32_t nact;
+    chunk_bucket(C, b, A, E, nbits, nact);
+    const uint64_t c0 = b * C.D.d;
+    const uint64_t blen = (c0 + C.D.d < C.D.n ? c0 + C.D.d : C.D.n) - c0;
+    if (j == 0) bad = (nact > C.nch || E - A >= (1ull << 31)) ? 1u : 0u;
+    __syncthreads();
+    const uint32_t na = bad ? 0u : nact;
+    // thread j takes chunks [j * per, (j + 1) * per)
+    const uint32_t per = (na + kWG - 1) / kWG;
+    const ChunkRec *R = C.rec + b * C.nch;
+    uint64_t sum = 0;
+    uint32_t mybad = 0;
+    for (uint32_t i = 0; i < per; ++i) {
+        const uint32_t cc = j * per + i;
+        if (cc >= na) break;
+        const ChunkRec rc = R[cc];
+        const uint32_t g0p = cc ? R[cc - 1].g0 : 0u;
+        if (rc.y == kChunkFail || (cc && R[cc - 1].y == kChunkFail) || rc.T < g0p) mybad = 1u;
+        sum += (uint64_t)rc.T - g0p + rc.gx;
+    }
+    tot[j] = sum;
+    if (mybad) bad = 1u;
+    __syncthreads();
+    uint64_t base = 0, all = 0;
+    for (uint32_t v = 0; v < kWG; ++v) {
+        if (v < j) base += tot[v];
+        all += tot[v];
+    }
+    if (all > blen) bad = 1u;
+    __syncthreads();
+    if (!bad) {
+        for (uint32_t i = 0; i < per; ++i) {
+            const uint32_t cc = j * per + i;
+            if (cc >= na) break;
+            const ChunkRec rc = R[cc];
+            C.vstart[b * C.nch + cc] = cc ? R[cc - 1].y : 32u;
+            C.vbase[b * C.nch + cc] = (uint32_t)base;
+            base += (uint64_t)rc.T - (cc ? R[cc - 1].g0 : 0u) + rc.gx;
+        }
+    }
+    if (j == 0) {
+        C.bstate[2 * b] = na;
+        C.bstate[2 * b + 1] = bad;
+    }
+}
+
+// The bucket norm from the stream's 32 bits at bit A.
+__device__ __forceinline__ float chunk_norm(const uint64_t *in, uint64_t A) {
+    const uint64_t w = in[A >> 6];
+    const uint32_t sh = (uint32_t)(A & 63u);
+    uint64_t x = w << sh;
+    if (sh > 32u) x |= in[(A >> 6) + 1] >> (64u - sh);
+    return __uint_as_float((uint32_t)(x >> 32));
+}
+
+template <bool ACC, int CODE>
+__global__ __launch_bounds__(kDecWG) void chunk_write_kernel(ChunkParams C) {
+    extern __shared__ __align__(16) uint64_t dsmem[];
+    uint32_t *lut = reinterpret_cast<uint32_t *>(reinterpret_cast<unsigned char *>(dsmem) +
+                                                 (size_t)kDecWaves * kWaveLdsBytes);
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(CODE ? kRecordLutGamma.e : kRecordLut.e);
+        uint4 *dst = reinterpret_cast<uint4 *>(lut);
+        for (uint32_t i = threadIdx.x; i < sizeof(RecordLut) / 16; i += kDecWG) dst[i] = src[i];
+    }
+    __syncthreads();
+    const int wv = wave_id();
+    uint64_t *stage = reinterpret_cast<uint64_t *>(reinterpret_cast<unsigned char *>(dsmem) +
+                                                   (size_t)wv * kWaveLdsBytes);
+    const uint64_t slot = (uint64_t)blockIdx.x * kDecWaves + (uint64_t)wv;
+    const uint64_t b = slot / C.nch;
+    const uint32_t c = (uint32_t)(slot % C.nch);
+    if (b >= C.D.nb) return;
+    const uint32_t na = C.bstate[2 * b], bad = C.bstate[2 * b + 1];
+    if (bad || c >= na) return;
+    uint64_t A, E, nbits;
+    uint32_t nact;
+    chunk_bucket(C, b, A, E, nbits, nact);
+    const uint64_t c0 = b * C.D.d;
+    const uint64_t blen = (c0 + C.D.d < C.D.n ? c0 + C.D.d : C.D.n) - c0;
+    const bool guess = nbits <= (uint64_t)kGuessBits * blen;
+    const uint64_t vs = A + C.vstart[slot];
+    const uint64_t ve = A + C.rec[slot].y;
+    const uint64_t base = C.vbase[slot];
+    const uint64_t vend = c + 1 < na ? C.vbase[slot + 1] : blen;
+    const uint64_t total_words = (C.offs[C.D.nb] + 63) >> 6;
+    const uint64_t w0 = vs >> 6;
+    const uint64_t wl = (ve + 256 + 63) >> 6;
+    chunk_stage(stage, C.in, w0, wl - w0, total_words);
+    Bits<true> rl{nullptr, 0u};
+    const uint64_t lgbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
+    GroupView gv{(uint32_t)(vs - lgbit), (uint32_t)(ve - lgbit), c0 + base, vend - base, blen,
+                 (double)chunk_norm(C.in, A), guess, false};
+    decode_group<false, true, false, ACC, CODE, false, 2>(C.D, nullptr, lut, rl, lgbit, 0, 0, nullptr,
+                                                          nullptr, 0, 0, &gv, nullptr);
+}
+
+// One wave per bucket: a failed bucket decoded whole by one team, reading the
+// stream from global memory.
+template <bool ACC, int CODE>
+__global__ __launch_bounds__(kDecWG) void chunk_fallback_kernel(ChunkParams C) {
+    extern __shared__ __align__(16) uint64_t dsmem[];
+    uint32_t *lut = reinterpret_cast<uint32_t *>(reinterpret_cast<unsigned char *>(dsmem) +
+                                                 (size_t)kDecWaves * kWaveLdsBytes);
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(CODE ? kRecordLutGamma.e : kRecordLut.e);
+        uint4 *dst = reinterpret_cast<uint4 *>(lut);
+        for (uint32_t i = threadIdx.x; i < sizeof(RecordLut) / 16; i += kDecWG) dst[i] = src[i];
+    }
+    __syncthreads();
+    const uint64_t b = (uint64_t)blockIdx.x * kDecWaves + (uint64_t)wave_id();
+    if (b >= C.D.nb || !C.bstate[2 * b + 1]) return;
+    const uint64_t total_words = (C.offs[C.D.nb] + 63) >> 6;
+    const uint64_t A0 = C.offs[b];
+    const uint64_t w0 = A0 >> 6;
+    if (w0 >= total_words || C.offs[b + 1] - A0 >= (1ull << 31)) return;
+    Bits<false> rg{reinterpret_cast<const uint32_t *>(C.in + w0), (uint32_t)(2 * (total_words - w0)) - 1u};
+    decode_group<false, false, false, ACC, CODE, false>(C.D, C.offs, lut, rg, w0 * 64, b, b + 1, nullptr,
+                                                        nullptr, 0, 0);
+}
 }  // namespace qsgd

@@ -1,0 +1,89 @@
+"""GPU parity of the decode of buckets longer than 16384 coordinates, which is
+cut into chunks of 16384 stream bits, one wave each (page "QSGD (Quantized
+Stochastic Gradient Descent) with Elias Coding", definition paragraph: the
+coding is lossless, for the whole vector v in R^n as for buckets).
+
+Cases: the whole-vector operator d = n at n = 4097, 10^6 and 60,192,808 (the
+ResNet-152-sized gradient as one bucket); streams on which chunk chains never
+meet, decoded by the whole-bucket fallback (constant vectors with
+s = sqrt(n), where every record is the same 3 bits, so chains started a
+multiple of 3 bits apart never meet); a mix of such buckets with Gaussian
+ones; the gamma code; and decode-accumulate over long buckets."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_sgd_amd as q
+from quantized_sgd_amd import workloads as wl
+from tests.parity import check_parity, to_dev, u64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.lib()
+
+
+@pytest.mark.parametrize("n,s,seed", [(4097, 4, 1), (1_000_000, 1000, 2), (1_000_000, 64, 3)])
+def test_whole_vector(n, s, seed):
+    print(f"whole vector n={n} s={s}", flush=True)
+    check_parity(wl.small_gaussian(n, seed), s, n, seed)
+
+
+@pytest.mark.parametrize("s", [64, 7759])
+def test_whole_vector_config3_gradient(s):
+    # the ResNet-152-sized gradient as one bucket, at the config's s and at
+    # s ~ sqrt(n), where the stream spans tens of thousands of chunks
+    w = wl.config3()
+    print(f"whole vector n={w.n} s={s} (config-3 gradient as one bucket)", flush=True)
+    g, _ = check_parity(w.v, s, w.n, w.seed)
+    print(f"  stream bits {g['bits']}", flush=True)
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_out_of_phase_chunks_take_the_fallback(sign):
+    # n = 65536 and s = 256 = sqrt(n): r = 1 exactly, every record is the same
+    # 3 bits, and chunk 1 starts 16384 = 1 (mod 3) bits after chunk 0
+    n, s = 65536, 256
+    v = np.full(n, sign, np.float32)
+    print(f"constant vector sign={sign}", flush=True)
+    g, _ = check_parity(v, s, n, 5)
+    assert g["bits"] == 32 + 3 * n
+
+
+def test_mixed_buckets_some_falling_back():
+    d, s = 65536, 256
+    v = np.concatenate([np.full(d, 1.0, np.float32), wl.small_gaussian(d, 6),
+                        np.full(d, -2.0, np.float32), wl.small_gaussian(d + 123, 7)])
+    print("mixed buckets", flush=True)
+    check_parity(v, s, d, 8)
+
+
+def test_chunked_gamma_and_maxnorm():
+    print("chunked gamma / maxnorm", flush=True)
+    check_parity(wl.small_gaussian(300000, 9), 16, 100000, 9, code=oracle.GAMMA)
+    check_parity(wl.small_gaussian(300000, 10), 64, 150000, 10, norm=q.MAXNORM)
+
+
+def test_chunked_decode_accumulate():
+    n, d, s = 400000, 200000, 64
+    bst = oracle.uniform_buckets(n, d)
+    streams, dev = [], []
+    for j in range(3):
+        v = wl.small_gaussian(n, 20 + j)
+        lev, nrm = oracle.quantize(v, bst, s, 30 + j)
+        words, offs, _ = oracle.encode(lev, nrm, bst, s)
+        streams.append((words, offs))
+        dev.append((to_dev(words.view(np.int64)), to_dev(offs.view(np.int64))))
+    acc0 = wl.small_gaussian(n, 40)
+    acc = to_dev(acc0.copy())
+    print("chunked decode-accumulate", flush=True)
+    q.decode_accumulate([w for w, _ in dev], [o for _, o in dev], n, s, d, acc)
+    torch.cuda.synchronize()
+    rc, want = oracle.decode_accumulate(streams, bst, s, acc0.copy())
+    assert rc == oracle.OK
+    assert np.array_equal(acc.cpu().numpy().view(np.uint32), want.view(np.uint32))
