@@ -210,6 +210,13 @@ qsgd_status qsgd_decode_accumulate(const uint64_t *const *in, const uint64_t *co
                                    uint32_t k, uint64_t n, uint32_t s, uint32_t d, float *acc,
                                    hipStream_t stream);
 
+/* qsgd_decode_accumulate for streams of either record code (all k streams of
+ * the same code) and uniform (bucket_start NULL, nb = ceil(n/d)) or ragged
+ * buckets; arguments otherwise as above and as in qsgd_decode_ex. */
+qsgd_status qsgd_decode_accumulate_ex(const uint64_t *const *in, const uint64_t *const *bucket_bit_offsets,
+                                      uint32_t k, uint64_t n, const uint64_t *bucket_start, uint64_t nb,
+                                      uint32_t s, uint32_t d, qsgd_code code, float *acc, hipStream_t stream);
+
 /* ---- ragged batches: several tensors in one flat buffer --------------------
  * Buckets restart at every tensor boundary (per-tensor quantization); the
  * Philox index of a coordinate is its flat index in the concatenation. The
@@ -246,6 +253,23 @@ qsgd_status qsgd_decode_accumulate_ragged(const uint64_t *const *in,
                                           const uint64_t *const *bucket_bit_offsets, uint32_t k,
                                           uint64_t n, const uint64_t *bucket_start, uint64_t nb,
                                           uint32_t s, uint32_t d, float *acc, hipStream_t stream);
+
+/* ---- ragged batches given by HOST tensor lengths ---------------------------
+ * The same three calls with the layout given as HOST seg_len[nseg] (tensor
+ * lengths, buckets of at most d restarting at every tensor, n = the sum of the
+ * lengths, nb = qsgd_num_buckets_ragged(seg_len, nseg, d)) instead of a device
+ * bucket table: the lengths travel in the kernel arguments, so these take at
+ * most 160 tensors (more returns QSGD_ERR_UNSUPPORTED before anything is
+ * enqueued; the table form has no such limit). Results are those of the table
+ * form for the same layout; out needs qsgd_encode_capacity_words_ragged(n, nb, s,
+ * d) words; seg_len is read during the call only. */
+qsgd_status qsgd_quantize_seglen(const float *v, const uint64_t *seg_len, uint32_t nseg, uint32_t s,
+                                 uint32_t d, uint64_t seed, int32_t *levels, float *norms, hipStream_t stream);
+qsgd_status qsgd_encode_seglen(const float *v, const uint64_t *seg_len, uint32_t nseg, uint32_t s, uint32_t d,
+                               uint64_t seed, uint64_t *out, uint64_t *out_bits, uint64_t *bucket_bit_offsets,
+                               hipStream_t stream);
+qsgd_status qsgd_decode_seglen(const uint64_t *in, const uint64_t *bucket_bit_offsets, const uint64_t *seg_len,
+                               uint32_t nseg, uint32_t s, uint32_t d, float *v_hat, hipStream_t stream);
 
 /* ---- encode without allocation ----------------------------------------------
  * For callers that cannot allocate device memory during the call (code under

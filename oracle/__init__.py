@@ -91,6 +91,10 @@ def lib():
         L.or_decode_accumulate.argtypes = [ctypes.c_void_p, _u64p, ctypes.c_void_p, ctypes.c_uint64,
                                            _u64p, ctypes.c_uint64, ctypes.c_uint32, _f32p, _f32p]
         L.or_decode_accumulate.restype = ctypes.c_int
+        L.or_decode_accumulate_code.argtypes = [ctypes.c_void_p, _u64p, ctypes.c_void_p, ctypes.c_uint64,
+                                                _u64p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, _f32p,
+                                                _f32p]
+        L.or_decode_accumulate_code.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -261,9 +265,10 @@ def decode(words, offsets, bstart, s: int, code: int = OMEGA):
     return int(rc), out[: int(bstart[-1])]
 
 
-def decode_accumulate(streams, bstart, s: int, acc):
-    """streams: list of (words, offsets). Returns (status, acc + the decodes added
-    in list order, one fp32 addition per stream and coordinate)."""
+def decode_accumulate(streams, bstart, s: int, acc, code: int = OMEGA):
+    """streams: list of (words, offsets) of the record code `code`. Returns
+    (status, acc + the decodes added in list order, one fp32 addition per
+    stream and coordinate)."""
     bstart = np.ascontiguousarray(bstart, dtype=np.uint64)
     n = int(bstart[-1])
     out = np.array(acc, dtype=np.float32, copy=True)
@@ -276,9 +281,9 @@ def decode_accumulate(streams, bstart, s: int, acc):
     wp = (ctypes.c_void_p * max(k, 1))(*[w.ctypes.data for w in ws])
     op = (ctypes.c_void_p * max(k, 1))(*[o.ctypes.data for o in offs])
     scratch = np.zeros(n, dtype=np.float32)
-    rc = lib().or_decode_accumulate(ctypes.addressof(wp), _p(nwords, _u64p), ctypes.addressof(op), k,
-                                    _p(bstart, _u64p), len(bstart) - 1, s, _p(out, _f32p),
-                                    _p(scratch, _f32p))
+    rc = lib().or_decode_accumulate_code(ctypes.addressof(wp), _p(nwords, _u64p), ctypes.addressof(op), k,
+                                         _p(bstart, _u64p), len(bstart) - 1, s, code, _p(out, _f32p),
+                                         _p(scratch, _f32p))
     return int(rc), out
 
 

@@ -389,9 +389,16 @@ int or_decode_code(const uint64_t *words, uint64_t nwords, const uint64_t *offse
 int or_decode_accumulate(const uint64_t *const *words, const uint64_t *nwords,
                          const uint64_t *const *offsets, uint64_t k, const uint64_t *bstart,
                          uint64_t nb, uint32_t s, float *acc, float *scratch) {
+    return or_decode_accumulate_code(words, nwords, offsets, k, bstart, nb, s, 0, acc, scratch);
+}
+
+/* The same with the record code of the streams (omega 0, gamma 1). */
+int or_decode_accumulate_code(const uint64_t *const *words, const uint64_t *nwords,
+                              const uint64_t *const *offsets, uint64_t k, const uint64_t *bstart,
+                              uint64_t nb, uint32_t s, int code, float *acc, float *scratch) {
     const uint64_t n = bstart[nb];
     for (uint64_t j = 0; j < k; ++j) {
-        int rc = or_decode(words[j], nwords[j], offsets[j], bstart, nb, s, scratch);
+        int rc = or_decode_code(words[j], nwords[j], offsets[j], bstart, nb, s, code, scratch);
         if (rc != OR_OK) return rc;
         for (uint64_t i = 0; i < n; ++i) acc[i] = acc[i] + scratch[i];
     }

@@ -127,6 +127,10 @@ int or_decode_code(const uint64_t *words, uint64_t nwords, const uint64_t *offse
 int or_decode_accumulate(const uint64_t *const *words, const uint64_t *nwords,
                          const uint64_t *const *offsets, uint64_t k, const uint64_t *bstart,
                          uint64_t nb, uint32_t s, float *acc, float *scratch);
+/* or_decode_accumulate for streams of the given record code (0 omega, 1 gamma). */
+int or_decode_accumulate_code(const uint64_t *const *words, const uint64_t *nwords,
+                              const uint64_t *const *offsets, uint64_t k, const uint64_t *bstart,
+                              uint64_t nb, uint32_t s, int code, float *acc, float *scratch);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,8 @@ __all__ = [
     "QsgdError", "lib", "num_buckets", "encode_capacity_words", "quantize", "encode",
     "decode", "RaggedLayout", "quantize_ragged", "encode_ragged", "decode_ragged",
     "max_bucket", "max_streams", "decode_accumulate", "decode_accumulate_ragged", "OMEGA", "GAMMA",
-    "L2", "MAXNORM", "encode_noalloc", "encode_noalloc_capacity_words",
+    "L2", "MAXNORM", "encode_noalloc", "encode_noalloc_capacity_words", "quantize_seglen", "encode_seglen",
+    "decode_seglen",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,10 +81,15 @@ def lib():
         L.qsgd_max_streams.restype = _u32
         L.qsgd_decode_accumulate.argtypes = [_vp, _vp, _u32, _u64, _u32, _u32, _vp, _vp]
         L.qsgd_decode_accumulate_ragged.argtypes = [_vp, _vp, _u32, _u64, _vp, _u64, _u32, _u32, _vp, _vp]
+        L.qsgd_decode_accumulate_ex.argtypes = [_vp, _vp, _u32, _u64, _vp, _u64, _u32, _u32, ctypes.c_int, _vp, _vp]
+        L.qsgd_quantize_seglen.argtypes = [_vp, _vp, _u32, _u32, _u32, _u64, _vp, _vp, _vp]
+        L.qsgd_encode_seglen.argtypes = [_vp, _vp, _u32, _u32, _u32, _u64, _vp, _vp, _vp, _vp]
+        L.qsgd_decode_seglen.argtypes = [_vp, _vp, _vp, _u32, _u32, _u32, _vp, _vp]
         L.qsgd_encode_noalloc_capacity_words.argtypes = [_u64, _u32, _u32]
         L.qsgd_encode_noalloc_capacity_words.restype = _u64
         L.qsgd_encode_noalloc.argtypes = [_vp, _u64, _u32, _u32, _u64, _vp, _vp, _vp, _vp]
-        for name in ("qsgd_encode_noalloc", "qsgd_quantize", "qsgd_encode", "qsgd_decode", "qsgd_ragged_bucket_table",
+        for name in ("qsgd_encode_noalloc", "qsgd_decode_accumulate_ex", "qsgd_quantize_seglen",
+                     "qsgd_encode_seglen", "qsgd_decode_seglen", "qsgd_quantize", "qsgd_encode", "qsgd_decode", "qsgd_ragged_bucket_table",
                      "qsgd_quantize_ragged", "qsgd_encode_ragged", "qsgd_decode_ragged",
                      "qsgd_decode_accumulate", "qsgd_decode_accumulate_ragged", "qsgd_encode_ex",
                      "qsgd_decode_ex", "qsgd_quantize_ex"):
@@ -212,13 +218,21 @@ def _pointer_arrays(words_list, offsets_list):
 
 
 def decode_accumulate(words_list, offsets_list, n: int, s: int, d: int, acc: torch.Tensor,
-                      stream=None):
-    """acc += the decodes of the streams, added in list order per coordinate
-    (one fp32 rounding per addition); returns acc."""
+                      stream=None, code: int = OMEGA):
+    """acc += the decodes of the streams (all of record code `code`), added in
+    list order per coordinate (one fp32 rounding per addition); returns acc."""
     k, ins, offs = _pointer_arrays(words_list, offsets_list)
-    _check(lib().qsgd_decode_accumulate(ctypes.addressof(ins), ctypes.addressof(offs), k, n, s, d,
-                                        _dev(acc, torch.float32, "acc"), _stream(stream)),
-           "qsgd_decode_accumulate")
+    if acc.numel() < n:
+        raise ValueError(f"acc holds {acc.numel()} values, needs {n}")
+    if code == OMEGA:
+        _check(lib().qsgd_decode_accumulate(ctypes.addressof(ins), ctypes.addressof(offs), k, n, s, d,
+                                            _dev(acc, torch.float32, "acc"), _stream(stream)),
+               "qsgd_decode_accumulate")
+    else:
+        _check(lib().qsgd_decode_accumulate_ex(ctypes.addressof(ins), ctypes.addressof(offs), k, n, None,
+                                               num_buckets(n, d), s, d, code, _dev(acc, torch.float32, "acc"),
+                                               _stream(stream)),
+               "qsgd_decode_accumulate_ex")
     return acc
 
 
@@ -346,3 +360,57 @@ def encode_noalloc(v: torch.Tensor, s: int, d: int, seed: int, out: torch.Tensor
                                      _dev(offsets, torch.int64, "offsets"), _stream(stream)),
            "qsgd_encode_noalloc")
     return out, out_bits, offsets
+
+
+def _seg_lengths(seg_len):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(seg_len, dtype=np.uint64))
+
+
+def quantize_seglen(v: torch.Tensor, seg_len, s: int, d: int, seed: int, stream=None):
+    """qsgd_quantize_seglen: the ragged quantize with the layout given by the
+    host tensor lengths (at most 160 tensors). Returns (levels, norms)."""
+    sl = _seg_lengths(seg_len)
+    n = int(sl.sum())
+    if v.numel() < n:
+        raise ValueError(f"v holds {v.numel()} values, the lengths sum to {n}")
+    nb = int(lib().qsgd_num_buckets_ragged(sl.ctypes.data, len(sl), d))
+    levels = torch.empty(max(n, 1), dtype=torch.int32, device=v.device)
+    norms = torch.empty(max(nb, 1), dtype=torch.float32, device=v.device)
+    _check(lib().qsgd_quantize_seglen(_dev(v, torch.float32, "v"), sl.ctypes.data, len(sl), s, d, seed,
+                                      _dev(levels, torch.int32, "levels"), _dev(norms, torch.float32, "norms"),
+                                      _stream(stream)), "qsgd_quantize_seglen")
+    return levels[:n], norms[:nb]
+
+
+def encode_seglen(v: torch.Tensor, seg_len, s: int, d: int, seed: int, stream=None):
+    """qsgd_encode_seglen: returns (out words, out_bits [1], offsets [nb + 1])."""
+    sl = _seg_lengths(seg_len)
+    n = int(sl.sum())
+    if v.numel() < n:
+        raise ValueError(f"v holds {v.numel()} values, the lengths sum to {n}")
+    nb = int(lib().qsgd_num_buckets_ragged(sl.ctypes.data, len(sl), d))
+    cap = int(lib().qsgd_encode_capacity_words_ragged(n, nb, s, d))
+    if cap == 0:
+        raise QsgdError(QSGD_ERR_UNSUPPORTED, "qsgd_encode_capacity_words_ragged")
+    out = torch.empty(cap, dtype=torch.int64, device=v.device)
+    out_bits = torch.empty(1, dtype=torch.int64, device=v.device)
+    offsets = torch.empty(nb + 1, dtype=torch.int64, device=v.device)
+    _check(lib().qsgd_encode_seglen(_dev(v, torch.float32, "v"), sl.ctypes.data, len(sl), s, d, seed,
+                                    _dev(out, torch.int64, "out"), _dev(out_bits, torch.int64, "out_bits"),
+                                    _dev(offsets, torch.int64, "offsets"), _stream(stream)), "qsgd_encode_seglen")
+    return out, out_bits, offsets
+
+
+def decode_seglen(words: torch.Tensor, offsets: torch.Tensor, seg_len, s: int, d: int, stream=None):
+    """qsgd_decode_seglen: the ragged decode with host tensor lengths."""
+    sl = _seg_lengths(seg_len)
+    n = int(sl.sum())
+    nb = int(lib().qsgd_num_buckets_ragged(sl.ctypes.data, len(sl), d))
+    if offsets.numel() < nb + 1:
+        raise ValueError(f"offsets holds {offsets.numel()} words, needs {nb + 1}")
+    v_hat = torch.empty(max(n, 1), dtype=torch.float32, device=words.device)
+    _check(lib().qsgd_decode_seglen(_dev(words, torch.int64, "words"), _dev(offsets, torch.int64, "offsets"),
+                                    sl.ctypes.data, len(sl), s, d, _dev(v_hat, torch.float32, "v_hat"),
+                                    _stream(stream)), "qsgd_decode_seglen")
+    return v_hat[:n]

@@ -209,13 +209,13 @@ uint64_t *scratch_on_current_device() {
 
 qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb,
                           uint32_t s, uint32_t d, uint64_t seed, int32_t *levels, float *norms,
-                          hipStream_t stream, uint32_t norm = QSGD_NORM_L2) {
+                          hipStream_t stream, uint32_t norm = QSGD_NORM_L2, const SegTable *seg = nullptr) {
     qsgd_status st = check_common(v, s, d);
     if (st != QSGD_OK) return st;
     if (norm > QSGD_NORM_MAX) return QSGD_ERR_INVALID_ARG;
     if (n == 0) return QSGD_OK;
     if (!v || !levels || !norms || !aligned16(levels)) return QSGD_ERR_INVALID_ARG;
-    const bool ragged = bstart != nullptr;
+    const bool ragged = bstart != nullptr || seg != nullptr;
     if (!ragged) d = eff_d(n, d);
     EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0), QSGD_CODE_OMEGA, ragged);
     if (p.K == 0) return QSGD_ERR_UNSUPPORTED;
@@ -226,6 +226,7 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
     P.obuf_words = 0;
     P.maxnorm = norm;
     P.sigma = odd_part(s);
+    if (seg) P.seg = *seg;
     if (p.span) {
         // the windows' partial sums live in the levels buffer (24 bytes per
         // window of 16 KB) until the last kernel overwrites it with the levels
@@ -242,7 +243,7 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
         hipLaunchKernelGGL(span_quantize_kernel, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P);
         return launch_status();
     }
-    if (use_aligned(bstart, s, d)) {
+    if (!ragged && use_aligned(nullptr, s, d)) {
         hipLaunchKernelGGL(quantize_aligned_kernel, dim3((uint32_t)p.ntiles), dim3(kWG), 0, stream, P,
                            log2u(d));
         return launch_status();
@@ -260,7 +261,8 @@ qsgd_status quantize_impl(const float *v, uint64_t n, const uint64_t *bstart, ui
 qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint64_t nb, uint32_t s,
                         uint32_t d, uint64_t seed, uint64_t *out, uint64_t *out_bits,
                         uint64_t *offsets, hipStream_t stream, uint32_t code = QSGD_CODE_OMEGA,
-                        uint32_t norm = QSGD_NORM_L2, uint64_t *ws = nullptr) {
+                        uint32_t norm = QSGD_NORM_L2, uint64_t *ws = nullptr,
+                        const SegTable *seg = nullptr) {
     qsgd_status st = check_common(v, s, d);
     if (st != QSGD_OK) return st;
     if (code > QSGD_CODE_GAMMA || norm > QSGD_NORM_MAX) return QSGD_ERR_INVALID_ARG;
@@ -270,7 +272,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
         return launch_status();
     }
     if (!v || !out || !aligned16(out)) return QSGD_ERR_INVALID_ARG;
-    const bool ragged = bstart != nullptr;
+    const bool ragged = bstart != nullptr || seg != nullptr;
     if (!ragged) d = eff_d(n, d);
     EncodePlan p = make_plan(n, nb, s, d, !ragged && (d % 16 == 0), code, ragged);
     if (p.K == 0) return QSGD_ERR_UNSUPPORTED;
@@ -286,6 +288,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
     P.code = code;
     P.maxnorm = norm;
     P.sigma = odd_part(s);
+    if (seg) P.seg = *seg;
     // pass 1 grid: at most the given number of workgroups (and kMaxRuns), each
     // taking a run of consecutive tiles
     auto runs_for = [&](uint32_t resident) {
@@ -330,7 +333,7 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
         return launch_status();
     }
     // pass 1: every tile into its slot
-    if (use_aligned(bstart, s, d)) {
+    if (!ragged && use_aligned(nullptr, s, d)) {
         const size_t lds = aligned_encode_lds_bytes(p.obuf_words);
         // records packed per quarter of a thread when levels are large: mean level
         // about 0.8 s / sqrt(d) under the L2 norm, 0.8 s / max|z| (about s / 4)
@@ -430,7 +433,8 @@ qsgd_status decode_chunked(const uint64_t *const *in, const uint64_t *const *off
 // streams in[k] / offsets[k] to v_hat in stream order.
 qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offsets, uint32_t nstreams,
                         bool acc, uint64_t n, const uint64_t *bstart, uint64_t nb, uint32_t s,
-                        uint32_t d, float *v_hat, hipStream_t stream, uint32_t code = QSGD_CODE_OMEGA) {
+                        uint32_t d, float *v_hat, hipStream_t stream, uint32_t code = QSGD_CODE_OMEGA,
+                        const SegTable *seg = nullptr) {
     qsgd_status st = check_common(nullptr, s, d);
     if (st != QSGD_OK) return st;
     if (code > QSGD_CODE_GAMMA) return QSGD_ERR_INVALID_ARG;
@@ -439,8 +443,9 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
     for (uint32_t k = 0; k < nstreams; ++k)
         if (!in[k] || !offsets[k]) return QSGD_ERR_INVALID_ARG;
     if (!v_hat || !aligned16(v_hat)) return QSGD_ERR_INVALID_ARG;
-    if (!bstart) d = eff_d(n, d);
-    if (!bstart && d > kChunkD) return decode_chunked(in, offsets, nstreams, acc, n, nb, s, d, v_hat, stream, code);
+    const bool ragged = bstart != nullptr || seg != nullptr;
+    if (!ragged) d = eff_d(n, d);
+    if (!ragged && d > kChunkD) return decode_chunked(in, offsets, nstreams, acc, n, nb, s, d, v_hat, stream, code);
     if (d > (1u << 24)) return QSGD_ERR_UNSUPPORTED;
     DecodeParams D{};
     for (uint32_t k = 0; k < nstreams; ++k) {
@@ -452,6 +457,7 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
     D.n = n; D.nb = nb; D.s = s; D.d = d;
     D.s_pow2 = (s & (s - 1)) == 0 ? 1u : 0u;
     D.inv_s = 1.0 / (double)s;
+    if (seg) D.seg = *seg;
     // LDS-staged output: whole groups of buckets of at most kGroupCoords
     // coordinates, levels fit int8. Team size: a power of two, about one lane per
     // 64 coordinates of a bucket, teams * buckets per group <= 64.
@@ -476,17 +482,18 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
         const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, resident_blocks(kernel, lds, kDecWG));
         hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kDecWG), lds, stream, D);
     };
-    // accumulation is served for omega streams; the code is a kernel parameter so
-    // that each kernel holds one record decoder
-    if (acc) {
-        if (code != QSGD_CODE_OMEGA) return QSGD_ERR_UNSUPPORTED;
-        if (bstart) lds_out ? launch(decode_kernel<true, true, true, 0>) : launch(decode_kernel<true, false, true, 0>);
+    // the code is a kernel parameter so that each kernel holds one record decoder
+    if (acc && code == QSGD_CODE_GAMMA) {
+        if (ragged) lds_out ? launch(decode_kernel<true, true, true, 1>) : launch(decode_kernel<true, false, true, 1>);
+        else lds_out ? launch(decode_kernel<false, true, true, 1>) : launch(decode_kernel<false, false, true, 1>);
+    } else if (acc) {
+        if (ragged) lds_out ? launch(decode_kernel<true, true, true, 0>) : launch(decode_kernel<true, false, true, 0>);
         else lds_out ? launch(decode_kernel<false, true, true, 0>) : launch(decode_kernel<false, false, true, 0>);
     } else if (code == QSGD_CODE_GAMMA) {
-        if (bstart) lds_out ? launch(decode_kernel<true, true, false, 1>) : launch(decode_kernel<true, false, false, 1>);
+        if (ragged) lds_out ? launch(decode_kernel<true, true, false, 1>) : launch(decode_kernel<true, false, false, 1>);
         else lds_out ? launch(decode_kernel<false, true, false, 1>) : launch(decode_kernel<false, false, false, 1>);
     } else {
-        if (bstart) lds_out ? launch(decode_kernel<true, true, false, 0>) : launch(decode_kernel<true, false, false, 0>);
+        if (ragged) lds_out ? launch(decode_kernel<true, true, false, 0>) : launch(decode_kernel<true, false, false, 0>);
         else lds_out ? launch(decode_kernel<false, true, false, 0>) : launch(decode_kernel<false, false, false, 0>);
     }
     return launch_status();
@@ -514,6 +521,32 @@ EncodePlan noalloc_plan(uint64_t n, uint32_t s, uint32_t d) {
     EncodePlan p = make_plan(n, nb, s, d, d % 16 == 0);
     if (p.K && p.ws_words * 8 > kScratchBytes) p.K = 0;
     return p;
+}
+
+// Kernel arguments stay within 4 KB with the segment table inside.
+static_assert(sizeof(QsgdParams) <= 3072 && sizeof(DecodeParams) <= 3584 && sizeof(ChunkParams) <= 3840,
+              "kernel argument size");
+
+// The segment table of host tensor lengths seg_len[nseg] with buckets of d;
+// false when nseg exceeds kMaxSegs or a count overflows.
+bool make_seg_table(const uint64_t *seg_len, uint32_t nseg, uint32_t d, SegTable &S, uint64_t &n,
+                    uint64_t &nb) {
+    if (nseg > kMaxSegs || d == 0 || (!seg_len && nseg)) return false;
+    S = SegTable{};
+    S.nseg = nseg;
+    S.d = d;
+    n = 0;
+    nb = 0;
+    for (uint32_t i = 0; i < nseg; ++i) {
+        S.start[i] = n;
+        S.first[i] = (uint32_t)nb;
+        n += seg_len[i];
+        nb += (seg_len[i] + d - 1) / d;
+        if (nb >= (1ull << 32)) return false;
+    }
+    S.start[nseg] = n;
+    S.first[nseg] = (uint32_t)nb;
+    return true;
 }
 
 }  // namespace
@@ -615,6 +648,44 @@ qsgd_status qsgd_decode_accumulate(const uint64_t *const *in, const uint64_t *co
                                    hipStream_t stream) {
     return decode_impl(in, bucket_bit_offsets, k, true, n, nullptr, qsgd_num_buckets(n, d), s, d, acc,
                        stream);
+}
+
+qsgd_status qsgd_quantize_seglen(const float *v, const uint64_t *seg_len, uint32_t nseg, uint32_t s,
+                                 uint32_t d, uint64_t seed, int32_t *levels, float *norms, hipStream_t stream) {
+    SegTable S;
+    uint64_t n, nb;
+    if (d == 0 || (!seg_len && nseg)) return QSGD_ERR_INVALID_ARG;
+    if (!make_seg_table(seg_len, nseg, d, S, n, nb)) return QSGD_ERR_UNSUPPORTED;
+    if (nb == 0) return QSGD_OK;
+    return quantize_impl(v, n, nullptr, nb, s, d, seed, levels, norms, stream, QSGD_NORM_L2, &S);
+}
+
+qsgd_status qsgd_encode_seglen(const float *v, const uint64_t *seg_len, uint32_t nseg, uint32_t s, uint32_t d,
+                               uint64_t seed, uint64_t *out, uint64_t *out_bits, uint64_t *bucket_bit_offsets,
+                               hipStream_t stream) {
+    SegTable S;
+    uint64_t n, nb;
+    if (d == 0 || (!seg_len && nseg)) return QSGD_ERR_INVALID_ARG;
+    if (!make_seg_table(seg_len, nseg, d, S, n, nb)) return QSGD_ERR_UNSUPPORTED;
+    return encode_impl(v, n, nullptr, nb, s, d, seed, out, out_bits, bucket_bit_offsets, stream,
+                       QSGD_CODE_OMEGA, QSGD_NORM_L2, nullptr, &S);
+}
+
+qsgd_status qsgd_decode_seglen(const uint64_t *in, const uint64_t *bucket_bit_offsets, const uint64_t *seg_len,
+                               uint32_t nseg, uint32_t s, uint32_t d, float *v_hat, hipStream_t stream) {
+    SegTable S;
+    uint64_t n, nb;
+    if (d == 0 || (!seg_len && nseg)) return QSGD_ERR_INVALID_ARG;
+    if (!make_seg_table(seg_len, nseg, d, S, n, nb)) return QSGD_ERR_UNSUPPORTED;
+    return decode_impl(&in, &bucket_bit_offsets, 1, false, n, nullptr, nb, s, d, v_hat, stream,
+                       QSGD_CODE_OMEGA, &S);
+}
+
+qsgd_status qsgd_decode_accumulate_ex(const uint64_t *const *in, const uint64_t *const *bucket_bit_offsets,
+                                      uint32_t k, uint64_t n, const uint64_t *bucket_start, uint64_t nb,
+                                      uint32_t s, uint32_t d, qsgd_code code, float *acc, hipStream_t stream) {
+    if (!bucket_start && nb != qsgd_num_buckets(n, d)) return QSGD_ERR_INVALID_ARG;
+    return decode_impl(in, bucket_bit_offsets, k, true, n, bucket_start, nb, s, d, acc, stream, (uint32_t)code);
 }
 
 uint64_t qsgd_num_buckets_ragged(const uint64_t *seg_len, uint32_t nseg, uint32_t d) {

@@ -74,6 +74,7 @@ struct DecodeParams {
     uint32_t lds_out;        // 1: levels staged in LDS (s <= 127, tpw * d <= kGroupCoords)
     uint32_t s_pow2;         // s is a power of two (norm / s exact)
     double inv_s;            // 1 / s (exact when s_pow2)
+    SegTable seg;            // ragged layout by tensor lengths (nseg > 0) instead of bstart
 };
 
 // ---- record table -------------------------------------------------------
@@ -663,7 +664,7 @@ struct QuadWriter {
 
 template <bool RAGGED>
 __device__ __forceinline__ uint64_t bucket_first(const DecodeParams &D, uint64_t b) {
-    if (RAGGED) return D.bstart[b];
+    if (RAGGED) return ragged_start(D.bstart, D.seg, b);
     const uint64_t g = b * D.d;
     return g < D.n ? g : D.n;
 }

@@ -366,6 +366,33 @@ __device__ __forceinline__ double block_seg_excl_sum(double v, int f, double *sv
     return ex;
 }
 
+// ---- ragged bucket layout carried in the kernel arguments ----
+// A batch of at most kMaxSegs tensors given by their lengths: tensor i starts
+// at coordinate start[i] and its buckets (of d coordinates, the last one
+// shorter) are first[i] .. first[i + 1] - 1; start[nseg] = n, first[nseg] = nb.
+// nseg = 0: the layout is the device bucket table instead.
+constexpr uint32_t kMaxSegs = 160;
+
+struct SegTable {
+    uint32_t nseg, d;
+    uint64_t start[kMaxSegs + 1];
+    uint32_t first[kMaxSegs + 1];
+};
+
+// First coordinate of bucket b (b = nb: n): from the segment table, or the
+// device table.
+__device__ __forceinline__ uint64_t ragged_start(const uint64_t *table, const SegTable &S, uint64_t b) {
+    if (S.nseg == 0) return table[b];
+    uint32_t lo = 0, hi = S.nseg;  // the last segment whose first bucket is <= b
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if ((uint64_t)S.first[mid] <= b) lo = mid; else hi = mid - 1;
+    }
+    if (lo == S.nseg) return S.start[S.nseg];
+    const uint64_t g = S.start[lo] + (b - S.first[lo]) * (uint64_t)S.d;
+    return g < S.start[lo + 1] ? g : S.start[lo + 1];
+}
+
 // ---- agent-scope flags for the cross-workgroup protocol ----
 __device__ __forceinline__ uint64_t ld_agent(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

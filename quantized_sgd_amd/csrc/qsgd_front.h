@@ -52,6 +52,7 @@ struct QsgdParams {
     uint32_t maxnorm;      // bucket scale: 0 the L2 norm, 1 the max-norm max|v_i| (QSGDinf)
     uint32_t sigma;        // odd part of s (ratio_may_tie)
     SpanParams sp;         // buckets longer than a tile only
+    SegTable seg;          // ragged layout by tensor lengths (nseg > 0) instead of bstart
 };
 
 // Runs of consecutive tiles: the first `rem` workgroups take run + 1 tiles, the
@@ -88,8 +89,8 @@ __device__ __forceinline__ Tile tile_geometry(const QsgdParams &P, uint32_t tile
     t.b0 = (uint64_t)tile * P.K;
     t.b1 = t.b0 + P.K < P.nb ? t.b0 + P.K : P.nb;
     if (RAGGED) {
-        t.c0 = P.bstart[t.b0];
-        t.c1 = P.bstart[t.b1];
+        t.c0 = ragged_start(P.bstart, P.seg, t.b0);
+        t.c1 = ragged_start(P.bstart, P.seg, t.b1);
     } else {
         t.c0 = t.b0 * P.d;
         const uint64_t e = t.b1 * P.d;
@@ -107,7 +108,7 @@ __device__ __forceinline__ void fill_bucket_starts(const QsgdParams &P, const Ti
     for (uint32_t k = threadIdx.x; k <= t.K; k += kWG) {
         uint64_t g;
         if (RAGGED) {
-            g = P.bstart[t.b0 + k];
+            g = ragged_start(P.bstart, P.seg, t.b0 + k);
         } else {
             g = (t.b0 + k) * P.d;
             if (g > P.n) g = P.n;

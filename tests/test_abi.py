@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(q.LIB_PATH)
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 26
     for name in names:
         assert hasattr(lib, name), name
 
@@ -99,6 +99,17 @@ def test_capacity_bounds_oracle_streams():
     lib = q.lib()
     assert lib.qsgd_encode_capacity_words_ragged(100000, 20, 4, 5000) == 0
     assert lib.qsgd_encode_capacity_words_ragged(100000, 30, 4, 4081) > 0
+
+
+def test_seglen_calls_refuse_more_tensors_than_the_arguments_hold():
+    # more than 160 tensors: refused on the host before anything is enqueued
+    lib = q.lib()
+    seg = np.full(161, 100, np.uint64)
+    assert lib.qsgd_quantize_seglen(16, seg.ctypes.data, 161, 4, 64, 1, 16, 16, None) == q.QSGD_ERR_UNSUPPORTED
+    assert lib.qsgd_encode_seglen(16, seg.ctypes.data, 161, 4, 64, 1, 16, 16, 16, None) == q.QSGD_ERR_UNSUPPORTED
+    assert lib.qsgd_decode_seglen(16, 16, seg.ctypes.data, 161, 4, 64, 16, None) == q.QSGD_ERR_UNSUPPORTED
+    assert lib.qsgd_encode_seglen(16, None, 3, 4, 64, 1, 16, 16, 16, None) == q.QSGD_ERR_INVALID_ARG
+    assert lib.qsgd_encode_seglen(16, seg.ctypes.data, 3, 4, 0, 1, 16, 16, 16, None) == q.QSGD_ERR_INVALID_ARG
 
 
 def test_status_strings():

@@ -116,3 +116,25 @@ def test_full_size_config3_four_streams():
     w = wl.config3()
     vs = [w.v] + [wl.peer_gradient(3, j) for j in range(1, 4)]
     _check(vs, w.s, w.d, w.seed)
+
+
+@pytest.mark.parametrize("n,d,s,k", [(50000, 512, 16, 3), (30000, 4096, 64, 2), (20000, 1000, 300, 4),
+                                     (200000, 50000, 8, 2)])
+def test_gamma_streams(n, d, s, k):
+    # streams of the Elias gamma record code, through qsgd_decode_accumulate_ex
+    vs = [wl.small_gaussian(n, 60 + j) for j in range(k)]
+    bst = oracle.uniform_buckets(n, d)
+    streams = []
+    for j, v in enumerate(vs):
+        _, _, words, offs, _ = oracle.compress(v, bst, s, 70 + j, code=oracle.GAMMA)
+        streams.append((words, offs))
+    acc0 = _start_acc(n, 80)
+    wd = [to_dev(np.ascontiguousarray(w).view(np.int64)) for w, _ in streams]
+    od = [to_dev(np.ascontiguousarray(o).view(np.int64)) for _, o in streams]
+    acc = to_dev(acc0.copy())
+    print(f"gamma accumulate n={n} d={d} s={s} k={k}", flush=True)
+    q.decode_accumulate(wd, od, n, s, d, acc, code=q.GAMMA)
+    torch.cuda.synchronize()
+    rc, want = oracle.decode_accumulate(streams, bst, s, acc0.copy(), code=oracle.GAMMA)
+    assert rc == oracle.OK
+    assert np.array_equal(acc.cpu().numpy().view(np.uint32), want.view(np.uint32))

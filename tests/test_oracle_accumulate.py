@@ -14,15 +14,16 @@ that zeros come back as +0.0. The accumulate must then be numpy's float32
 left fold of the inputs.
 """
 import numpy as np
+import pytest
 
 import oracle
 
 
-def _streams(vectors, s, d, seed0=11):
+def _streams(vectors, s, d, seed0=11, code=oracle.OMEGA):
     bst = oracle.uniform_buckets(vectors[0].size, d)
     out = []
     for j, v in enumerate(vectors):
-        _, _, words, offs, _ = oracle.compress(v, bst, s, seed0 + j)
+        _, _, words, offs, _ = oracle.compress(v, bst, s, seed0 + j, code=code)
         out.append((words, offs))
     return bst, out
 
@@ -54,7 +55,8 @@ def test_identity_buckets_fold_in_stream_order():
     assert np.isneginf(out[10])  # -3e38 + -3e38 overflows in fp32
 
 
-def test_identity_buckets_random_fold():
+@pytest.mark.parametrize("code", [oracle.OMEGA, oracle.GAMMA])
+def test_identity_buckets_random_fold(code):
     rng = np.random.default_rng(5)
     n, k = 2000, 6
     vs = []
@@ -64,8 +66,8 @@ def test_identity_buckets_random_fold():
         vs.append(v)
     acc = (rng.standard_normal(n) * 1e3).astype(np.float32)
     acc[::7] = -0.0
-    bst, streams = _streams(vs, 1, 1)
-    rc, out = oracle.decode_accumulate(streams, bst, 1, acc)
+    bst, streams = _streams(vs, 1, 1, code=code)
+    rc, out = oracle.decode_accumulate(streams, bst, 1, acc, code=code)
     assert rc == oracle.OK
     assert np.array_equal(_bits(out), _bits(_fold(acc, vs)))
 
@@ -79,6 +81,10 @@ def test_one_stream_from_zero_is_decode_and_none_is_identity():
     rc2, ref = oracle.decode(words, offs, bst, 16)
     assert rc == rc2 == oracle.OK
     assert np.array_equal(_bits(out), _bits(ref))
+    # a gamma stream from zero decodes to the same values as the omega one
+    _, _, gw, go, _ = oracle.compress(v, bst, 16, 3, code=oracle.GAMMA)
+    rc, gout = oracle.decode_accumulate([(gw, go)], bst, 16, np.zeros(v.size, np.float32), code=oracle.GAMMA)
+    assert rc == oracle.OK and np.array_equal(_bits(gout), _bits(ref))
     acc = rng.standard_normal(v.size).astype(np.float32)
     rc, out = oracle.decode_accumulate([], bst, 16, acc)
     assert rc == oracle.OK and np.array_equal(_bits(out), _bits(acc))
