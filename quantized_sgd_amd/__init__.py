@@ -108,6 +108,13 @@ def _stream(stream=None) -> int:
     return s.cuda_stream
 
 
+def _need(t: torch.Tensor, count: int, name: str):
+    """Raises before any device work when a buffer holds fewer than `count`
+    elements (the kernels would write past it)."""
+    if t.numel() < count:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {count}")
+
+
 def _dev(t: torch.Tensor, dtype, name: str) -> int:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -142,6 +149,8 @@ def quantize(v: torch.Tensor, s: int, d: int, seed: int, levels=None, norms=None
         levels = torch.empty(n, dtype=torch.int32, device=v.device)
     if norms is None:
         norms = torch.empty(max(nb, 1), dtype=torch.float32, device=v.device)
+    _need(levels, n, "levels")
+    _need(norms, nb, "norms")
     if norm == L2:
         _check(lib().qsgd_quantize(_dev(v, torch.float32, "v"), n, s, d, seed,
                                    _dev(levels, torch.int32, "levels"),
@@ -173,6 +182,8 @@ def encode(v: torch.Tensor, s: int, d: int, seed: int, out=None, out_bits=None, 
         out_bits = torch.empty(1, dtype=torch.int64, device=v.device)
     if offsets is None:
         offsets = torch.empty(nb + 1, dtype=torch.int64, device=v.device)
+    _need(out_bits, 1, "out_bits")
+    _need(offsets, nb + 1, "offsets")
     if code == OMEGA and norm == L2:
         _check(lib().qsgd_encode(_dev(v, torch.float32, "v"), n, s, d, seed,
                                  _dev(out, torch.int64, "out"), _dev(out_bits, torch.int64, "out_bits"),
@@ -192,6 +203,8 @@ def decode(words: torch.Tensor, offsets: torch.Tensor, n: int, s: int, d: int, v
     (float32 [n])."""
     if v_hat is None:
         v_hat = torch.empty(n, dtype=torch.float32, device=words.device)
+    _need(v_hat, n, "v_hat")
+    _need(offsets, num_buckets(n, d) + 1, "offsets")
     if code == OMEGA:
         _check(lib().qsgd_decode(_dev(words, torch.int64, "words"), _dev(offsets, torch.int64, "offsets"),
                                  n, s, d, _dev(v_hat, torch.float32, "v_hat"), _stream(stream)),
@@ -222,8 +235,9 @@ def decode_accumulate(words_list, offsets_list, n: int, s: int, d: int, acc: tor
     """acc += the decodes of the streams (all of record code `code`), added in
     list order per coordinate (one fp32 rounding per addition); returns acc."""
     k, ins, offs = _pointer_arrays(words_list, offsets_list)
-    if acc.numel() < n:
-        raise ValueError(f"acc holds {acc.numel()} values, needs {n}")
+    _need(acc, n, "acc")
+    for o in offsets_list:
+        _need(o, num_buckets(n, d) + 1, "offsets")
     if code == OMEGA:
         _check(lib().qsgd_decode_accumulate(ctypes.addressof(ins), ctypes.addressof(offs), k, n, s, d,
                                             _dev(acc, torch.float32, "acc"), _stream(stream)),
@@ -262,6 +276,7 @@ class RaggedLayout:
 
 def quantize_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, stream=None,
                     norm: int = L2):
+    _need(v, layout.n, "v")
     levels = torch.empty(layout.n, dtype=torch.int32, device=v.device)
     norms = torch.empty(max(layout.nb, 1), dtype=torch.float32, device=v.device)
     bs = _dev(layout.bucket_start, torch.int64, "bucket_start")
@@ -289,6 +304,10 @@ def encode_ragged(v: torch.Tensor, layout: RaggedLayout, s: int, seed: int, out=
         out_bits = torch.empty(1, dtype=torch.int64, device=v.device)
     if offsets is None:
         offsets = torch.empty(layout.nb + 1, dtype=torch.int64, device=v.device)
+    _need(out, cap, "out")
+    _need(out_bits, 1, "out_bits")
+    _need(offsets, layout.nb + 1, "offsets")
+    _need(v, layout.n, "v")
     if code == OMEGA and norm == L2:
         _check(lib().qsgd_encode_ragged(_dev(v, torch.float32, "v"), layout.n,
                                         _dev(layout.bucket_start, torch.int64, "bucket_start"), layout.nb,
@@ -310,6 +329,8 @@ def decode_ragged(words: torch.Tensor, offsets: torch.Tensor, layout: RaggedLayo
                   v_hat=None, stream=None, code: int = OMEGA):
     if v_hat is None:
         v_hat = torch.empty(layout.n, dtype=torch.float32, device=words.device)
+    _need(v_hat, layout.n, "v_hat")
+    _need(offsets, layout.nb + 1, "offsets")
     bs = _dev(layout.bucket_start, torch.int64, "bucket_start")
     if code == OMEGA:
         _check(lib().qsgd_decode_ragged(_dev(words, torch.int64, "words"),
@@ -328,6 +349,9 @@ def decode_accumulate_ragged(words_list, offsets_list, layout: RaggedLayout, s: 
                              stream=None):
     """Ragged decode_accumulate."""
     k, ins, offs = _pointer_arrays(words_list, offsets_list)
+    _need(acc, layout.n, "acc")
+    for o in offsets_list:
+        _need(o, layout.nb + 1, "offsets")
     _check(lib().qsgd_decode_accumulate_ragged(ctypes.addressof(ins), ctypes.addressof(offs), k, layout.n,
                                                _dev(layout.bucket_start, torch.int64, "bucket_start"),
                                                layout.nb, s, layout.d, _dev(acc, torch.float32, "acc"),

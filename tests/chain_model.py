@@ -11,13 +11,29 @@ Test infrastructure: used by tests only.
 """
 from __future__ import annotations
 
+import os
+import re
+
 import numpy as np
 
-TABLE_BITS = 12
-FIELD_MAX = 16
-SYNC_BITS = 128
-GUESS_STEPS = 6
-GUESS_BITS_PER_COORD = 4
+_DECODER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "quantized_sgd_amd", "csrc", "qsgd_decode.h")
+
+
+def _decoder_constant(pattern: str) -> int:
+    """A constant of the decoder's source, so that the model follows it."""
+    with open(_DECODER) as f:
+        m = re.search(pattern, f.read())
+    if m is None:
+        raise RuntimeError(f"decoder constant not found: {pattern}")
+    return int(m.group(1))
+
+
+TABLE_BITS = _decoder_constant(r"constexpr int kLutBits = (\d+);")
+FIELD_MAX = 16  # the table's largest gap and level: four bits each in an entry
+SYNC_BITS = _decoder_constant(r"constexpr int kSyncWin = (\d+);")
+GUESS_STEPS = _decoder_constant(r"#define QSGD_GUESS_STEPS (\d+)")
+GUESS_BITS_PER_COORD = _decoder_constant(r"constexpr uint32_t kGuessBits = (\d+);")
 
 
 def stream_bits(words) -> list:

@@ -133,3 +133,22 @@ def test_product_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "qsgd_oracle" not in text, f
+
+
+def test_binding_refuses_short_buffers_before_any_device_work():
+    # the wrappers compare buffer sizes with what the call writes; a CPU tensor
+    # is enough to see the refusal, which comes before the device check
+    import torch
+    v = torch.zeros(1000)
+    with pytest.raises(ValueError):
+        q.quantize(v, 4, 100, 1, levels=torch.zeros(999, dtype=torch.int32), norms=torch.zeros(10))
+    with pytest.raises(ValueError):
+        q.quantize(v, 4, 100, 1, levels=torch.zeros(1000, dtype=torch.int32), norms=torch.zeros(9))
+    with pytest.raises(ValueError):
+        q.encode(v, 4, 100, 1, offsets=torch.zeros(10, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        q.decode(torch.zeros(4, dtype=torch.int64), torch.zeros(11, dtype=torch.int64), 1000, 4, 100,
+                 v_hat=torch.zeros(999))
+    with pytest.raises(ValueError):
+        q.decode(torch.zeros(4, dtype=torch.int64), torch.zeros(10, dtype=torch.int64), 1000, 4, 100,
+                 v_hat=torch.zeros(1000))
