@@ -1,15 +1,20 @@
 """Benchmark of the QSGD compressor hot path on one MI355X.
 
 A step is one encode (quantize + Elias-omega stream, one pass over v) and one
-decode (parse + dequantize) of the ResNet-152-sized synthetic gradient
-(n = 60,192,808 fp32, buckets d = 4096, s = 64), inputs resident in HBM.
-Several copies of the input and output buffers are rotated so that no step
-finds its input in the 256 MB Infinity Cache.
+decode (parse + dequantize) of a synthetic gradient shaped like the pages'
+workloads; by default the ResNet-152-sized one (n = 60,192,808 fp32, buckets
+d = 4096, s = 64), --config 1..5 picks another. Inputs are resident in HBM.
+Several copies of the input and output buffers are rotated, and a 512 MiB
+buffer is overwritten before each timed call (outside the timed region), so
+that no call finds its input in the 256 MB Infinity Cache -- decode included,
+which would otherwise read the stream the encode has just written.
 
 Prints one JSON line: value = whole-job round-trip throughput 4n bytes of fp32
-gradient / (encode + decode time) in GB/s, plus per-direction rates and HBM
-fractions, bits per coordinate, the roofline object of the dominant kernel and
-the oracle's CPU rate on a bounded sample.
+gradient / (encode + decode time) in GB/s, plus per-direction rates (median,
+p10, p90) and HBM fractions, bits per coordinate, the roofline object of the
+dominant single kernel (the decode call is one kernel launch) with its
+counter-measured HBM traffic and VALU-issue fraction where the committed
+counters match the sources, and the oracle's rate on one pinned host core.
 """
 from __future__ import annotations
 
@@ -21,7 +26,11 @@ import time
 
 HBM_PEAK_GBPS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c3.json")
+VALU_PEAK_GIPS = 256 * 4 * 2.4e9 / 4 / 1e9  # wave64 VALU instructions per s: 614.4 G
+
+
+def traffic_file(config: int) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_c{config}.json")
 
 
 def kernel_source_hash() -> str:
@@ -36,18 +45,36 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None if it is missing or was taken on other kernel sources."""
+def measured_counters(config: int, kernel: str):
+    """The committed counter record of `kernel` on this config (HBM bytes and
+    VALU instructions per launch), or {} if it is missing or was taken on other
+    kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(config)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     if rec.get("source_hash") != kernel_source_hash():
-        return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+        return {}
+    return rec.get("kernels", {}).get(kernel, {})
+
+
+def cpu_identity():
+    """Host CPU model and core counts (the CPU baseline's context)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count()
+    return {"cpu_model": model, "nproc": avail, "cpu_count": os.cpu_count()}
 
 
 def copy_calibration(mbytes: int, reps: int):
@@ -66,10 +93,18 @@ def copy_calibration(mbytes: int, reps: int):
 def cpu_baseline(w, max_coords: int, reps: int = 3):
     """The oracle (single-threaded C, as it stands) on the first whole buckets
     of the workload (all of it by default): quantize + encode + decode, median of
-    `reps` runs."""
+    `reps` runs, with this process pinned to one host core (the first it may
+    use) for the duration."""
     import numpy as np
 
     import oracle
+    ident = cpu_identity()
+    try:
+        prev = os.sched_getaffinity(0)
+        core = min(prev)
+        os.sched_setaffinity(0, {core})
+    except (AttributeError, OSError):
+        prev, core = None, None
     if w.seg_len is not None:  # ragged batch: the whole batch
         m = w.n
         bst = oracle.ragged_buckets(w.seg_len, w.d)
@@ -85,10 +120,13 @@ def cpu_baseline(w, max_coords: int, reps: int = 3):
         rc, vh = oracle.decode(words, offs, bst, w.s)
         times.append(time.perf_counter() - t0)
         assert rc == oracle.OK
+    if prev is not None:
+        os.sched_setaffinity(0, prev)
     t = sorted(times)[len(times) // 2]
     return {"value": round(4.0 * m / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{m} coordinates ({len(bst) - 1} buckets) of the same gradient; "
-                      f"quantize+encode+decode, median of {reps} runs, {t:.2f} s each"}
+                      f"quantize+encode+decode, median of {reps} runs, {t:.2f} s each",
+            "pinned_core": core, **ident}
 
 
 def variant_leg(q, torch, args, v, lay, n, s, d, seed, nb, stream, nbits_omega, code, norm):
@@ -190,6 +228,8 @@ def main():
                     help="skip the Elias-gamma and max-norm legs")
     ap.add_argument("--acc-streams", type=int, default=4,
                     help="streams of the decode-accumulate measurement (configs 2, 3; 0: skip)")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="MiB overwritten before each timed call, outside the timed region (0: none)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -235,28 +275,39 @@ def main():
         else:
             q.decode(outs[r], offs[r], n, s, d, v_hat=vhs[r])
 
+    flush_buf = torch.empty(max(1, args.flush_mb) * (1 << 20) // 4, dtype=torch.float32, device=dev) \
+        if args.flush_mb else None
+
+    def flush():
+        # overwrite a buffer larger than the Infinity Cache (outside the timed region)
+        if flush_buf is not None:
+            flush_buf.fill_(0.0)
+
     for i in range(args.warmup):
         enc(i % R)
         dec(i % R)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         r = i % R
+        flush()
         ev[i][0].record(stream)
         enc(r)
         ev[i][1].record(stream)
-        dec(r)
+        flush()
         ev[i][2].record(stream)
+        dec(r)
+        ev[i][3].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     enc_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
-    med = lambda a: a[len(a) // 2]
+    dec_ms = sorted(e[2].elapsed_time(e[3]) for e in ev)
+    pct = lambda a, f: a[min(len(a) - 1, int(round(f * (len(a) - 1))))]
     enc_avg = sum(enc_ms) / K
     dec_avg = sum(dec_ms) / K
     ms_per_step = (t1 - t0) * 1e3 / K
@@ -269,8 +320,20 @@ def main():
     dec_bytes = nbits / 8.0 + side + 4.0 * n
     enc_gbps = enc_bytes / (enc_avg * 1e-3) / 1e9
     dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
-    dominant = "encode" if enc_avg >= dec_avg else "decode"
-    ach = enc_gbps if dominant == "encode" else dec_gbps
+
+    def roofline(kind, t_ms, alg_bytes):
+        c = measured_counters(args.config, kind)
+        ach = alg_bytes / (t_ms * 1e-3) / 1e9
+        out = {"bound": "hbm", "kernel": c.get("kernel_names", [kind]), "achieved": round(ach, 2),
+               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+               "traffic": c.get("hbm_bytes_per_launch"), "algorithmic_bytes": round(alg_bytes),
+               "launch_ms_avg": round(t_ms, 4)}
+        valu = c.get("valu_insts_per_launch")
+        if valu is not None:
+            out["valu"] = {"insts_per_launch": valu, "peak_ginsts_per_s": VALU_PEAK_GIPS,
+                           "frac": round(valu / (t_ms * 1e-3) / (VALU_PEAK_GIPS * 1e9), 4)}
+        return out
+
     res = {
         "metric": "QSGD encode/decode GB/s of fp32 gradient on 1 MI355X; % HBM peak; bits/coord",
         "value": round(gbytes / ((enc_avg + dec_avg) * 1e-3), 3),
@@ -285,9 +348,11 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "n": n, "d": d, "s": s, "buckets": nb,
-                   "input_copies_rotated": R},
-        "encode_ms_median": round(med(enc_ms), 4),
-        "decode_ms_median": round(med(dec_ms), 4),
+                   "input_copies_rotated": R, "flush_mb_between_calls": args.flush_mb},
+        "encode_ms": {"median": round(pct(enc_ms, 0.5), 4), "p10": round(pct(enc_ms, 0.1), 4),
+                      "p90": round(pct(enc_ms, 0.9), 4), "avg": round(enc_avg, 4)},
+        "decode_ms": {"median": round(pct(dec_ms, 0.5), 4), "p10": round(pct(dec_ms, 0.1), 4),
+                      "p90": round(pct(dec_ms, 0.9), 4), "avg": round(dec_avg, 4)},
         "encode_GBps_fp32": round(gbytes / (enc_avg * 1e-3), 2),
         "decode_GBps_fp32": round(gbytes / (dec_avg * 1e-3), 2),
         "encode_hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
@@ -295,10 +360,10 @@ def main():
         "bits_per_coord": round(nbits / n, 4),
         "compression_vs_fp32": round(32.0 * n / nbits, 3),
         "compression_vs_fp32_with_offsets": round(32.0 * n / (nbits + 64.0 * (nb + 1)), 3),
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 2),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(dominant),
-                     "algorithmic_bytes": round(enc_bytes if dominant == "encode" else dec_bytes)},
+        # the decode call is a single kernel launch; the encode call is two
+        # (pass 1 and the pass-2 gather) and is reported beside it
+        "roofline": roofline("decode", dec_avg, dec_bytes),
+        "encode_call_roofline": roofline("encode", enc_avg, enc_bytes),
     }
     if not args.no_variants:
         res["gamma"] = variant_leg(q, torch, args, vs[0], lay, n, s, d, seed, nb, stream, nbits,
