@@ -473,6 +473,9 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
     D.team = team;
     D.tpw = tpw;
     D.lds_out = lds_out ? 1u : 0u;
+    // units of 64 sparse buckets a lane each (plain decodes of groups of 8 or
+    // more buckets)
+    D.solo = (!acc && lds_out && tpw >= 8 && kSoloBuckets % tpw == 0) ? 1u : 0u;
     const uint64_t groups = (nb + tpw - 1) / tpw;
     const uint64_t want = (groups + kDecWaves - 1) / kDecWaves;
     const size_t lds = decode_lds_bytes();

@@ -54,6 +54,14 @@ constexpr int kStageWords = 320;    // 64-bit stream words staged per wave
 constexpr int kStagePad = 4;        // zero words after the staged stream
 constexpr int kGroupCoords = 4096;  // coordinates of a group whose levels are staged in LDS
 constexpr uint32_t kLevelSpare = kGroupCoords + 16;  // level byte for out-of-range writes
+// Sparse streams: a unit of kSoloBuckets consecutive buckets whose stream fits
+// the stage and whose payloads are at most kSoloMaxBits bits each is decoded by
+// one wave, a lane per bucket (decode_kernel).
+constexpr uint32_t kSoloBuckets = 64;
+constexpr uint32_t kSoloMaxBits = 1024;
+// Streams of more bits per bucket on average (a unit of them would not fit the
+// stage) skip the per-group test for such units altogether.
+constexpr uint32_t kSoloAvgBits = (uint32_t)kStageWords * 64u / kSoloBuckets;
 
 // Streams that one decode-accumulate call sums.
 constexpr uint32_t kMaxStreams = 32;
@@ -73,6 +81,7 @@ struct DecodeParams {
     uint32_t tpw;            // buckets per wave group (tpw * team <= 64)
     uint32_t lds_out;        // 1: levels staged in LDS (s <= 127, tpw * d <= kGroupCoords)
     uint32_t s_pow2;         // s is a power of two (norm / s exact)
+    uint32_t solo;           // 1: units of sparse buckets are decoded a lane per bucket (decode_kernel)
     double inv_s;            // 1 / s (exact when s_pow2)
     SegTable seg;            // ragged layout by tensor lengths (nseg > 0) instead of bstart
 };
@@ -994,6 +1003,85 @@ static_assert(2 * ((size_t)kDecWaves * kWaveLdsBytes + 16384) <= 160 * 1024, "de
 
 constexpr size_t decode_lds_bytes() { return (size_t)kDecWaves * kWaveLdsBytes + sizeof(RecordLut); }
 
+// Whether the unit of buckets [ub0, ub1) of stream `offs` is decoded a lane per
+// bucket: its stream words fit the stage and every bucket's bit length is at
+// most kSoloMaxBits (which also makes its offsets non-decreasing). Uniform.
+__device__ __forceinline__ bool solo_unit_ok(const uint64_t *offs, uint64_t ub0, uint64_t ub1,
+                                             uint64_t total_words) {
+    const uint64_t A0 = offs[ub0], E1 = offs[ub1];
+    if (E1 < A0) return false;
+    const uint64_t w0 = A0 >> 6;
+    uint64_t w1 = (E1 + 63) >> 6;
+    if (w1 > total_words) w1 = total_words;
+    if (w1 > w0 && w1 - w0 > (uint64_t)kStageWords) return false;
+    const uint64_t b = ub0 + (uint64_t)lane_id();
+    bool bad = false;
+    if (b < ub1) {
+        const uint64_t A = offs[b], E = offs[b + 1];
+        bad = E < A || E - A > (uint64_t)kSoloMaxBits;
+    }
+    return __ballot(bad) == 0;
+}
+
+// Decodes the unit [ub0, ub1) (solo_unit_ok) of a plain decode: its stream
+// words to the stage; +0.0f to all of its outputs with 16-byte stores where
+// whole aligned quads allow; then, once those stores are done, lane i follows
+// bucket ub0 + i from its first record and writes each record's value
+// RN32(norm k / s) with its sign at its coordinate.
+template <bool RAGGED, int CODE>
+__device__ __forceinline__ void solo_unit(const DecodeParams &D, const uint64_t *in, const uint64_t *offs,
+                                          const uint32_t *lut, uint64_t *stage, uint64_t ub0,
+                                          uint64_t ub1, uint64_t total_words) {
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint64_t w0 = offs[ub0] >> 6;
+    uint64_t w1 = (offs[ub1] + 63) >> 6;
+    if (w1 > total_words) w1 = total_words;
+    const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
+    for (uint64_t i = lane; i < nw + kStagePad; i += 64)
+        stage[i] = i < nw ? __builtin_bitreverse64(in[w0 + i]) : 0ull;
+    // zeros over the unit's coordinates [C0, C1)
+    const uint64_t C0 = bucket_first<RAGGED>(D, ub0), C1 = bucket_first<RAGGED>(D, ub1);
+    const uint64_t qa = (C0 + 3) >> 2, qb = C1 >> 2;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (qa < qb) {
+        for (uint64_t qd = qa + lane; qd < qb; qd += 64) *reinterpret_cast<float4 *>(D.v_hat + (qd << 2)) = z;
+        if (lane < (uint32_t)((qa << 2) - C0)) D.v_hat[C0 + lane] = 0.0f;
+        if (lane < (uint32_t)(C1 - (qb << 2))) D.v_hat[(qb << 2) + lane] = 0.0f;
+    } else if (C0 + lane < C1) {
+        D.v_hat[C0 + lane] = 0.0f;
+    }
+    // the zeros are written before this wave writes any value over them
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    wave_sync();
+    const Bits<true> r{nullptr, 0u};
+    const uint64_t gbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
+    const uint64_t b = ub0 + lane;
+    if (b < ub1) {
+        const uint32_t A = (uint32_t)(offs[b] - gbit), E = (uint32_t)(offs[b + 1] - gbit);
+        const uint64_t c0 = bucket_first<RAGGED>(D, b);
+        const uint64_t len = bucket_first<RAGGED>(D, b + 1) - c0;
+        if (E >= A + 32u && len > 0) {
+            const double e_b = (double)__uint_as_float(__builtin_bitreverse32((uint32_t)r.at(A)));
+            const RecordCtx<CODE> x{lut, bitlen32((uint32_t)len), bitlen32(D.s), D.s};
+            uint32_t p = A + 32u;
+            uint64_t jj = ~0ull;
+            Win W = win_at(r, p);
+            while (p < E) {
+                uint32_t gap, neg, k;
+                const uint32_t nq = record_at(r, x, p, gap, neg, k, W);
+                if (!nq) break;
+                jj += gap;
+                if (jj >= len) break;
+                const float m = dequant_value(e_b, k, D.s, D.s_pow2 != 0u, D.inv_s);
+                D.v_hat[c0 + jj] = neg ? -m : m;
+                p = nq;
+            }
+        }
+    }
+    // the stage is reused by this wave's next unit or group
+    wave_sync();
+}
+
 // LDS_OUT: levels staged in LDS (D.lds_out), else each lane writes its range.
 // ACC: the output accumulates the D.nstreams streams in order, per coordinate
 // out = ((out + v_hat_0) + v_hat_1) + ...; the wave takes all streams of a
@@ -1022,9 +1110,31 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     double *ebs = reinterpret_cast<double *>(wbase + kStageBytes + kLevelBytes);
     const uint32_t tpw = D.tpw;
     const uint64_t ngroups = (D.nb + tpw - 1) / tpw;
+    // with D.solo, and a stream of at most kSoloAvgBits bits per bucket on
+    // average, groups are taken unit by unit transposed (the first group of
+    // every unit, then the second ...), so that the units decoded a lane per
+    // bucket spread over the waves; the other groups of such a unit are skipped
+    const bool solo = !ACC && LDS_OUT && D.solo != 0u &&
+                      D.offsets[0][D.nb] <= D.nb * (uint64_t)kSoloAvgBits;
+    const uint64_t gpu = solo ? kSoloBuckets / tpw : 1u;  // groups per unit
+    const uint64_t nunits = (ngroups + gpu - 1) / gpu;
 
-    for (uint64_t g = (uint64_t)blockIdx.x * kDecWaves + (uint64_t)wv; g < ngroups;
-         g += (uint64_t)gridDim.x * kDecWaves) {
+    for (uint64_t t = (uint64_t)blockIdx.x * kDecWaves + (uint64_t)wv; t < nunits * gpu;
+         t += (uint64_t)gridDim.x * kDecWaves) {
+        uint64_t g = t;
+        if (solo) {
+            const uint64_t u = t % nunits, j = t / nunits;
+            g = u * gpu + j;
+            if (g >= ngroups) continue;
+            const uint64_t ub0 = u * kSoloBuckets;
+            const uint64_t ub1 = ub0 + kSoloBuckets < D.nb ? ub0 + kSoloBuckets : D.nb;
+            const uint64_t *offs = D.offsets[0];
+            const uint64_t total_words = (offs[D.nb] + 63) >> 6;
+            if (solo_unit_ok(offs, ub0, ub1, total_words)) {
+                if (j == 0) solo_unit<RAGGED, CODE>(D, D.in[0], offs, lut, stage, ub0, ub1, total_words);
+                continue;
+            }
+        }
         const uint64_t b0 = g * tpw;
         const uint64_t b1 = b0 + tpw < D.nb ? b0 + tpw : D.nb;
         const uint64_t lbase = bucket_first<RAGGED>(D, b0) & ~(uint64_t)3;
