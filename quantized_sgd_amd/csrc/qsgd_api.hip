@@ -407,6 +407,11 @@ qsgd_status decode_chunked(const uint64_t *const *in, const uint64_t *const *off
     const size_t lds = decode_lds_bytes();
     const uint32_t grid = (uint32_t)((slots + kDecWaves - 1) / kDecWaves);
     const uint32_t fgrid = (uint32_t)((nb + kDecWaves - 1) / kDecWaves);
+    if (!acc) {
+        // the chunk writers write only the records' values
+        const uint64_t zb = std::min<uint64_t>((n / 4 + kWG - 1) / kWG + 1, 8192);
+        hipLaunchKernelGGL(zero_fill_kernel, dim3((uint32_t)zb), dim3(kWG), 0, stream, v_hat, n);
+    }
     for (uint32_t k = 0; k < nstreams; ++k) {
         C.in = in[k];
         C.offs = offsets[k];

@@ -717,7 +717,8 @@ struct ChunkOut {
 // MODE 0: the buckets [b0, b1) of a wave group. MODE 1: parse a chunk of a long
 // bucket with one team (no output; lane 0 may start on a guess). MODE 2: decode
 // a piece [P0, E) of a long bucket that starts on an exact record boundary,
-// with one team, into [c0, c0 + len) (lane writers).
+// with one team, into [c0, c0 + len) (lane writers). MODE 3: as MODE 2 into an
+// output already zeroed, writing only the records' values.
 template <bool RAGGED, bool LDS_IN, bool LDS_OUT, bool ACC, int CODE, bool CUM, int MODE = 0>
 __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64_t *offs,
                                              const uint32_t *lut,
@@ -915,6 +916,24 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
         if (lo > len) lo = len;
         if (hi > len) hi = len;
         if (hi < lo) hi = lo;
+        if (MODE == 3) {
+            if (act) {
+                uint32_t p = ystart;
+                uint64_t jj = (uint64_t)basej - 1u;
+                Win W = win_at(r, p);
+                while (p < ynext) {
+                    uint32_t gap, neg, k;
+                    const uint32_t nq = record_at(r, x, p, gap, neg, k, W);
+                    if (!nq) break;
+                    jj += gap;
+                    if (jj >= hi) break;
+                    const float m = dequant_value(e_b, k, D.s, D.s_pow2 != 0u, D.inv_s);
+                    D.v_hat[c0 + jj] = neg ? -m : m;
+                    p = nq;
+                }
+            }
+            return;
+        }
         QuadWriter<ACC> w;
         w.init(D.v_hat, c0 + lo, c0 + hi);
         if (act) {
@@ -1225,13 +1244,21 @@ struct ChunkParams {
     uint32_t nch;             // chunk slots per bucket
 };
 
-// The payload bit range and chunk count of bucket b.
+// The payload bit range and chunk count of bucket b (chunk_end).
 __device__ __forceinline__ void chunk_bucket(const ChunkParams &C, uint64_t b, uint64_t &A, uint64_t &E,
                                              uint64_t &nbits, uint32_t &nact) {
     A = C.offs[b];
     E = C.offs[b + 1];
     nbits = E >= A + 32 ? E - A - 32 : 0;
-    nact = (uint32_t)((nbits + kChunkBits - 1) / kChunkBits);
+    nact = nbits <= kChunkBits ? (nbits ? 1u : 0u) : (uint32_t)(nbits / kChunkBits);
+}
+
+// End of chunk c of nact starting at payload bit P: whole chunks of kChunkBits
+// bits, the last one taking the rest (fewer than 2 kChunkBits bits), so that a
+// chain started on a guess in it has at least kChunkBits bits to meet the exact
+// one before the bucket ends.
+__device__ __forceinline__ uint64_t chunk_end(uint64_t P, uint32_t c, uint32_t nact, uint64_t E) {
+    return c + 1 >= nact ? E : P + (uint64_t)(c + 1) * kChunkBits;
 }
 
 // Lanes and segment length of a team parse of [P0, E) (as decode_group sets them).
@@ -1254,7 +1281,7 @@ __device__ __forceinline__ void chunk_stage(uint64_t *stage, const uint64_t *in,
 }
 
 constexpr uint64_t kChunkStageWords = (uint64_t)kBigStageWords;
-static_assert((kChunkBits + kChunkMerge + 256) / 64 + 2 <= kChunkStageWords, "chunk stage");
+static_assert((2 * kChunkBits + kChunkMerge + 256) / 64 + 2 <= kChunkStageWords, "chunk stage");
 
 template <int CODE>
 __global__ __launch_bounds__(kDecWG) void chunk_parse_kernel(ChunkParams C) {
@@ -1284,7 +1311,7 @@ __global__ __launch_bounds__(kDecWG) void chunk_parse_kernel(ChunkParams C) {
     const uint64_t total_words = (C.offs[C.D.nb] + 63) >> 6;
     // stage from the word holding the chunk's first bit through the merge window
     const uint64_t cs = A + 32 + (uint64_t)c * kChunkBits;
-    const uint64_t ce = cs + kChunkBits < E ? cs + kChunkBits : E;
+    const uint64_t ce = chunk_end(A + 32, c, nact, E);
     const uint64_t w0 = cs >> 6;
     const uint64_t wl = (ce + kChunkMerge + 256 + 63) >> 6;
     chunk_stage(stage, C.in, w0, wl - w0, total_words);
@@ -1306,7 +1333,7 @@ __global__ __launch_bounds__(kDecWG) void chunk_parse_kernel(ChunkParams C) {
             // the next chunk's lane 0 starts at ce with the same guess steps
             uint32_t pa = co.X, pb = Er, ga = 0, gb = 0;
             Win Wa = win_at(rl, pa), Wb = win_at(rl, pb);
-            const uint64_t ce2 = ce + kChunkBits < E ? ce + kChunkBits : E;
+            const uint64_t ce2 = chunk_end(A + 32, c + 1, nact, E);
             if (guess) guess_steps(rl, x, pb, chunk_lane0_end(Er, (uint32_t)(ce2 - lgbit)), gb, Wb);
             const uint32_t lim = Er + kChunkMerge;
             while (pa != pb && pa <= lim && pb <= lim && pa <= Eb && pb <= Eb) {
@@ -1335,7 +1362,9 @@ __global__ __launch_bounds__(kWG) void chunk_scan_kernel(ChunkParams C) {
     chunk_bucket(C, b, A, E, nbits, nact);
     const uint64_t c0 = b * C.D.d;
     const uint64_t blen = (c0 + C.D.d < C.D.n ? c0 + C.D.d : C.D.n) - c0;
-    if (j == 0) bad = (nact > C.nch || E - A >= (1ull << 31)) ? 1u : 0u;
+    // a bucket without payload (or shorter than its norm) is written by the
+    // fallback, which writes its zeros (accumulates them: -0.0f + +0.0f)
+    if (j == 0) bad = (nact == 0 || nact > C.nch || E - A >= (1ull << 31)) ? 1u : 0u;
     __syncthreads();
     const uint32_t na = bad ? 0u : nact;
     // thread j takes chunks [j * per, (j + 1) * per)
@@ -1424,8 +1453,19 @@ __global__ __launch_bounds__(kDecWG) void chunk_write_kernel(ChunkParams C) {
     const uint64_t lgbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
     GroupView gv{(uint32_t)(vs - lgbit), (uint32_t)(ve - lgbit), c0 + base, vend - base, blen,
                  (double)chunk_norm(C.in, A), guess, false};
-    decode_group<false, true, false, ACC, CODE, false, 2>(C.D, nullptr, lut, rl, lgbit, 0, 0, nullptr,
-                                                          nullptr, 0, 0, &gv, nullptr);
+    // a plain decode's output was zeroed first (zero_fill_kernel): only values are written
+    decode_group<false, true, false, ACC, CODE, false, ACC ? 2 : 3>(C.D, nullptr, lut, rl, lgbit, 0, 0,
+                                                                    nullptr, nullptr, 0, 0, &gv, nullptr);
+}
+
+// +0.0f to p[0, n) (p 16-byte aligned), 16-byte stores.
+__global__ __launch_bounds__(kWG) void zero_fill_kernel(float *p, uint64_t n) {
+    const uint64_t nq = n >> 2;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    const uint64_t stride = (uint64_t)gridDim.x * kWG;
+    for (uint64_t i = (uint64_t)blockIdx.x * kWG + threadIdx.x; i < nq; i += stride)
+        reinterpret_cast<float4 *>(p)[i] = z;
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3u)) p[(nq << 2) + threadIdx.x] = 0.0f;
 }
 
 // One wave per bucket: a failed bucket decoded whole by one team, reading the

@@ -8,7 +8,12 @@ ResNet-152-sized gradient as one bucket); streams on which chunk chains never
 meet, decoded by the whole-bucket fallback (constant vectors with
 s = sqrt(n), where every record is the same 3 bits, so chains started a
 multiple of 3 bits apart never meet); a mix of such buckets with Gaussian
-ones; the gamma code; and decode-accumulate over long buckets."""
+ones; the gamma code; decode-accumulate over long buckets; payloads a few bits
+longer than a multiple of the chunk (the last chunk takes the rest, so that a
+chain started in it has a whole chunk to meet the exact one); buckets without
+records among long ones (written, and accumulated, as zeros); and very sparse
+whole vectors, whose outputs are zeroed first and then get the records'
+values."""
 import numpy as np
 import pytest
 import torch
@@ -87,3 +92,55 @@ def test_chunked_decode_accumulate():
     rc, want = oracle.decode_accumulate(streams, bst, s, acc0.copy())
     assert rc == oracle.OK
     assert np.array_equal(acc.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("s,seed,n", [(64, 11, 61620), (16, 12, 61970)])
+def test_payload_just_past_whole_chunks(s, seed, n):
+    v = wl.small_gaussian(120000, seed)[:n]
+    bst = oracle.uniform_buckets(n, n)
+    _, _, _, _, nbits = oracle.compress(v, bst, s, seed)
+    payload = nbits - 32
+    assert payload > 16384 and 0 < payload % 16384 < 8
+    print(f"whole vector n={n} s={s}: payload {payload} bits", flush=True)
+    check_parity(v, s, n, seed)
+
+
+def test_long_buckets_without_records():
+    # a zero bucket (norm 0: its stream is the 32-bit norm alone) between long
+    # Gaussian buckets, decoded into a buffer of sentinels, and accumulated
+    # into -0.0f accumulators there
+    d, s = 20000, 64
+    rng = np.random.default_rng(31)
+    v = np.concatenate([rng.standard_normal(d), np.zeros(d), rng.standard_normal(d + 5)]).astype(np.float32)
+    n = v.size
+    bst = oracle.uniform_buckets(n, d)
+    lev, nrm = oracle.quantize(v, bst, s, 32)
+    words, offs, _ = oracle.encode(lev, nrm, bst, s)
+    assert offs[2] - offs[1] == 32
+    want = oracle.dequantize(lev, nrm, bst, s)
+    wd, od = to_dev(words.view(np.int64)), to_dev(offs.view(np.int64))
+    print("long buckets without records", flush=True)
+    vh = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    q.decode(wd, od, n, s, d, v_hat=vh)
+    torch.cuda.synchronize()
+    assert np.array_equal(vh.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    acc0 = rng.standard_normal(n).astype(np.float32)
+    acc0[d:2 * d] = -0.0
+    acc = to_dev(acc0.copy())
+    q.decode_accumulate([wd], [od], n, s, d, acc)
+    torch.cuda.synchronize()
+    rc, exp = oracle.decode_accumulate([(words, offs)], bst, s, acc0.copy())
+    assert rc == oracle.OK
+    got = acc.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), exp.view(np.uint32))
+    assert np.all(got[d:2 * d].view(np.uint32) == 0)     # -0.0 + +0.0 = +0.0
+
+
+@pytest.mark.parametrize("n,s", [(1_000_000, 1), (3_000_000, 2)])
+def test_very_sparse_whole_vectors(n, s):
+    # few records with gaps of thousands of coordinates: the output is zeroed by
+    # a parallel fill and the chunk writers store only the records' values
+    v = wl.small_gaussian(n, 41 + s)
+    print(f"sparse whole vector n={n} s={s}", flush=True)
+    g, _ = check_parity(v, s, n, 42)
+    assert g["bits"] < n // 50
