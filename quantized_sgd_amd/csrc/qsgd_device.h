@@ -64,9 +64,10 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
 //    below 2^-126, where the decision u < p is the same for both;
 //  - a midpoint of the normal range (25-bit odd mu): the odd parts of s, |v| and
 //    norm then satisfy sigma alpha' = mu nu' with alpha' < 2^24 < mu, so the odd
-//    part of norm's significand is below the odd part sigma of s. A bucket where
-//    that can happen (never for s a power of two) takes the exact form: the
-//    fp64 quotient of the exact product s |v| and norm, rounded to fp32.
+//    part of norm's significand is below the odd part sigma of s. In a bucket
+//    where that can happen (never for s a power of two) |v| c may fall just below
+//    q = M and round to the neighbour below, where the correct rounding takes the
+//    even one of the two; ratio_tiefix tests for exactly that case.
 __device__ __forceinline__ double ratio_scale(float norm, uint32_t s) {
     if (norm == 0.0f) return 0.0;
     const double q = (double)s / (double)norm;                 // RN64
@@ -88,9 +89,24 @@ __device__ __forceinline__ bool ratio_may_tie(float norm, uint32_t sigma) {
 // The fast form of the signed ratio: sign of v, magnitude RN32(|v| c).
 __device__ __forceinline__ float ratio_fast(float v, double c) { return (float)((double)v * c); }
 
-// The exact form: the fp64 quotient of s v (exact) and norm, rounded to fp32.
-__device__ __forceinline__ float ratio_exact(float v, float norm, uint32_t s) {
-    return norm == 0.0f ? 0.0f * v : (float)(((double)s * (double)v) / (double)norm);
+// The fast form r = ratio_fast(v, c) corrected at exact midpoints (a bucket
+// where ratio_may_tie): with a = |r| and a+ the next binary32 value above it,
+// q = s |v| / norm is the midpoint M = (a + a+) / 2 exactly when s |v| = M norm,
+// a comparison of two exact fp64 products (48 and 49 significant bits); then
+// the correct rounding is the one of a, a+ with an even significand.
+__device__ __forceinline__ float ratio_tiefix(float v, float r, float norm, uint32_t s) {
+    const float a = fabsf(r);
+    const float up = __uint_as_float(__float_as_uint(a) + 1u);
+    const double M = ((double)a + (double)up) * 0.5;  // exact
+    const bool tie = (double)s * (double)fabsf(v) == M * (double)norm;
+    const float m = (tie && (__float_as_uint(a) & 1u)) ? up : a;
+    return __builtin_copysignf(m, v);
+}
+
+// The signed ratio of a coordinate: c = ratio_scale, tie = ratio_may_tie.
+__device__ __forceinline__ float ratio_of(float v, double c, bool tie, float norm, uint32_t s) {
+    const float r = ratio_fast(v, c);
+    return tie ? ratio_tiefix(v, r, norm, s) : r;
 }
 
 // Level k from the signed ratio r of a coordinate: l = floor(|r|),
@@ -105,10 +121,10 @@ __device__ __forceinline__ uint32_t level_of_ratio(float r, uint32_t w) {
     return l + (u < p ? 1u : 0u);
 }
 
-// Level of one coordinate of a bucket (c = ratio_scale, exact = ratio_may_tie).
-__device__ __forceinline__ uint32_t qlevel(float v, double c, bool exact, float norm, uint32_t s,
+// Level of one coordinate of a bucket (c = ratio_scale, tie = ratio_may_tie).
+__device__ __forceinline__ uint32_t qlevel(float v, double c, bool tie, float norm, uint32_t s,
                                            uint32_t w) {
-    return level_of_ratio(exact ? ratio_exact(v, norm, s) : ratio_fast(v, c), w);
+    return level_of_ratio(ratio_of(v, c, tie, norm, s), w);
 }
 
 // Odd part of s.

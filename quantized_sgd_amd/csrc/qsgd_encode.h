@@ -429,20 +429,6 @@ __device__ __forceinline__ float aligned_norm(const float (&x)[kCPT], uint32_t G
     return MAXN ? (float)acc : (float)sqrt(acc);
 }
 
-// The signed ratios r_q = RN32(s x_q / norm) of a thread's coordinates (all in
-// one bucket): the fast form, or, where the bucket's norm admits exact fp32
-// midpoints (ratio_may_tie), the exact one for the whole thread.
-__device__ __forceinline__ void signed_ratios(const float (&x)[kCPT], float norm, uint32_t s,
-                                              uint32_t sigma, float (&rr)[kCPT]) {
-    const double cb = ratio_scale(norm, s);
-#pragma unroll
-    for (int q = 0; q < kCPT; ++q) rr[q] = ratio_fast(x[q], cb);
-    if (ratio_may_tie(norm, sigma)) {
-#pragma unroll
-        for (int q = 0; q < kCPT; ++q) rr[q] = ratio_exact(x[q], norm, s);
-    }
-}
-
 // Quantize, aligned fast path (the encode fast path's front half): one
 // workgroup per 4096-coordinate tile; writes sgn * k and the bucket norms.
 __global__ __launch_bounds__(kWG) void quantize_aligned_kernel(QsgdParams P, uint32_t log2d) {
@@ -455,8 +441,9 @@ __global__ __launch_bounds__(kWG) void quantize_aligned_kernel(QsgdParams P, uin
     aligned_load(P, g0, x);
     const float norm = P.maxnorm ? aligned_norm<true>(x, G, sh_red) : aligned_norm<false>(x, G, sh_red);
     if ((j & (G - 1)) == 0 && g0 < P.n) P.norms[g0 >> log2d] = norm;
-    float rr[kCPT];
-    signed_ratios(x, norm, P.s, P.sigma, rr);
+    // ratios (ratio_of) per block of four, just before their levels
+    const double cb = ratio_scale(norm, P.s);
+    const bool tie = ratio_may_tie(norm, P.sigma);
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
     int32_t lv[kCPT];
 #pragma unroll
@@ -464,11 +451,18 @@ __global__ __launch_bounds__(kWG) void quantize_aligned_kernel(QsgdParams P, uin
         uint32_t w[4];
         const uint64_t blk = (g0 >> 2) + (uint64_t)g;
         philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), key0, key1, w);
+        float rq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rq[e] = ratio_fast(x[4 * g + e], cb);
+        if (tie) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rq[e] = ratio_tiefix(x[4 * g + e], rq[e], norm, P.s);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int q = 4 * g + e;
-            const int k = (int)level_of_ratio(rr[q], w[e]);
-            lv[q] = (__float_as_uint(rr[q]) >> 31) ? -k : k;
+            const int k = (int)level_of_ratio(rq[e], w[e]);
+            lv[q] = (__float_as_uint(rq[e]) >> 31) ? -k : k;
         }
     }
     if (g0 + kCPT <= P.n) {
@@ -588,8 +582,14 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
         }
         const float norm = P.maxnorm ? aligned_norm<true>(x, G, sh_red) : aligned_norm<false>(x, G, sh_red);
         const bool bstart = first_of_bucket && g0 < P.n;
-        float rr[kCPT];
-        signed_ratios(x, norm, P.s, P.sigma, rr);
+        // ratios (ratio_of) per block of four, just before their levels; the
+        // coordinates are converted to fp64 again there, so that the norm's fp64
+        // copies do not stay live through the loop (91 VGPRs instead of 117, five
+        // waves per SIMD instead of four)
+        const double cb = ratio_scale(norm, P.s);
+        const bool tie = ratio_may_tie(norm, P.sigma);
+#pragma unroll
+        for (int q = 0; q < kCPT; ++q) asm volatile("" : "+v"(x[q]));
 
         // ---- levels and record codes; records packed right-aligned into two
         // 64-bit registers (coordinates 0-7 and 8-15) ----
@@ -610,12 +610,19 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
             uint32_t k0 = key0, k1 = key1;
             asm volatile("" : "+s"(k0), "+s"(k1));
             philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), k0, k1, w);
+            float rq[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rq[e] = ratio_fast(x[4 * g + e], cb);
+            if (tie) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rq[e] = ratio_tiefix(x[4 * g + e], rq[e], norm, P.s);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int q = 4 * g + e;
                 const int xi = x0 + q;
-                const uint32_t k = level_of_ratio(rr[q], w[e]);
-                const uint32_t neg = __float_as_uint(rr[q]) >> 31;
+                const uint32_t k = level_of_ratio(rq[e], w[e]);
+                const uint32_t neg = __float_as_uint(rq[e]) >> 31;
                 const uint32_t gg = have ? (uint32_t)(xi - prev) : 0u;
                 const uint32_t ent = rt[code_index(gg, k, neg)];
                 const uint32_t len = ent & 31u;
@@ -700,8 +707,7 @@ __global__ __launch_bounds__(kWG) void encode_aligned_kernel(QsgdParams P, uint3
                     asm volatile("" : "+s"(k0), "+s"(k1));
                     philox4x32_10((uint32_t)(gi >> 2), (uint32_t)(gi >> 34), k0, k1, w);
                     const float xv = gi < P.n ? P.v[gi] : 0.0f;
-                    const uint32_t k = qlevel(xv, ratio_scale(norm, P.s), ratio_may_tie(norm, P.sigma), norm,
-                                              P.s, w[q & 3]);
+                    const uint32_t k = qlevel(xv, cb, tie, norm, P.s, w[q & 3]);
                     const uint32_t neg = __float_as_uint(xv) >> 31;
                     if (q >= QW * h) {
                         const uint32_t gg = hv ? (uint32_t)(x0 + q - pv) : 0u;

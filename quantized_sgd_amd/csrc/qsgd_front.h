@@ -70,8 +70,8 @@ __host__ __device__ __forceinline__ uint32_t run_of(uint32_t t, uint32_t run, ui
 // LDS carved out of the dynamic shared memory block for the front half.
 struct FrontLds {
     int32_t *bs;      // [K + 1] bucket starts relative to A
-    double *cb;       // [K] sum of squares, then ratio_scale(norm, s), or -1 where
-                      // the bucket takes the exact ratio (ratio_may_tie)
+    double *cb;       // [K] sum of squares, then ratio_scale(norm, s), negated where
+                      // the bucket's ratios take the midpoint test (ratio_may_tie)
     float *nrm;       // [K] norms
     double *segv;     // [kWaves] scan scratch
     int *segf;        // [kWaves]
@@ -169,8 +169,8 @@ __device__ __forceinline__ int first_bucket(const QsgdParams &P, const Tile &t, 
 // segmented scan in thread order. The order is fixed, so results are
 // reproducible; it differs from a plain left-to-right sum only in rounding.
 // Afterwards L.nrm[k] = RN32(sqrt(sum)) and L.cb[k] = RD64(s / norm) (0 for a
-// zero bucket; -1 for a bucket whose ratios are computed exactly, see
-// ratio_may_tie). MAXN: the max-norm max|v_i| instead (exact, in any order).
+// zero bucket; negated for a bucket whose ratios take the midpoint test, see
+// ratio_may_tie and ratio_tiefix). MAXN: the max-norm max|v_i| instead (exact, in any order).
 // Ends with a barrier.
 template <bool RAGGED, bool MAXN = false>
 __device__ __forceinline__ void bucket_norms(const QsgdParams &P, const Tile &t, FrontLds &L,
@@ -216,7 +216,7 @@ __device__ __forceinline__ void bucket_norms(const QsgdParams &P, const Tile &t,
     for (uint32_t b = threadIdx.x; b < t.K; b += kWG) {
         const float nr = MAXN ? (float)L.cb[b] : (float)sqrt(L.cb[b]);
         L.nrm[b] = nr;
-        L.cb[b] = ratio_may_tie(nr, P.sigma) ? -1.0 : ratio_scale(nr, P.s);
+        L.cb[b] = ratio_may_tie(nr, P.sigma) ? -ratio_scale(nr, P.s) : ratio_scale(nr, P.s);
     }
     __syncthreads();
 }
@@ -257,7 +257,7 @@ __device__ __forceinline__ void quantize_coords(const QsgdParams &P, const Tile 
                     cb = L.cb[k];
                     o.bst |= 1u << q;
                 }
-                kk = level_of_ratio(cb < 0.0 ? ratio_exact(c.x[q], L.nrm[k], P.s) : ratio_fast(c.x[q], cb),
+                kk = level_of_ratio(ratio_of(c.x[q], fabs(cb), cb < 0.0, L.nrm[k], P.s),
                                     w[e]);
                 if (__float_as_uint(c.x[q]) >> 31) o.neg |= 1u << q;
             }

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kWG) void span_norm_fold_kernel(QsgdParams P) {
     }
 }
 
-// The window's bucket constants in LDS: norms, ratio scales (-1: exact ratios)
+// The window's bucket constants in LDS: norms, ratio scales (negated: midpoint test)
 // and bucket starts.
 __device__ __forceinline__ void span_constants(const QsgdParams &P, const SpanWin &w, float *s_nrm,
                                                double *s_cb, int *s_bs) {
@@ -162,7 +162,7 @@ __device__ __forceinline__ void span_constants(const QsgdParams &P, const SpanWi
     if (j < w.K) {
         const float norm = P.sp.norms[w.kb0 + j];
         s_nrm[j] = norm;
-        s_cb[j] = ratio_may_tie(norm, P.sigma) ? -1.0 : ratio_scale(norm, P.s);
+        s_cb[j] = ratio_may_tie(norm, P.sigma) ? -ratio_scale(norm, P.s) : ratio_scale(norm, P.s);
     }
     if (j <= (uint32_t)kSpanK) s_bs[j] = span_bucket_start(P, w, j);
 }
@@ -188,7 +188,7 @@ __device__ __forceinline__ void span_levels(const QsgdParams &P, const SpanWin &
             if (w.A + (uint64_t)xi < w.end) {
                 const uint32_t b = span_piece(bs, w.K, xi);
                 const double cb = s_cb[b];
-                kk = level_of_ratio(cb < 0.0 ? ratio_exact(x[q], s_nrm[b], P.s) : ratio_fast(x[q], cb), wd[e]);
+                kk = level_of_ratio(ratio_of(x[q], fabs(cb), cb < 0.0, s_nrm[b], P.s), wd[e]);
                 if (__float_as_uint(x[q]) >> 31) neg |= 1u << q;
             }
             k[q] = kk;
