@@ -786,8 +786,16 @@ __global__ __launch_bounds__(kWG) void encode_finish_kernel(FinishParams F) {
     const uint32_t r0 = run_of(t0, F.run, F.rem);
     const uint32_t m = t1 - t0;  // this share's tiles (chunk <= kFinishTiles <= kWG)
     const uint64_t mine = (uint32_t)j < m ? (uint64_t)F.tile_bits[t0 + j] : 0ull;
+    // (eight loads in flight per thread: a sum over a strided loop would wait
+    // for each load before issuing the next)
     uint64_t acc = 0;
-    for (uint32_t i = (uint32_t)j; i < r0; i += kWG) acc += F.run_bits[i];
+    for (uint32_t i = (uint32_t)j; i < r0; i += 8u * kWG) {
+        uint64_t rb[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8u; ++u) rb[u] = i + u * kWG < r0 ? F.run_bits[i + u * kWG] : 0ull;
+#pragma unroll
+        for (uint32_t u = 0; u < 8u; ++u) acc += rb[u];
+    }
     for (uint32_t t = run_first(r0, F.run, F.rem) + (uint32_t)j; t < t0; t += kWG) acc += F.tile_bits[t];
     acc = wave_incl_add_u64(acc);
     if (lane == 63) sh_red[wave] = acc;

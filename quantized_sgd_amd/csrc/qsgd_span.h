@@ -472,7 +472,19 @@ __global__ __launch_bounds__(kWG) void span_finish_kernel(SpanFinishParams S) {
     const uint32_t m = t1 - t0;
     const uint64_t mine = (uint32_t)j < m ? (uint64_t)span_str(S, t0 + j).T : 0ull;
     uint64_t acc = 0;
-    for (uint32_t i = (uint32_t)j; i < r0; i += kWG) acc += F.run_bits[i] + S.sp.lp[i];
+    // (eight pairs of loads in flight per thread)
+    for (uint32_t i = (uint32_t)j; i < r0; i += 8u * kWG) {
+        uint64_t rb[8];
+        uint32_t lp[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8u; ++u) {
+            const bool in = i + u * kWG < r0;
+            rb[u] = in ? F.run_bits[i + u * kWG] : 0ull;
+            lp[u] = in ? S.sp.lp[i + u * kWG] : 0u;
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < 8u; ++u) acc += rb[u] + lp[u];
+    }
     for (uint32_t t = run_first(r0, F.run, F.rem) + (uint32_t)j; t < t0; t += kWG) acc += span_str(S, t).T;
     acc = wave_incl_add_u64(acc);
     if (lane == 63) sh_red[wave] = acc;
