@@ -136,10 +136,21 @@ __global__ __launch_bounds__(kWG) void span_norm_fold_kernel(QsgdParams P) {
     const uint64_t c0 = b * P.d;
     const uint64_t c1 = c0 + P.d < P.n ? c0 + P.d : P.n;
     const uint64_t tf = c0 >> 12, tl = (c1 - 1) >> 12;
+    // the bucket's piece in window t: every window after its first one starts
+    // inside it, so only the first window needs the division; eight loads in
+    // flight per thread, folded in the same order as one at a time
+    const uint64_t kf = b - (tf << 12) / P.d;
     double acc = 0.0;
-    for (uint64_t t = tf + threadIdx.x; t <= tl; t += kWG) {
-        const uint64_t k = b - (t << 12) / P.d;
-        acc = op(acc, P.sp.partial[t * kSpanK + k]);
+    for (uint64_t t = tf + threadIdx.x; t <= tl; t += 8u * kWG) {
+        double pv[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8u; ++u) {
+            const uint64_t tu = t + (uint64_t)u * kWG;
+            pv[u] = tu <= tl ? P.sp.partial[tu * kSpanK + (tu == tf ? kf : 0u)] : 0.0;
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < 8u; ++u)
+            if (t + (uint64_t)u * kWG <= tl) acc = op(acc, pv[u]);
     }
     const double tot = wave_total_f64<MAXN>(acc);
     const int wave = __builtin_amdgcn_readfirstlane(wave_id());
