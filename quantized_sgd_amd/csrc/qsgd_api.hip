@@ -339,20 +339,23 @@ qsgd_status encode_impl(const float *v, uint64_t n, const uint64_t *bstart, uint
         // about 0.8 s / sqrt(d) under the L2 norm, 0.8 s / max|z| (about s / 4)
         // under the max-norm; past about 2 a half's 8 records pass 64 bits
         const bool quarters = norm == QSGD_NORM_MAX ? s >= 8 : (uint64_t)s * s >= 6ull * d;
-        // twice the resident workgroups: the second half starts as workgroups of
-        // the first finish, which evens out the end of the pass (per encode, c3:
-        // 115.7 -> 109.2 us, c2: 54.9 -> 54.0, c4: 455 -> 442; on c3 1.5 times is
-        // slower than once, 2.5 and 4 times a little slower than twice)
+        // three times the resident workgroups: later ones start as workgroups of
+        // the first finish, which evens out the end of the pass (per encode with
+        // five workgroups per CU, against twice: c3 128.5 -> 127.1 us, c2 64.6 ->
+        // 62.9, c4 441 -> 430; once is slower than twice, and four times, capped at
+        // kMaxRuns runs, about the same as three)
         auto launch = [&](auto kernel) {
-            const uint32_t blocks = runs_for(2 * resident_blocks(kernel, lds));
+            const uint32_t blocks = runs_for(3 * resident_blocks(kernel, lds));
             hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), lds, stream, P, log2u(d));
         };
         if (quarters) launch(encode_aligned_kernel<true>);
         else launch(encode_aligned_kernel<false>);
     } else {
-        // twice the resident workgroups too (c5: 221 -> 211 us per encode)
+        // four times the resident workgroups (kMaxRuns with four per CU; c5 per
+        // encode: once 221, twice 211, three times and four times 224 and 220 us
+        // against twice's 226 on a later box)
         auto launch = [&](auto kernel) {
-            const uint32_t blocks = runs_for(2 * resident_blocks(kernel, p.lds_bytes));
+            const uint32_t blocks = runs_for(4 * resident_blocks(kernel, p.lds_bytes));
             hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWG), p.lds_bytes, stream, P);
         };
         if (ragged) {
