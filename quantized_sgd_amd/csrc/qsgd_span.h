@@ -313,6 +313,9 @@ __global__ __launch_bounds__(kWG) void span_encode_kernel(QsgdParams P) {
                 prev = xi;
                 have = 1;
             }
+            // markers formed four coordinates at a time, not left to sink below
+            // the loop with 16 lane masks live in SGPRs
+            if ((q & 3) == 3) asm volatile("" : "+v"(pendx), "+v"(prev), "+v"(have));
         }
         const int marker = have ? prev : INT_MIN;
 
