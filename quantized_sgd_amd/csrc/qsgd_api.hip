@@ -486,11 +486,16 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
     D.solo = (!acc && lds_out && tpw >= 8 && kSoloBuckets % tpw == 0) ? 1u : 0u;
     const uint64_t groups = (nb + tpw - 1) / tpw;
     const uint64_t want = (groups + kDecWaves - 1) / kDecWaves;
+    // with sparse units possible, a wave per unit of kSoloBuckets buckets
+    const uint64_t want_units = D.solo ? ((nb + kSoloBuckets - 1) / kSoloBuckets + kDecWaves - 1) / kDecWaves : 0;
     const size_t lds = decode_lds_bytes();
     // the resident workgroups (twice as many: c3 119 -> 118.6 us, but c2 61.6 ->
-    // 64.9 us, where that gives every group a workgroup of its own)
+    // 64.9 us, where that gives every group a workgroup of its own), or more
+    // for a wave per sparse unit (the 2^28-coordinate heavy-tailed stream:
+    // 406 -> 385 us)
     auto launch = [&](auto kernel) {
-        const uint32_t blocks = (uint32_t)std::min<uint64_t>(want, resident_blocks(kernel, lds, kDecWG));
+        const uint32_t blocks = (uint32_t)std::max<uint64_t>(
+            want_units, std::min<uint64_t>(want, resident_blocks(kernel, lds, kDecWG)));
         hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kDecWG), lds, stream, D);
     };
     // the code is a kernel parameter so that each kernel holds one record decoder

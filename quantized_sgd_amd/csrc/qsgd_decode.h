@@ -636,16 +636,23 @@ struct QuadWriter {
         }
         *p4 = v;
     }
+    // The elements of the quad v at out[a, a + 4) that lie in [l, h), one by one
+    // (a quad cut by a range end). The empty asm keeps the compiler from merging
+    // the last of these stores with the 16-byte store of a whole quad in the
+    // caller's other branch, which it would then split into 12- and 4-byte stores.
+    __device__ __forceinline__ static void put_part(float *out, uint64_t a, uint64_t l, uint64_t h, float4 v) {
+        if (a >= l && a < h) put1(out + a, v.x);
+        if (a + 1 >= l && a + 1 < h) put1(out + a + 1, v.y);
+        if (a + 2 >= l && a + 2 < h) put1(out + a + 2, v.z);
+        if (a + 3 >= l && a + 3 < h) put1(out + a + 3, v.w);
+        asm volatile("" ::: "memory");
+    }
     __device__ __forceinline__ void flush() const {
         const uint64_t a = q << 2;
-        if (a >= lo && a + 4 <= hi) {
+        if (a >= lo && a + 4 <= hi)
             put4(out + a, make_float4(v0, v1, v2, v3));
-        } else {
-            if (a >= lo && a < hi) put1(out + a, v0);
-            if (a + 1 >= lo && a + 1 < hi) put1(out + a + 1, v1);
-            if (a + 2 >= lo && a + 2 < hi) put1(out + a + 2, v2);
-            if (a + 3 >= lo && a + 3 < hi) put1(out + a + 3, v3);
-        }
+        else
+            put_part(out, a, lo, hi, make_float4(v0, v1, v2, v3));
     }
     // moves to quad nq > q: writes the current quad and the all-zero quads between
     __device__ __forceinline__ void advance(uint64_t nq) {
@@ -992,14 +999,10 @@ __device__ __forceinline__ void store_group(const DecodeParams &D, const uint8_t
                 const uint32_t word = lw[(a - lbase) >> 2];
                 const float v0 = tbl[word & 0xffu], v1 = tbl[(word >> 8) & 0xffu];
                 const float v2 = tbl[(word >> 16) & 0xffu], v3 = tbl[word >> 24];
-                if (a >= A && a + 4 <= B) {
+                if (a >= A && a + 4 <= B)
                     QuadWriter<ACC>::put4(D.v_hat + a, make_float4(v0, v1, v2, v3));
-                } else {
-                    if (a >= A && a < B) QuadWriter<ACC>::put1(D.v_hat + a, v0);
-                    if (a + 1 >= A && a + 1 < B) QuadWriter<ACC>::put1(D.v_hat + a + 1, v1);
-                    if (a + 2 >= A && a + 2 < B) QuadWriter<ACC>::put1(D.v_hat + a + 2, v2);
-                    if (a + 3 >= A && a + 3 < B) QuadWriter<ACC>::put1(D.v_hat + a + 3, v3);
-                }
+                else
+                    QuadWriter<ACC>::put_part(D.v_hat, a, A, B, make_float4(v0, v1, v2, v3));
             }
         }
         // the table is rebuilt for the next bucket
@@ -1042,14 +1045,29 @@ __device__ __forceinline__ bool solo_unit_ok(const uint64_t *offs, uint64_t ub0,
     return __ballot(bad) == 0;
 }
 
-// Decodes the unit [ub0, ub1) (solo_unit_ok) of a plain decode: its stream
-// words to the stage; +0.0f to all of its outputs with 16-byte stores where
-// whole aligned quads allow; then, once those stores are done, lane i follows
-// bucket ub0 + i from its first record and writes each record's value
-// RN32(norm k / s) with its sign at its coordinate.
+// Coordinates of one bucket per window of the sparse-unit decode: a lane's row
+// of the wave's tile (64 rows of fp32 in the level buffer).
+constexpr uint32_t kSoloWin = 16;
+static_assert(kSoloBuckets * kSoloWin * 4 <= kLevelBytes, "sparse-unit tile in the level buffer");
+
+// Float index in the tile of coordinate i (0..15) of row `row`: the row's four
+// quads rotated by the row number, so that lanes writing the same i of
+// neighbouring rows hit different LDS banks.
+__device__ __forceinline__ uint32_t solo_slot(uint32_t row, uint32_t i) {
+    return row * kSoloWin + ((((i >> 2) ^ row) & 3u) << 2) + (i & 3u);
+}
+
+// Decodes the unit [ub0, ub1) (solo_unit_ok) of a plain decode. Lane i follows
+// bucket ub0 + i from its first record; the value of each record is
+// RN32(norm k / s) with its sign, every other coordinate +0.0f. Each bucket's
+// coordinates are taken in windows of kSoloWin from its first 16-byte quad on:
+// per window, each lane puts the values of its records in the window into its
+// tile row (otherwise zero), and the wave stores the 64 rows with 16-byte
+// stores, the quads a bucket shares with a neighbour element by element. Every
+// output is thus written once, by coalesced stores.
 template <bool RAGGED, int CODE>
 __device__ __forceinline__ void solo_unit(const DecodeParams &D, const uint64_t *in, const uint64_t *offs,
-                                          const uint32_t *lut, uint64_t *stage, uint64_t ub0,
+                                          const uint32_t *lut, uint64_t *stage, float *tile, uint64_t ub0,
                                           uint64_t ub1, uint64_t total_words) {
     const uint32_t lane = (uint32_t)lane_id();
     const uint64_t w0 = offs[ub0] >> 6;
@@ -1058,47 +1076,100 @@ __device__ __forceinline__ void solo_unit(const DecodeParams &D, const uint64_t 
     const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
     for (uint64_t i = lane; i < nw + kStagePad; i += 64)
         stage[i] = i < nw ? __builtin_bitreverse64(in[w0 + i]) : 0ull;
-    // zeros over the unit's coordinates [C0, C1)
-    const uint64_t C0 = bucket_first<RAGGED>(D, ub0), C1 = bucket_first<RAGGED>(D, ub1);
-    const uint64_t qa = (C0 + 3) >> 2, qb = C1 >> 2;
     const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (qa < qb) {
-        for (uint64_t qd = qa + lane; qd < qb; qd += 64) *reinterpret_cast<float4 *>(D.v_hat + (qd << 2)) = z;
-        if (lane < (uint32_t)((qa << 2) - C0)) D.v_hat[C0 + lane] = 0.0f;
-        if (lane < (uint32_t)(C1 - (qb << 2))) D.v_hat[(qb << 2) + lane] = 0.0f;
-    } else if (C0 + lane < C1) {
-        D.v_hat[C0 + lane] = 0.0f;
+    {
+        float4 *row4 = reinterpret_cast<float4 *>(tile + lane * kSoloWin);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) row4[q] = z;
     }
-    // the zeros are written before this wave writes any value over them
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    // this lane's bucket, coordinates relative to U (the unit's first quad)
+    const uint64_t U = bucket_first<RAGGED>(D, ub0) & ~(uint64_t)3;
+    const uint64_t b = ub0 + lane;
+    uint32_t c0 = 0, c1 = 0;
+    if (b < ub1) {
+        c0 = (uint32_t)(bucket_first<RAGGED>(D, b) - U);
+        c1 = (uint32_t)(bucket_first<RAGGED>(D, b + 1) - U);
+    }
+    const uint32_t a = c0 & ~3u;  // the row's first coordinate
+    const uint32_t nwin = c1 > c0 ? (c1 - a + kSoloWin - 1) / kSoloWin : 0u;
+    uint32_t maxwin = nwin;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) maxwin = max(maxwin, (uint32_t)__shfl_xor((int)maxwin, o));
+    // the rows this lane stores: 16 r + lane / 4, quad lane % 4 of each window
+    uint32_t ra[4], rc0[4], rc1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int src = 16 * q + (int)(lane >> 2);
+        ra[q] = (uint32_t)__shfl((int)a, src);
+        rc0[q] = (uint32_t)__shfl((int)c0, src);
+        rc1[q] = (uint32_t)__shfl((int)c1, src);
+    }
+    // the staged words and zeroed rows are read by other lanes of this wave
     wave_sync();
+
     const Bits<true> r{nullptr, 0u};
     const uint64_t gbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
-    const uint64_t b = ub0 + lane;
+    const uint32_t len = c1 - c0;
+    uint32_t p = 0, E = 0;
+    double e_b = 0.0;
     if (b < ub1) {
-        const uint32_t A = (uint32_t)(offs[b] - gbit), E = (uint32_t)(offs[b + 1] - gbit);
-        const uint64_t c0 = bucket_first<RAGGED>(D, b);
-        const uint64_t len = bucket_first<RAGGED>(D, b + 1) - c0;
-        if (E >= A + 32u && len > 0) {
-            const double e_b = (double)__uint_as_float(__builtin_bitreverse32((uint32_t)r.at(A)));
-            const RecordCtx<CODE> x{lut, bitlen32((uint32_t)len), bitlen32(D.s), D.s};
-            uint32_t p = A + 32u;
-            uint64_t jj = ~0ull;
-            Win W = win_at(r, p);
-            while (p < E) {
-                uint32_t gap, neg, k;
-                const uint32_t nq = record_at(r, x, p, gap, neg, k, W);
-                if (!nq) break;
-                jj += gap;
-                if (jj >= len) break;
-                const float m = dequant_value(e_b, k, D.s, D.s_pow2 != 0u, D.inv_s);
-                D.v_hat[c0 + jj] = neg ? -m : m;
-                p = nq;
-            }
+        p = (uint32_t)(offs[b] - gbit);
+        E = (uint32_t)(offs[b + 1] - gbit);
+        if (E >= p + 32u && len > 0) {
+            e_b = (double)__uint_as_float(__builtin_bitreverse32((uint32_t)r.at(p)));
+            p += 32u;
+        } else {
+            E = p;  // no records
         }
     }
-    // the stage is reused by this wave's next unit or group
-    wave_sync();
+    const RecordCtx<CODE> x{lut, bitlen32(len), bitlen32(D.s), D.s};
+    Win W = win_at(r, p);
+    uint32_t jj = ~0u;      // bucket index of the last record
+    uint32_t rel = 0;       // row coordinate of the pending record
+    float val = 0.0f;       // its value
+    bool has = false;
+    // the next record of the bucket, if any (a record that does not parse, or
+    // lies past the bucket, ends it)
+    auto next = [&]() {
+        has = false;
+        if (p < E) {
+            uint32_t gap, neg, k;
+            const uint32_t nq = record_at(r, x, p, gap, neg, k, W);
+            if (nq) {
+                jj += gap;
+                if (jj < len) {
+                    const float m = dequant_value(e_b, k, D.s, D.s_pow2 != 0u, D.inv_s);
+                    val = neg ? -m : m;
+                    rel = (c0 - a) + jj;
+                    has = true;
+                    p = nq;
+                }
+            }
+        }
+    };
+    next();
+    for (uint32_t i = 0; i < maxwin; ++i) {
+        const uint32_t lo = i * kSoloWin;
+        while (has && rel < lo + kSoloWin) {
+            tile[solo_slot(lane, rel - lo)] = val;
+            next();
+        }
+        wave_sync();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t row = 16u * (uint32_t)q + (lane >> 2);
+            float4 *src = reinterpret_cast<float4 *>(tile + row * kSoloWin) + (((lane ^ row) & 3u));
+            const float4 v = *src;
+            *src = z;
+            const uint32_t X = ra[q] + lo + 4u * (lane & 3u);
+            if (X >= rc0[q] && X + 4u <= rc1[q])
+                *reinterpret_cast<float4 *>(D.v_hat + U + X) = v;
+            else  // a quad shared with a neighbouring bucket, or past the row's bucket
+                QuadWriter<false>::put_part(D.v_hat + U, X, rc0[q], rc1[q], v);
+        }
+        // the rows are filled again for the next window
+        wave_sync();
+    }
 }
 
 // LDS_OUT: levels staged in LDS (D.lds_out), else each lane writes its range.
@@ -1129,78 +1200,84 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     double *ebs = reinterpret_cast<double *>(wbase + kStageBytes + kLevelBytes);
     const uint32_t tpw = D.tpw;
     const uint64_t ngroups = (D.nb + tpw - 1) / tpw;
-    // with D.solo, and a stream of at most kSoloAvgBits bits per bucket on
-    // average, groups are taken unit by unit transposed (the first group of
-    // every unit, then the second ...), so that the units decoded a lane per
-    // bucket spread over the waves; the other groups of such a unit are skipped
+    // Plain decodes with D.solo of a stream of at most kSoloAvgBits bits per
+    // bucket on average go by units of kSoloBuckets buckets, a wave each: a
+    // unit that qualifies is decoded a lane per bucket (solo_unit), the groups
+    // of any other by the same wave in turn. For such streams the host launches
+    // a wave per unit rather than the resident workgroups, so that workgroups
+    // start as others finish: the memory system serves the resident waves
+    // unevenly, and a fixed share of units per wave would leave the slowest
+    // waves running alone at the end. Otherwise the waves take groups in turn.
     const bool solo = !ACC && LDS_OUT && D.solo != 0u &&
                       D.offsets[0][D.nb] <= D.nb * (uint64_t)kSoloAvgBits;
-    const uint64_t gpu = solo ? kSoloBuckets / tpw : 1u;  // groups per unit
-    const uint64_t nunits = (ngroups + gpu - 1) / gpu;
+    const uint64_t gpu = kSoloBuckets / tpw;  // groups per unit (with solo)
+    const uint64_t items = solo ? (D.nb + kSoloBuckets - 1) / kSoloBuckets : ngroups;
 
-    for (uint64_t t = (uint64_t)blockIdx.x * kDecWaves + (uint64_t)wv; t < nunits * gpu;
-         t += (uint64_t)gridDim.x * kDecWaves) {
-        uint64_t g = t;
+    for (uint64_t w = (uint64_t)blockIdx.x * kDecWaves + (uint64_t)wv; w < items;
+         w += (uint64_t)gridDim.x * kDecWaves) {
+        uint64_t g0 = w, g1 = w + 1;
         if (solo) {
-            const uint64_t u = t % nunits, j = t / nunits;
-            g = u * gpu + j;
-            if (g >= ngroups) continue;
-            const uint64_t ub0 = u * kSoloBuckets;
+            const uint64_t ub0 = w * kSoloBuckets;
             const uint64_t ub1 = ub0 + kSoloBuckets < D.nb ? ub0 + kSoloBuckets : D.nb;
             const uint64_t *offs = D.offsets[0];
             const uint64_t total_words = (offs[D.nb] + 63) >> 6;
             if (solo_unit_ok(offs, ub0, ub1, total_words)) {
-                if (j == 0) solo_unit<RAGGED, CODE>(D, D.in[0], offs, lut, stage, ub0, ub1, total_words);
+                solo_unit<RAGGED, CODE>(D, D.in[0], offs, lut, stage, reinterpret_cast<float *>(lvl), ub0, ub1,
+                                        total_words);
                 continue;
             }
+            g0 = w * gpu;
+            g1 = g0 + gpu < ngroups ? g0 + gpu : ngroups;
         }
-        const uint64_t b0 = g * tpw;
-        const uint64_t b1 = b0 + tpw < D.nb ? b0 + tpw : D.nb;
-        const uint64_t lbase = bucket_first<RAGGED>(D, b0) & ~(uint64_t)3;
-        const uint32_t span = LDS_OUT ? (uint32_t)(bucket_first<RAGGED>(D, b1) - lbase) : 0u;
-        const uint32_t nclear16 = (span + 3 + 15) >> 4;
-        for (uint32_t k = 0; k < (ACC ? D.nstreams : 1u); ++k) {
-            const uint64_t *in = D.in[k];
-            const uint64_t *offs = D.offsets[k];
-            const uint64_t total_words = (offs[D.nb] + 63) >> 6;
-            const uint64_t A0 = offs[b0], E1 = offs[b1];
-            const uint64_t w0 = A0 >> 6;
-            uint64_t w1 = E1 > A0 ? ((E1 + 63) >> 6) : w0;
-            if (w1 > total_words) w1 = total_words;
-            const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
-            // a group whose stream does not fit the stage is staged over the
-            // stage and the level buffer together (each lane then writes its
-            // outputs directly), or, larger still, read from global memory
-            const bool in_lds = nw <= (uint64_t)kStageWords;
-            const bool in_big = !in_lds && nw <= (uint64_t)kBigStageWords;
-            if (in_lds || in_big) {
-                // bit-reversed words: stream bit 64 i + t of the group in bit t of word i
-                for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64)
-                    stage[i] = i < nw ? __builtin_bitreverse64(in[w0 + i]) : 0ull;
-            }
-            // staged words are read by other lanes of this wave
-            wave_sync();
-            // LDS positions are LDS bit addresses: the group's bit 0 is the first bit of stage
-            Bits<true> rl{nullptr, 0u};
-            const uint64_t lgbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
-            Bits<false> rg{reinterpret_cast<const uint32_t *>(in + w0),
-                           (uint32_t)(2 * (total_words - w0)) - 1u};
-            if (in_lds)
-                decode_group<RAGGED, true, LDS_OUT, ACC, CODE, true>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
-                                                               lbase, nclear16);
-            else if (in_big)
-                decode_group<RAGGED, true, false, ACC, CODE, false>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
-                                                              lbase, nclear16);
-            else
-                decode_group<RAGGED, false, LDS_OUT, ACC, CODE, true>(D, offs, lut, rg, w0 * 64, b0, b1, lvl,
-                                                                ebs, lbase, nclear16);
-            if (LDS_OUT && !in_big) {
+        for (uint64_t g = g0; g < g1; ++g) {
+            const uint64_t b0 = g * tpw;
+            const uint64_t b1 = b0 + tpw < D.nb ? b0 + tpw : D.nb;
+            const uint64_t lbase = bucket_first<RAGGED>(D, b0) & ~(uint64_t)3;
+            const uint32_t span = LDS_OUT ? (uint32_t)(bucket_first<RAGGED>(D, b1) - lbase) : 0u;
+            const uint32_t nclear16 = (span + 3 + 15) >> 4;
+            for (uint32_t k = 0; k < (ACC ? D.nstreams : 1u); ++k) {
+                const uint64_t *in = D.in[k];
+                const uint64_t *offs = D.offsets[k];
+                const uint64_t total_words = (offs[D.nb] + 63) >> 6;
+                const uint64_t A0 = offs[b0], E1 = offs[b1];
+                const uint64_t w0 = A0 >> 6;
+                uint64_t w1 = E1 > A0 ? ((E1 + 63) >> 6) : w0;
+                if (w1 > total_words) w1 = total_words;
+                const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
+                // a group whose stream does not fit the stage is staged over the
+                // stage and the level buffer together (each lane then writes its
+                // outputs directly), or, larger still, read from global memory
+                const bool in_lds = nw <= (uint64_t)kStageWords;
+                const bool in_big = !in_lds && nw <= (uint64_t)kBigStageWords;
+                if (in_lds || in_big) {
+                    // bit-reversed words: stream bit 64 i + t of the group in bit t of word i
+                    for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64)
+                        stage[i] = i < nw ? __builtin_bitreverse64(in[w0 + i]) : 0ull;
+                }
+                // staged words are read by other lanes of this wave
                 wave_sync();
-                // the staged stream is done with: its space holds the value table
-                store_group<RAGGED, ACC>(D, lvl, ebs, reinterpret_cast<float *>(stage), lbase, b0, b1);
+                // LDS positions are LDS bit addresses: the group's bit 0 is the first bit of stage
+                Bits<true> rl{nullptr, 0u};
+                const uint64_t lgbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
+                Bits<false> rg{reinterpret_cast<const uint32_t *>(in + w0),
+                               (uint32_t)(2 * (total_words - w0)) - 1u};
+                if (in_lds)
+                    decode_group<RAGGED, true, LDS_OUT, ACC, CODE, true>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
+                                                                   lbase, nclear16);
+                else if (in_big)
+                    decode_group<RAGGED, true, false, ACC, CODE, false>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
+                                                                  lbase, nclear16);
+                else
+                    decode_group<RAGGED, false, LDS_OUT, ACC, CODE, true>(D, offs, lut, rg, w0 * 64, b0, b1, lvl,
+                                                                    ebs, lbase, nclear16);
+                if (LDS_OUT && !in_big) {
+                    wave_sync();
+                    // the staged stream is done with: its space holds the value table
+                    store_group<RAGGED, ACC>(D, lvl, ebs, reinterpret_cast<float *>(stage), lbase, b0, b1);
+                }
+                // the LDS buffers are reused by the next stream or group of this wave
+                wave_sync();
             }
-            // the LDS buffers are reused by the next stream or group of this wave
-            wave_sync();
         }
     }
 }

@@ -185,6 +185,9 @@ __global__ __launch_bounds__(kWG) void quantize_kernel(QsgdParams P) {
             if (x >= c.vx0 && x < c.vx1)
                 P.levels[g0 + q] = (lv.neg >> q) & 1 ? -(int)lv.k[q] : (int)lv.k[q];
         }
+        // keeps the compiler from merging the last of these stores with the last
+        // 16-byte store above (which it would split into 12- and 4-byte stores)
+        asm volatile("" ::: "memory");
     }
     for (uint32_t b = threadIdx.x; b < t.K; b += kWG) P.norms[t.b0 + b] = L.f.nrm[b];
 }

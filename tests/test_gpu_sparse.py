@@ -1,9 +1,10 @@
 """GPU parity of plain decodes of sparse streams: units of 64 consecutive buckets
 whose stream fits the decoder's stage and whose payloads are at most 1024 bits
-each are decoded a lane per bucket, after the unit's outputs are zeroed; other
-units take the team decode. Page "QSGD (Quantized Stochastic Gradient Descent)
-with Elias Coding", encoding paragraph: a bucket's record stream is parsed from
-its norm on, and coordinates without a record decode to zero.
+each are decoded a lane per bucket, in windows of 16 coordinates per bucket that
+the wave stores whole (quads shared by neighbouring buckets element by element);
+other units take the team decode. Page "QSGD (Quantized Stochastic Gradient
+Descent) with Elias Coding", encoding paragraph: a bucket's record stream is
+parsed from its norm on, and coordinates without a record decode to zero.
 
 The inputs are mostly tiny values with a few large ones per bucket (few nonzero
 levels at s = 1, 2), a heavy-tailed Student-t draw like the 2^28-coordinate
