@@ -1180,6 +1180,8 @@ __device__ __forceinline__ void solo_unit(const DecodeParams &D, const uint64_t 
 template <bool RAGGED, bool LDS_OUT, bool ACC, int CODE>
 __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     extern __shared__ __align__(16) uint64_t dsmem[];
+    __shared__ uint32_t next_item;  // the workgroup's next item (below)
+    if (threadIdx.x == 0) next_item = 0;
     // record table after the waves' regions (a constant offset: folds into the
     // LDS instructions' offset field)
     uint32_t *lut = reinterpret_cast<uint32_t *>(reinterpret_cast<unsigned char *>(dsmem) +
@@ -1212,9 +1214,19 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
                       D.offsets[0][D.nb] <= D.nb * (uint64_t)kSoloAvgBits;
     const uint64_t gpu = kSoloBuckets / tpw;  // groups per unit (with solo)
     const uint64_t items = solo ? (D.nb + kSoloBuckets - 1) / kSoloBuckets : ngroups;
-
-    for (uint64_t w = (uint64_t)blockIdx.x * kDecWaves + (uint64_t)wv; w < items;
-         w += (uint64_t)gridDim.x * kDecWaves) {
+    // Workgroup b of G takes the consecutive items [b N / G, (b + 1) N / G) of
+    // the N, so that the workgroups' shares differ by at most one. Its waves
+    // take them one at a time from a counter in LDS, so waves that the SIMDs
+    // serve faster (the older ones of a workgroup issue first) take more (c3:
+    // with a fixed share per wave the last wave ended 37% after the median one).
+    const uint64_t ibase = items * blockIdx.x / gridDim.x;
+    const uint64_t ilim = items * (blockIdx.x + 1) / gridDim.x;
+    while (true) {
+        uint32_t k = 0;
+        if (lane == 0) k = atomicAdd(&next_item, 1u);
+        k = (uint32_t)__builtin_amdgcn_readfirstlane((int)k);
+        const uint64_t w = ibase + k;
+        if (w >= ilim) break;
         uint64_t g0 = w, g1 = w + 1;
         if (solo) {
             const uint64_t ub0 = w * kSoloBuckets;
