@@ -129,11 +129,11 @@ def cpu_baseline(w, max_coords: int, reps: int = 3):
             "pinned_core": core, **ident}
 
 
-def variant_leg(q, torch, args, v, lay, n, s, d, seed, nb, stream, nbits_omega, code, norm):
+def variant_leg(q, torch, args, v, lay, n, s, d, seed, nb, stream, nbits_omega, code, norm, flush):
     """The same workload with another record code (Elias gamma) or bucket scale
     (max-norm, the QSGDinf reading), through qsgd_encode_ex / qsgd_decode_ex:
-    call times on the launch stream, bits per coordinate, and the
-    algorithmic-bytes HBM fractions, next to the default's."""
+    call times on the launch stream (the same cache flush before each), bits per
+    coordinate, and the algorithmic-bytes HBM fractions, next to the default's."""
     dev = v.device
     G = code
     ragged = lay is not None
@@ -160,16 +160,19 @@ def variant_leg(q, torch, args, v, lay, n, s, d, seed, nb, stream, nbits_omega, 
         dec()
     torch.cuda.synchronize()
     steps = max(1, args.steps)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
+        flush()
         ev[i][0].record(stream)
         enc()
         ev[i][1].record(stream)
-        dec()
+        flush()
         ev[i][2].record(stream)
+        dec()
+        ev[i][3].record(stream)
     torch.cuda.synchronize()
     e_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    d_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    d_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
     nbits = int(bits.item())
     alg = 4.0 * n + nbits / 8.0 + 8.0 * (nb + 1)
     return {"encode_ms_avg": round(e_ms, 4), "decode_ms_avg": round(d_ms, 4),
@@ -179,7 +182,7 @@ def variant_leg(q, torch, args, v, lay, n, s, d, seed, nb, stream, nbits_omega, 
             "decode_hbm_frac": round(alg / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
-def decode_accumulate_leg(q, wl, torch, args, v0, n, s, d, seed, nb, stream):
+def decode_accumulate_leg(q, wl, torch, args, v0, n, s, d, seed, nb, stream, flush):
     """Decode-accumulate of k workers' streams (worker 0: the config's gradient)
     into one fp32 buffer, timed with HIP events on the launch stream. Algorithmic
     HBM bytes (the least any implementation moves): the k streams and offset
@@ -201,6 +204,7 @@ def decode_accumulate_leg(q, wl, torch, args, v0, n, s, d, seed, nb, stream):
     steps = max(1, args.steps)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
+        flush()
         ev[i][0].record(stream)
         q.decode_accumulate(words, offs, n, s, d, acc)
         ev[i][1].record(stream)
@@ -229,7 +233,10 @@ def main():
     ap.add_argument("--acc-streams", type=int, default=4,
                     help="streams of the decode-accumulate measurement (configs 2, 3; 0: skip)")
     ap.add_argument("--flush-mb", type=int, default=512,
-                    help="MiB overwritten before each timed call, outside the timed region (0: none)")
+                    help="MiB read (or overwritten) before each timed call, outside the timed region (0: none)")
+    ap.add_argument("--flush-kind", choices=["read", "write"], default="read",
+                    help="how the cache flush before each timed call evicts the inputs: "
+                         "by reading the flush buffer, or by overwriting it")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -279,9 +286,16 @@ def main():
         if args.flush_mb else None
 
     def flush():
-        # overwrite a buffer larger than the Infinity Cache (outside the timed region)
+        # evict the inputs from the caches (outside the timed region) by reading a
+        # buffer larger than the 256 MB Infinity Cache: dirty lines are written
+        # back here, and the timed call finds the caches holding clean lines only.
+        # Overwriting the buffer instead leaves up to 256 MB of its dirty lines for
+        # the timed call to write back.
         if flush_buf is not None:
-            flush_buf.fill_(0.0)
+            if args.flush_kind == "read":
+                flush_buf.sum(dtype=torch.float32)
+            else:
+                flush_buf.fill_(0.0)
 
     for i in range(args.warmup):
         enc(i % R)
@@ -348,7 +362,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "n": n, "d": d, "s": s, "buckets": nb,
-                   "input_copies_rotated": R, "flush_mb_between_calls": args.flush_mb},
+                   "input_copies_rotated": R, "flush_mb_between_calls": args.flush_mb,
+                   "flush_kind": args.flush_kind},
         "encode_ms": {"median": round(pct(enc_ms, 0.5), 4), "p10": round(pct(enc_ms, 0.1), 4),
                       "p90": round(pct(enc_ms, 0.9), 4), "avg": round(enc_avg, 4)},
         "decode_ms": {"median": round(pct(dec_ms, 0.5), 4), "p10": round(pct(dec_ms, 0.1), 4),
@@ -367,11 +382,12 @@ def main():
     }
     if not args.no_variants:
         res["gamma"] = variant_leg(q, torch, args, vs[0], lay, n, s, d, seed, nb, stream, nbits,
-                                   q.GAMMA, q.L2)
+                                   q.GAMMA, q.L2, flush)
         res["maxnorm"] = variant_leg(q, torch, args, vs[0], lay, n, s, d, seed, nb, stream, nbits,
-                                     q.OMEGA, q.MAXNORM)
+                                     q.OMEGA, q.MAXNORM, flush)
     if args.acc_streams and args.config in (2, 3) and not ragged:
-        res["decode_accumulate"] = decode_accumulate_leg(q, wl, torch, args, vs[0], n, s, d, seed, nb, stream)
+        res["decode_accumulate"] = decode_accumulate_leg(q, wl, torch, args, vs[0], n, s, d, seed, nb, stream,
+                                                         flush)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
     print(json.dumps(res), flush=True)
