@@ -489,6 +489,21 @@ qsgd_status decode_impl(const uint64_t *const *in, const uint64_t *const *offset
     // with sparse units possible, a wave per unit of kSoloBuckets buckets
     const uint64_t want_units = D.solo ? ((nb + kSoloBuckets - 1) / kSoloBuckets + kDecWaves - 1) / kDecWaves : 0;
     const size_t lds = decode_lds_bytes();
+    // decode-accumulate of up to kDecWaves streams over uniform buckets of
+    // kFoldMinD or more coordinates, a multiple of 4, levels in a byte: a
+    // workgroup decodes the streams of a group side by side and adds them to
+    // the output in one pass (accumulate_fold_kernel)
+    if (acc && !ragged && lds_out && nstreams <= (uint32_t)kDecWaves && d % 4u == 0 && d >= kFoldMinD) {
+        const uint64_t rounds = (groups + kDecWaves / nstreams - 1) / (kDecWaves / nstreams);
+        auto fold = [&](auto kernel) {
+            const uint32_t blocks =
+                (uint32_t)std::min<uint64_t>(rounds, resident_blocks(kernel, lds, kDecWG));
+            hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kDecWG), lds, stream, D);
+        };
+        if (code == QSGD_CODE_GAMMA) fold(accumulate_fold_kernel<1>);
+        else fold(accumulate_fold_kernel<0>);
+        return launch_status();
+    }
     // the resident workgroups (twice as many: c3 119 -> 118.6 us, but c2 61.6 ->
     // 64.9 us, where that gives every group a workgroup of its own), or more
     // for a wave per sparse unit (the 2^28-coordinate heavy-tailed stream:

@@ -1177,6 +1177,61 @@ __device__ __forceinline__ void solo_unit(const DecodeParams &D, const uint64_t 
 // out = ((out + v_hat_0) + v_hat_1) + ...; the wave takes all streams of a
 // group in turn, reading, adding to and writing back the group's outputs once
 // per stream.
+// One group of buckets [b0, b1) of every stream in turn (one stream for a plain
+// decode; decode-accumulate adds each stream's values to the output before the
+// next stream's): staged in the wave's LDS region, decoded, written.
+template <bool RAGGED, bool LDS_OUT, bool ACC, int CODE>
+__device__ __forceinline__ void decode_group_streams(const DecodeParams &D, const uint32_t *lut, uint64_t *stage,
+                                                     uint8_t *lvl, double *ebs, uint64_t b0, uint64_t b1) {
+    const int lane = lane_id();
+    const uint64_t lbase = bucket_first<RAGGED>(D, b0) & ~(uint64_t)3;
+    const uint32_t span = LDS_OUT ? (uint32_t)(bucket_first<RAGGED>(D, b1) - lbase) : 0u;
+    const uint32_t nclear16 = (span + 3 + 15) >> 4;
+    for (uint32_t k = 0; k < (ACC ? D.nstreams : 1u); ++k) {
+        const uint64_t *in = D.in[k];
+        const uint64_t *offs = D.offsets[k];
+        const uint64_t total_words = (offs[D.nb] + 63) >> 6;
+        const uint64_t A0 = offs[b0], E1 = offs[b1];
+        const uint64_t w0 = A0 >> 6;
+        uint64_t w1 = E1 > A0 ? ((E1 + 63) >> 6) : w0;
+        if (w1 > total_words) w1 = total_words;
+        const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
+        // a group whose stream does not fit the stage is staged over the
+        // stage and the level buffer together (each lane then writes its
+        // outputs directly), or, larger still, read from global memory
+        const bool in_lds = nw <= (uint64_t)kStageWords;
+        const bool in_big = !in_lds && nw <= (uint64_t)kBigStageWords;
+        if (in_lds || in_big) {
+            // bit-reversed words: stream bit 64 i + t of the group in bit t of word i
+            for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64)
+                stage[i] = i < nw ? __builtin_bitreverse64(in[w0 + i]) : 0ull;
+        }
+        // staged words are read by other lanes of this wave
+        wave_sync();
+        // LDS positions are LDS bit addresses: the group's bit 0 is the first bit of stage
+        Bits<true> rl{nullptr, 0u};
+        const uint64_t lgbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
+        Bits<false> rg{reinterpret_cast<const uint32_t *>(in + w0),
+                       (uint32_t)(2 * (total_words - w0)) - 1u};
+        if (in_lds)
+            decode_group<RAGGED, true, LDS_OUT, ACC, CODE, true>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
+                                                           lbase, nclear16);
+        else if (in_big)
+            decode_group<RAGGED, true, false, ACC, CODE, false>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
+                                                          lbase, nclear16);
+        else
+            decode_group<RAGGED, false, LDS_OUT, ACC, CODE, true>(D, offs, lut, rg, w0 * 64, b0, b1, lvl,
+                                                            ebs, lbase, nclear16);
+        if (LDS_OUT && !in_big) {
+            wave_sync();
+            // the staged stream is done with: its space holds the value table
+            store_group<RAGGED, ACC>(D, lvl, ebs, reinterpret_cast<float *>(stage), lbase, b0, b1);
+        }
+        // the LDS buffers are reused by the next stream or group of this wave
+        wave_sync();
+    }
+}
+
 template <bool RAGGED, bool LDS_OUT, bool ACC, int CODE>
 __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
     extern __shared__ __align__(16) uint64_t dsmem[];
@@ -1244,56 +1299,204 @@ __global__ __launch_bounds__(kDecWG) void decode_kernel(DecodeParams D) {
         for (uint64_t g = g0; g < g1; ++g) {
             const uint64_t b0 = g * tpw;
             const uint64_t b1 = b0 + tpw < D.nb ? b0 + tpw : D.nb;
-            const uint64_t lbase = bucket_first<RAGGED>(D, b0) & ~(uint64_t)3;
-            const uint32_t span = LDS_OUT ? (uint32_t)(bucket_first<RAGGED>(D, b1) - lbase) : 0u;
-            const uint32_t nclear16 = (span + 3 + 15) >> 4;
-            for (uint32_t k = 0; k < (ACC ? D.nstreams : 1u); ++k) {
-                const uint64_t *in = D.in[k];
-                const uint64_t *offs = D.offsets[k];
+            decode_group_streams<RAGGED, LDS_OUT, ACC, CODE>(D, lut, stage, lvl, ebs, b0, b1);
+        }
+    }
+}
+
+
+// ---- decode-accumulate with the streams of a group folded once ------------------
+// For k <= kDecWaves streams over uniform buckets of kFoldMinD or more
+// coordinates, a multiple of 4, with levels that fit a byte (the LDS level
+// path). The waves of a workgroup take the k streams of P = kDecWaves / k
+// consecutive groups at once, wave w stream w % k of group w / k: each decodes
+// its stream's part of the group into level bytes in its own LDS region. Then,
+// bucket by bucket, each such wave tabulates the 256 level bytes' values of its
+// stream's bucket in its stage, and the whole workgroup adds the k values of
+// every coordinate to the output in stream order, ((acc + v_0) + v_1) + ...:
+// the output is read and written once per call instead of once per stream. A
+// group with a stream that does not fit the stage is done by the wave of its
+// first stream alone, stream by stream (decode_group_streams).
+constexpr uint32_t kFoldMinD = 256;
+
+template <int CODE>
+__global__ __launch_bounds__(kDecWG) void accumulate_fold_kernel(DecodeParams D) {
+    extern __shared__ __align__(16) uint64_t dsmem[];
+    __shared__ uint32_t fold_slot[kDecWaves];  // group slot p of the round is folded
+    unsigned char *base = reinterpret_cast<unsigned char *>(dsmem);
+    uint32_t *lut = reinterpret_cast<uint32_t *>(base + (size_t)kDecWaves * kWaveLdsBytes);
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(CODE ? kRecordLutGamma.e : kRecordLut.e);
+        uint4 *dst = reinterpret_cast<uint4 *>(lut);
+        for (uint32_t i = threadIdx.x; i < sizeof(RecordLut) / 16; i += kDecWG) dst[i] = src[i];
+    }
+    __syncthreads();
+
+    const int lane = lane_id();
+    const uint32_t wv = (uint32_t)wave_id();
+    unsigned char *wbase = base + (size_t)wv * kWaveLdsBytes;
+    uint64_t *stage = reinterpret_cast<uint64_t *>(wbase);
+    uint8_t *lvl = wbase + kStageBytes;
+    double *ebs = reinterpret_cast<double *>(wbase + kStageBytes + kLevelBytes);
+    const uint32_t K = D.nstreams;          // 1 .. kDecWaves
+    const uint32_t P = kDecWaves / K;       // groups per round
+    const uint32_t slot = wv / K, j = wv - slot * K;
+    const uint32_t tpw = D.tpw, d = D.d;
+    const uint32_t nqd = d >> 2;            // quads per bucket
+    const uint64_t ngroups = (D.nb + tpw - 1) / tpw;
+    const uint64_t rounds = (ngroups + P - 1) / P;
+    // workgroup b of G takes the consecutive rounds [b R / G, (b + 1) R / G)
+    const uint64_t r0 = rounds * blockIdx.x / gridDim.x, r1 = rounds * (blockIdx.x + 1) / gridDim.x;
+    for (uint64_t r = r0; r < r1; ++r) {
+        const uint64_t g = r * P + slot;
+        const bool mine = slot < P && g < ngroups;
+        const uint64_t b0 = g * tpw;
+        const uint64_t b1 = b0 + tpw < D.nb ? b0 + tpw : D.nb;
+        bool fold = false;
+        if (mine) {
+            // the group fits the stage in every stream (lane t looks at stream t)
+            bool ok = true;
+            if ((uint32_t)lane < K) {
+                const uint64_t *offs = D.offsets[lane];
+                const uint64_t total_words = (offs[D.nb] + 63) >> 6;
+                const uint64_t A0 = offs[b0], E1 = offs[b1];
+                const uint64_t w0 = A0 >> 6;
+                uint64_t w1 = E1 > A0 ? ((E1 + 63) >> 6) : w0;
+                if (w1 > total_words) w1 = total_words;
+                ok = (w1 > w0 ? w1 - w0 : 0) <= (uint64_t)kStageWords;
+            }
+            fold = __ballot(!ok) == 0;
+            if (fold) {
+                const uint64_t *in = D.in[j];
+                const uint64_t *offs = D.offsets[j];
                 const uint64_t total_words = (offs[D.nb] + 63) >> 6;
                 const uint64_t A0 = offs[b0], E1 = offs[b1];
                 const uint64_t w0 = A0 >> 6;
                 uint64_t w1 = E1 > A0 ? ((E1 + 63) >> 6) : w0;
                 if (w1 > total_words) w1 = total_words;
                 const uint64_t nw = w1 > w0 ? w1 - w0 : 0;
-                // a group whose stream does not fit the stage is staged over the
-                // stage and the level buffer together (each lane then writes its
-                // outputs directly), or, larger still, read from global memory
-                const bool in_lds = nw <= (uint64_t)kStageWords;
-                const bool in_big = !in_lds && nw <= (uint64_t)kBigStageWords;
-                if (in_lds || in_big) {
-                    // bit-reversed words: stream bit 64 i + t of the group in bit t of word i
-                    for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64)
-                        stage[i] = i < nw ? __builtin_bitreverse64(in[w0 + i]) : 0ull;
-                }
-                // staged words are read by other lanes of this wave
+                for (uint64_t i = (uint64_t)lane; i < nw + kStagePad; i += 64)
+                    stage[i] = i < nw ? __builtin_bitreverse64(in[w0 + i]) : 0ull;
                 wave_sync();
-                // LDS positions are LDS bit addresses: the group's bit 0 is the first bit of stage
-                Bits<true> rl{nullptr, 0u};
+                const Bits<true> rl{nullptr, 0u};
                 const uint64_t lgbit = w0 * 64 - (uint64_t)lds_address(stage) * 8;
-                Bits<false> rg{reinterpret_cast<const uint32_t *>(in + w0),
-                               (uint32_t)(2 * (total_words - w0)) - 1u};
-                if (in_lds)
-                    decode_group<RAGGED, true, LDS_OUT, ACC, CODE, true>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
+                const uint64_t lbase = b0 * d;
+                const uint32_t nclear16 = ((uint32_t)(bucket_first<false>(D, b1) - lbase) + 3 + 15) >> 4;
+                decode_group<false, true, true, false, CODE, true>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
                                                                    lbase, nclear16);
-                else if (in_big)
-                    decode_group<RAGGED, true, false, ACC, CODE, false>(D, offs, lut, rl, lgbit, b0, b1, lvl, ebs,
-                                                                  lbase, nclear16);
-                else
-                    decode_group<RAGGED, false, LDS_OUT, ACC, CODE, true>(D, offs, lut, rg, w0 * 64, b0, b1, lvl,
-                                                                    ebs, lbase, nclear16);
-                if (LDS_OUT && !in_big) {
-                    wave_sync();
-                    // the staged stream is done with: its space holds the value table
-                    store_group<RAGGED, ACC>(D, lvl, ebs, reinterpret_cast<float *>(stage), lbase, b0, b1);
-                }
-                // the LDS buffers are reused by the next stream or group of this wave
                 wave_sync();
+            } else if (j == 0) {
+                decode_group_streams<false, true, true, CODE>(D, lut, stage, lvl, ebs, b0, b1);
             }
+        }
+        if (slot < P && j == 0 && lane == 0) fold_slot[slot] = fold ? 1u : 0u;
+        __syncthreads();
+        if (tpw > 1u && D.s_pow2) {
+            // several buckets per group and s a power of two: each value formed
+            // directly, (k * (norm / s)) rounded once (dequant_value), every
+            // bucket of the round in one pass
+            const uint32_t gq = tpw * nqd;  // quads per group
+            for (uint32_t i = threadIdx.x; i < P * gq; i += kDecWG) {
+                const uint32_t p = i / gq, gi = i - p * gq;
+                const uint32_t t = 4u * gi / d;
+                const uint64_t bb = (r * P + p) * tpw + t;
+                if (!fold_slot[p] || bb >= D.nb) continue;
+                const uint64_t a = (r * P + p) * tpw * (uint64_t)d + 4u * gi;
+                if (a >= D.n) continue;
+                const unsigned char *sb = base + (size_t)(p * K) * kWaveLdsBytes;
+                float *o = D.v_hat + a;
+                const bool whole = a + 4u <= D.n;
+                float4 x;
+                if (whole) {
+                    x = *reinterpret_cast<const float4 *>(o);
+                } else {
+                    x.x = o[0];
+                    x.y = a + 1u < D.n ? o[1] : 0.0f;
+                    x.z = a + 2u < D.n ? o[2] : 0.0f;
+                    x.w = 0.0f;
+                }
+                for (uint32_t jj = 0; jj < K; ++jj) {
+                    const unsigned char *wb = sb + (size_t)jj * kWaveLdsBytes;
+                    const uint32_t word = *reinterpret_cast<const uint32_t *>(wb + kStageBytes + 4u * gi);
+                    const double e = reinterpret_cast<const double *>(wb + kStageBytes + kLevelBytes)[t];
+                    float v4[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t byte = (word >> (8 * u)) & 0xffu;
+                        const float m = dequant_value(e, byte & 127u, D.s, true, D.inv_s);
+                        v4[u] = __uint_as_float(__float_as_uint(m) | ((byte & 128u) << 24));
+                    }
+                    x.x = x.x + v4[0];
+                    x.y = x.y + v4[1];
+                    x.z = x.z + v4[2];
+                    x.w = x.w + v4[3];
+                }
+                if (whole) {
+                    *reinterpret_cast<float4 *>(o) = x;
+                } else {
+                    o[0] = x.x;
+                    if (a + 1u < D.n) o[1] = x.y;
+                    if (a + 2u < D.n) o[2] = x.z;
+                }
+            }
+            // the level bytes are reused by the next round
+            __syncthreads();
+            continue;
+        }
+        for (uint32_t t = 0; t < tpw; ++t) {
+            // this wave's stream: the values of bucket b0 + t's 256 level bytes
+            if (fold && b0 + t < b1) {
+                float *tbl = reinterpret_cast<float *>(stage);
+                const double e = ebs[t];
+#pragma unroll
+                for (uint32_t v = (uint32_t)lane; v < 256u; v += 64u) {
+                    const float m = dequant_value(e, v & 127u, D.s, D.s_pow2 != 0u, D.inv_s);
+                    tbl[v] = __uint_as_float(__float_as_uint(m) | ((v & 128u) << 24));
+                }
+            }
+            __syncthreads();
+            // bucket t of every folded group: quad i of group slot p
+            for (uint32_t i = threadIdx.x; i < P * nqd; i += kDecWG) {
+                const uint32_t p = i / nqd, qi = i - p * nqd;
+                const uint64_t bb = (r * P + p) * tpw + t;
+                if (!fold_slot[p] || bb >= D.nb) continue;
+                const uint64_t a = bb * d + 4u * qi;
+                if (a >= D.n) continue;
+                const uint32_t li = t * d + 4u * qi;  // the quad's level bytes in the group's buffer
+                const unsigned char *sb = base + (size_t)(p * K) * kWaveLdsBytes;
+                float *o = D.v_hat + a;
+                const bool whole = a + 4u <= D.n;
+                float4 x;
+                if (whole) {
+                    x = *reinterpret_cast<const float4 *>(o);
+                } else {
+                    x.x = o[0];
+                    x.y = a + 1u < D.n ? o[1] : 0.0f;
+                    x.z = a + 2u < D.n ? o[2] : 0.0f;
+                    x.w = 0.0f;
+                }
+                for (uint32_t jj = 0; jj < K; ++jj) {
+                    const unsigned char *wb = sb + (size_t)jj * kWaveLdsBytes;
+                    const uint32_t word = *reinterpret_cast<const uint32_t *>(wb + kStageBytes + li);
+                    const float *tb = reinterpret_cast<const float *>(wb);
+                    x.x = x.x + tb[word & 0xffu];
+                    x.y = x.y + tb[(word >> 8) & 0xffu];
+                    x.z = x.z + tb[(word >> 16) & 0xffu];
+                    x.w = x.w + tb[word >> 24];
+                }
+                if (whole) {
+                    *reinterpret_cast<float4 *>(o) = x;
+                } else {
+                    o[0] = x.x;
+                    if (a + 1u < D.n) o[1] = x.y;
+                    if (a + 2u < D.n) o[2] = x.z;
+                }
+            }
+            // the tables and level bytes are reused by the next bucket and round
+            __syncthreads();
         }
     }
 }
-
 
 // ---- buckets longer than a chunk ---------------------------------------------
 // A bucket whose payload is too long for one team is cut into chunks of

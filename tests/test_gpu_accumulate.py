@@ -4,9 +4,14 @@ The streams are written by the oracle (so no oracle input comes from the HIP
 path), copied to the device, and summed into an accumulator that starts from
 seeded values with some -0.0 entries; the result must be bit-identical to the
 oracle's in-order fp32 fold. Cases cover the LDS-staged path (s <= 127,
-d <= 4096), the per-lane writer path (s > 127 or d > 4096), ragged buckets, one
-to 32 streams, zero streams, and the config-3 workload at full size with the
-launch configuration the benchmark times.
+d <= 4096): with up to 8 streams over buckets of 256 or more coordinates (a
+multiple of 4) the streams of a group are decoded side by side and folded into
+the accumulator at once (values tabulated per bucket, or formed directly where
+groups hold several buckets and s is a power of two; groups that do not fit the
+stage summed stream by stream), otherwise stream by stream; the per-lane writer
+path (s > 127 or d > 4096), ragged buckets, one to 32 streams, zero streams,
+and the config-3 workload at full size with the launch configuration the
+benchmark times.
 """
 import numpy as np
 import pytest
@@ -69,6 +74,8 @@ def _check(vs, s, d, seed, seg_len=None):
 @pytest.mark.parametrize("n,d,s,k,seed", [
     (20000, 512, 16, 3, 1), (9999, 37, 3, 5, 2), (3 * 4096 + 5, 4096, 64, 4, 3),
     (5000, 64, 4, 32, 4), (4097, 4096, 1, 2, 5), (1, 1, 1, 3, 6),
+    (50000, 512, 16, 1, 11), (20000, 256, 8, 5, 12), (30002, 1024, 32, 8, 13), (9000, 300, 4, 2, 14),
+    (12000, 512, 12, 3, 16), (8002, 1024, 100, 2, 17),
 ])
 def test_accumulate_lds_path(n, d, s, k, seed):
     vs = [wl.small_gaussian(n, seed * 100 + j) for j in range(k)]
@@ -80,6 +87,31 @@ def test_accumulate_lds_path(n, d, s, k, seed):
 def test_accumulate_lane_writer_path(n, d, s, k, seed):
     vs = [wl.small_gaussian(n, seed * 100 + j) for j in range(k)]
     _check(vs, s, d, seed)
+
+
+def test_accumulate_groups_past_the_stage():
+    # d = 4096, s = 64, three streams; stream 1 scales buckets 1 and 3 by their
+    # largest magnitude (about 9.5 bits per coordinate: those groups do not fit
+    # the decoder's stage and are summed stream by stream), the other buckets and
+    # streams by the L2 norm
+    n, d, s, seed = 5 * 4096 + 100, 4096, 64, 15
+    vs = [wl.small_gaussian(n, 1500 + j) for j in range(3)]
+    bst = oracle.uniform_buckets(n, d)
+    streams = []
+    for j, v in enumerate(vs):
+        norms = oracle.bucket_norms(v, bst)
+        if j == 1:
+            mx = oracle.bucket_max_norms(v, bst)
+            norms[[1, 3]] = mx[[1, 3]]
+        _, _, words, offs, _ = oracle.compress(v, bst, s, seed + j, norms=norms)
+        streams.append((words, offs))
+    per_bucket = np.diff(streams[1][1].astype(np.int64)) / d
+    assert per_bucket[1] > 8 and per_bucket[3] > 8 and per_bucket[0] < 4
+    acc0 = _start_acc(n, seed)
+    got = _run(streams, bst, n, s, d, acc0)
+    rc, exp = oracle.decode_accumulate(streams, bst, s, acc0)
+    assert rc == oracle.OK
+    assert np.array_equal(got.view(np.uint32), exp.view(np.uint32))
 
 
 def test_accumulate_sparse_and_mixed_values():
