@@ -191,10 +191,13 @@ qsgd_status qsgd_decode_ex(const uint64_t *in, const uint64_t *bucket_bit_offset
 uint32_t qsgd_max_streams(void);
 
 /*
- * qsgd_decode_accumulate: adds the decodes of k streams to acc in one launch
- * (each wave decodes all k streams of a group of buckets in turn and adds each
- * to the group's part of acc: acc is read and written once per stream, the
- * decoded values never go to memory).
+ * qsgd_decode_accumulate: adds the decodes of k streams to acc in one launch;
+ * the decoded values never go to memory. For k <= 8 streams over uniform
+ * buckets of 256 or more coordinates (a multiple of 4) with s <= 127, the waves
+ * of a workgroup decode the k streams of a group side by side and add them to
+ * acc together, reading and writing acc once per call; otherwise each wave
+ * decodes the k streams of a group in turn and adds each to the group's part
+ * of acc (acc read and written once per stream). The result is the same.
  *   in                  HOST array of k DEVICE pointers: stream words of each
  *                       stream, written by qsgd_encode with the same n, s, d.
  *   bucket_bit_offsets  HOST array of k DEVICE pointers: each stream's
