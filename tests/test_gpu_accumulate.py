@@ -150,6 +150,15 @@ def test_full_size_config3_four_streams():
     _check(vs, w.s, w.d, w.seed)
 
 
+def test_full_size_config2_four_streams():
+    # eight buckets of 512 per group and s = 16: the folded sum forms each value
+    # directly, the whole round in one pass
+    w = wl.config2()
+    vs = [w.v] + [wl.peer_gradient(2, j) for j in range(1, 4)]
+    print(f"decode-accumulate full size n={w.n} d={w.d} s={w.s} k=4", flush=True)
+    _check(vs, w.s, w.d, w.seed)
+
+
 @pytest.mark.parametrize("n,d,s,k", [(50000, 512, 16, 3), (30000, 4096, 64, 2), (20000, 1000, 300, 4),
                                      (200000, 50000, 8, 2)])
 def test_gamma_streams(n, d, s, k):
