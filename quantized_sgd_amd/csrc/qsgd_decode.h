@@ -97,8 +97,10 @@ struct DecodeParams {
 //   bits 20-23  gap - 1 of the second record
 //   bits 24-31  level byte of the second record
 // With total length 0, the first field alone (any value) if it ends within the
-// 12 bits: bits 4-7 its length, bits 8-15 its value (else 0); the general path
-// decodes from it. Computed at compile time.
+// 12 bits: bits 4-7 its length, bits 8-15 its value; else, for an omega field
+// that starts with whole groups within the 12 bits, bits 16-19 the bits those
+// groups take and bits 20-31 the value they leave (the next group's length - 1);
+// else 0. The general path decodes from it. Computed at compile time.
 struct alignas(16) RecordLut {
     uint32_t e[1 << kLutBits];
 };
@@ -223,7 +225,20 @@ constexpr RecordLut make_record_lut() {
         } else {
             LutCursor cf{reverse_bits(i, kLutBits), 0};
             const int N = lut_field_any<CODE>(cf);
-            if (N > 0) e = ((uint32_t)N << 8) | ((uint32_t)cf.pos << 4);
+            if (N > 0) {
+                e = ((uint32_t)N << 8) | ((uint32_t)cf.pos << 4);
+            } else if (!CODE) {
+                // an omega field longer than the window: its whole groups within it
+                LutCursor cp{reverse_bits(i, kLutBits), 0};
+                int Np = 1, m = 0;
+                while (lut_take(cp, 1) == 1) {
+                    const int v = lut_take(cp, Np);
+                    if (v < 0) break;
+                    Np = (1 << Np) | v;
+                    m = cp.pos;
+                }
+                if (m > 0) e = ((uint32_t)Np << 20) | ((uint32_t)m << 16);
+            }
         }
         t.e[i] = e;
     }
@@ -300,11 +315,14 @@ struct RecordCtx {
     uint32_t gbits, kbits, s;
 };
 
+__device__ __forceinline__ uint32_t bitlen32(uint32_t x) { return 32u - (uint32_t)__clz(x); }
+
 // General omega decoding from bit p: returns N and advances p, or 0 if a group
-// is longer than maxbits (<= 25, so each group lies in one 64-bit read).
+// is longer than maxbits (<= 25, so each group lies in one 64-bit read). N: the
+// value left by the groups before p (1 at a codeword's start).
 template <bool LDS>
-__device__ __forceinline__ uint32_t omega_at(const Bits<LDS> &r, uint32_t &p, uint32_t maxbits) {
-    uint32_t N = 1;
+__device__ __forceinline__ uint32_t omega_at(const Bits<LDS> &r, uint32_t &p, uint32_t maxbits,
+                                             uint32_t N = 1u) {
     while (true) {
         const uint32_t w = (uint32_t)r.at(p);
         if ((w & 1u) == 0) {
@@ -374,7 +392,21 @@ __device__ __forceinline__ uint32_t record_slow(const Bits<LDS> &r, const X &x, 
         }
     }
     uint32_t q = p;
-    gap = X::code ? gamma_at(r, q, x.gbits) : omega_at(r, q, x.gbits);
+    if (X::code) {
+        gap = gamma_at(r, q, x.gbits);
+    } else {
+        // an omega gap field longer than the window goes on from the groups e0
+        // holds; their longest group is the last, as long as the value they leave
+        const uint32_t m = (e0 >> 16) & 15u, N0 = e0 >> 20;
+        if (m == 0u) {
+            gap = omega_at(r, q, x.gbits);
+        } else if (bitlen32(N0) <= x.gbits) {
+            q += m;
+            gap = omega_at(r, q, x.gbits, N0);
+        } else {
+            gap = 0;
+        }
+    }
     if (gap == 0) return 0;
     neg = (uint32_t)r.at(q) & 1u;
     q += 1u;
@@ -443,7 +475,6 @@ __device__ __forceinline__ uint32_t record_at(const Bits<LDS> &r, const X &x, ui
     return q;
 }
 
-__device__ __forceinline__ uint32_t bitlen32(uint32_t x) { return 32u - (uint32_t)__clz(x); }
 
 // Slots of a lane's gap-prefix table (bytes, in the wave's level buffer while
 // the chains are being synchronised); positions past the table are not looked up.
