@@ -320,19 +320,28 @@ __device__ __forceinline__ uint32_t bitlen32(uint32_t x) { return 32u - (uint32_
 // General omega decoding from bit p: returns N and advances p, or 0 if a group
 // is longer than maxbits (<= 25, so each group lies in one 64-bit read). N: the
 // value left by the groups before p (1 at a codeword's start).
+// One read serves the groups and the final bit that lie within its first 33
+// bits; the stream is read again only where a group passes them.
 template <bool LDS>
 __device__ __forceinline__ uint32_t omega_at(const Bits<LDS> &r, uint32_t &p, uint32_t maxbits,
                                              uint32_t N = 1u) {
+    uint64_t w = r.at(p);
+    uint32_t have = 33u;  // bits of w that are stream bits from p on
     while (true) {
-        const uint32_t w = (uint32_t)r.at(p);
         if ((w & 1u) == 0) {
             p += 1u;
             return N;
         }
         const uint32_t g = N + 1u;
         if (g > maxbits) return 0;
-        N = __builtin_bitreverse32(w) >> (32u - g);
+        if (g >= have) {
+            w = r.at(p);
+            have = 33u;
+        }
+        N = __builtin_bitreverse32((uint32_t)w) >> (32u - g);
         p += g;
+        w >>= g;
+        have -= g;
     }
 }
 
