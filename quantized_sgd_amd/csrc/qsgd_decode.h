@@ -495,10 +495,17 @@ constexpr uint32_t kCumSlots = 63;
 #define QSGD_GUESS_STEPS 6
 #endif
 constexpr int kGuessSteps = QSGD_GUESS_STEPS;
-// Buckets whose payload averages more bits per coordinate than this take no
-// guess steps: their long records miss the table on the true chain too, where
-// moving one bit on derails the chain.
+// Buckets whose payload averages more bits per coordinate than kGuessBits, or
+// fewer than kGuessMinBits, take no guess steps: their long records (large
+// levels, or long gaps between sparse non-zeros) miss the table on the true
+// chain too, where moving one bit on derails the chain.
 constexpr uint32_t kGuessBits = 4;
+constexpr uint32_t kGuessMinBits = 1;
+
+// Whether a bucket of len coordinates and payload bits takes guess steps.
+__device__ __forceinline__ bool guess_bucket(uint64_t bits, uint64_t len) {
+    return bits <= (uint64_t)kGuessBits * len && bits >= (uint64_t)kGuessMinBits * len;
+}
 
 // The first steps of a chain whose start is only a guess at a record boundary.
 // Such a start lands on bits that are not a record start as often as not, and
@@ -812,8 +819,8 @@ __device__ __forceinline__ void decode_group(const DecodeParams &D, const uint64
                 if (nl == 0) nl = 1;
             }
             // guess steps pay where table misses are rare on the true chain:
-            // short records, at most kGuessBits payload bits per coordinate
-            guess = (uint64_t)Lp <= (uint64_t)kGuessBits * len;
+            // short records, kGuessMinBits to kGuessBits payload bits per coordinate
+            guess = guess_bucket(Lp, len);
         }
     }
     if (LDS_OUT && tactive && q == 0) ebs[team] = e_b;
@@ -1639,7 +1646,7 @@ __global__ __launch_bounds__(kDecWG) void chunk_parse_kernel(ChunkParams C) {
     if (c >= nact || E - A >= (1ull << 31)) return;
     const uint64_t c0 = b * C.D.d;
     const uint64_t blen = (c0 + C.D.d < C.D.n ? c0 + C.D.d : C.D.n) - c0;
-    const bool guess = nbits <= (uint64_t)kGuessBits * blen;
+    const bool guess = guess_bucket(nbits, blen);
     const uint64_t total_words = (C.offs[C.D.nb] + 63) >> 6;
     // stage from the word holding the chunk's first bit through the merge window
     const uint64_t cs = A + 32 + (uint64_t)c * kChunkBits;
@@ -1772,7 +1779,7 @@ __global__ __launch_bounds__(kDecWG) void chunk_write_kernel(ChunkParams C) {
     chunk_bucket(C, b, A, E, nbits, nact);
     const uint64_t c0 = b * C.D.d;
     const uint64_t blen = (c0 + C.D.d < C.D.n ? c0 + C.D.d : C.D.n) - c0;
-    const bool guess = nbits <= (uint64_t)kGuessBits * blen;
+    const bool guess = guess_bucket(nbits, blen);
     const uint64_t vs = A + C.vstart[slot];
     const uint64_t ve = A + C.rec[slot].y;
     const uint64_t base = C.vbase[slot];

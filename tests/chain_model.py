@@ -34,6 +34,7 @@ FIELD_MAX = 16  # the table's largest gap and level: four bits each in an entry
 SYNC_BITS = _decoder_constant(r"constexpr int kSyncWin = (\d+);")
 GUESS_STEPS = _decoder_constant(r"#define QSGD_GUESS_STEPS (\d+)")
 GUESS_BITS_PER_COORD = _decoder_constant(r"constexpr uint32_t kGuessBits = (\d+);")
+GUESS_MIN_BITS_PER_COORD = _decoder_constant(r"constexpr uint32_t kGuessMinBits = (\d+);")
 
 
 def stream_bits(words) -> list:
@@ -89,7 +90,7 @@ class Bucket:
         lp = end - self.P0
         self.nl = max(1, min(team, lp // SYNC_BITS)) if lp > 0 else 0
         self.seg = (lp + self.nl - 1) // self.nl if self.nl else 0
-        self.guess = lp <= GUESS_BITS_PER_COORD * length
+        self.guess = GUESS_MIN_BITS_PER_COORD * length <= lp <= GUESS_BITS_PER_COORD * length
         self.gbits = max(1, int(length).bit_length())
         self.kbits = int(s).bit_length()
         self._table = {}
